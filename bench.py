@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeek-V4 hybrid sparse MQA attention path on one GPU.
+
+One step = one dsv4_attn_forward call (gather + fused split kernel + merge)
+over one batch of a synthetic workload already resident in HBM.  To keep the
+256 MB Infinity Cache from serving repeated steps, the step rotates over
+several GPU copies of the inputs (same values, different addresses) whose
+referenced bytes together exceed the cache several times.
+
+Prints ONE JSON line: tokens (query rows) per second of the whole job, plus
+a roofline object for the dominant kernel (algorithmic bytes per launch over
+its average duration from HIP events recorded on the launch stream) and the
+fp64 oracle timed on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "decode attention tokens/s + achieved HBM GB/s (% peak), C4/C128 at batch×ctx"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+KV_ROW_BYTES = {"bf16": 1024, "fp8": 584}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_mqa_amd", "csrc", f)
+                  for f in ("dsv4_attn_kernels.hip", "dsv4_device.h", "dsv4_launch.h")]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case) -> dict:
+    """Bytes one call must move: Q, out, lse, C4 index lists and every unique
+    KV row it reads (SWA window rows and visible/selected compressed rows)."""
+    T, H = case.T, case.H
+    q = T * H * 512 * 2
+    out = T * H * 512 * 2
+    lse = T * H * 4
+    idx = T * case.K * 4 if case.R == 4 else 0
+    swa_rows = 0
+    ext_rows = 0
+    for r in range(case.B):
+        lo_t, hi_t = int(case.qo_indptr[r]), int(case.qo_indptr[r + 1])
+        n_q = hi_t - lo_t
+        if n_q == 0:
+            continue
+        L = int(case.seq_lens[r])
+        p_first, p_last = L - n_q, L - 1
+        swa_rows += p_last - max(0, p_first - case.W + 1) + 1
+        if case.R == 128:
+            ext_rows += (p_last + 1) // 128
+        elif case.R == 4:
+            ids = case.c4_indices[lo_t:hi_t]
+            ext_rows += len(np.unique(ids[ids >= 0]))
+    kv = (swa_rows + ext_rows) * KV_ROW_BYTES[case.kv]
+    return dict(total=q + out + lse + idx + kv, kv=kv, q=q, out=out, lse=lse, idx=idx,
+                kv_rows=swa_rows + ext_rows)
+
+
+def describe_workload(n, case) -> dict:
+    sl = case.seq_lens
+    return {
+        "workload": case.name,
+        "batch": int(case.B),
+        "query_rows": int(case.T),
+        "seq_len": int(sl[0]) if np.all(sl == sl[0]) else f"{int(sl.min())}-{int(sl.max())}",
+        "q_heads": int(case.H),
+        "kv_heads": 1,
+        "head_dim": 512,
+        "window": int(case.W),
+        "compress_ratio": int(case.R),
+        "c4_topk": int(case.K) if case.R == 4 else None,
+        "kv_format": case.kv,
+        "page_size": 256,
+    }
+
+
+def cpu_baseline(case, target_s: float):
+    """The fp64 oracle on the host cores over a bounded sample of rows."""
+    import oracle
+
+    orc = oracle.Oracle()
+    threads = orc.max_threads()
+    t0 = time.perf_counter()
+    orc.attention(case, rows=[0])
+    per_row_1 = time.perf_counter() - t0
+    n = int(max(1, min(case.T, target_s * max(1, min(threads, case.T)) / max(per_row_1, 1e-6))))
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(case.T, size=n, replace=False)).astype(np.int32)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:  # repeat small samples until the timing is stable (>= 3 s)
+        orc.attention(case, rows=rows)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min(3.0, target_s) or dt >= target_s:
+            break
+    used = min(threads, n)
+    return {
+        "value": reps * n / dt,
+        "unit": "tokens/s",
+        "cores": int(used),
+        "kind": "oracle",
+        "sample": f"{n} of {case.T} query rows of the same workload x {reps} repetitions "
+                  f"(fp64 C, OpenMP over rows), {dt:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: C4 decode, batch 32)")
+    ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size target")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-keys", type=int, default=0, help="force keys per split (0 = library plan)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the attention shards by "
+              "request, so N GPUs run N independent copies of this benchmark)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from hybrid_sparse_mqa_amd import (dsv4_attn_forward, dsv4_attn_plan, dsv4_attn_set_split_keys,
+                                       dsv4_attn_timing_enable, dsv4_attn_timing_read)
+    from synth import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    case = make_config(args.config)
+    ab = algorithmic_bytes(case)
+    bf = torch.bfloat16
+
+    def up(a, dt=None):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        return (x.view(dt) if dt is not None else x).to(dev)
+
+    def pool(a):
+        return None if a is None else (up(a.view(np.int16), bf) if case.kv == "bf16" else up(a))
+
+    base = dict(q=up(case.q.view(np.int16), bf), swa_pool=pool(case.swa_pool), extra_pool=pool(case.extra_pool))
+    meta = dict(swa_page_table=up(case.swa_page_table), extra_page_table=up(case.extra_page_table),
+                c4_indices=up(case.c4_indices), seq_lens=up(case.seq_lens), qo_indptr=up(case.qo_indptr),
+                sink=up(case.sink))
+    set_bytes = sum(x.numel() * x.element_size() for x in base.values() if x is not None)
+    n_sets = args.sets or int(min(64, max(2, -(-3 * MALL_BYTES // max(ab["total"], 1)))))
+    n_sets = max(1, min(n_sets, int((48 << 30) // max(set_bytes, 1))))
+    sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(n_sets - 1)]
+    cold = n_sets * ab["total"] > 2 * MALL_BYTES
+    outs = [torch.empty((case.T, case.H, 512), dtype=bf, device=dev) for _ in range(2)]
+    lses = [torch.empty((case.T, case.H), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    if args.split_keys:
+        dsv4_attn_set_split_keys(args.split_keys)
+    splits, chunk = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
+                                   0 if case.extra_page_table is None else case.extra_page_table.shape[1])
+
+    def step(i):
+        s = sets[i % n_sets]
+        dsv4_attn_forward(s["q"], s["swa_pool"], meta["swa_page_table"], s["extra_pool"], meta["extra_page_table"],
+                          meta["c4_indices"], meta["seq_lens"], meta["qo_indptr"], meta["sink"], case.R, case.W,
+                          case.scale, out=outs[i & 1], lse=lses[i & 1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {case.name}: T={case.T} H={case.H} splits={splits} keys/split={chunk} "
+          f"sets={n_sets} ({'cold' if cold else 'warm'}) algorithmic {ab['total'] / 1e6:.2f} MB/call",
+          file=sys.stderr, flush=True)
+
+    # Eager calls: per-call kernel time from the library's HIP events on the
+    # launch stream, and the wall time of the Python-driven loop.
+    n_eager = min(args.steps, 100)
+    dsv4_attn_timing_read()  # clear
+    dsv4_attn_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_eager):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
+    dsv4_attn_timing_enable(False)
+    kern_ms, calls = dsv4_attn_timing_read()
+    kernel_avg_ms = kern_ms / max(calls, 1)
+
+    # Timed region: exactly `steps` steps replayed from HIP graphs (one graph
+    # holds one call per input set; a second holds the remainder), bracketed by
+    # HIP events on the replay stream.
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    full, rem = divmod(args.steps, n_sets)
+    with torch.cuda.stream(stream):
+        for count in ([n_sets] if full else []) + ([rem] if rem else []):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(count):
+                    step(i)
+            graphs.append((g, count))
+        for g, _ in graphs:  # warm replay
+            g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(full):
+            graphs[0][0].replay()
+        if rem:
+            graphs[-1][0].replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    event_ms = ev0.elapsed_time(ev1)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = case.T / (ms_per_step / 1e3)
+    graph_kernel_ms = event_ms / args.steps   # kernel + in-graph launch gap per step
+    achieved = ab["total"] / (graph_kernel_ms * 1e-3) / 1e9
+    main_bytes = ab["total"]
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(case.name)
+        if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("split_keys", 0) == args.split_keys:
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(describe_workload(args.config, case), splits=int(splits), keys_per_split=int(chunk),
+                       input_sets=int(n_sets), cache="cold-rotated" if cold else "warm-rotated",
+                       timed="HIP graph replay", parallelism="single GPU"),
+        "achieved_gbs_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9,
+        "kernel_ms": {"attn_fused_kernel_graph_events": graph_kernel_ms,
+                      "attn_fused_kernel_eager_events": kernel_avg_ms},
+        "eager_ms_per_call": eager_ms,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_fused_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": main_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,120 @@
+"""Python entry points with the names of the C ABI (include/dsv4_attn.h).
+
+They only build descriptors and pass the current stream; all work happens in
+``libdsv4_attn.so``.  Tensors must already be on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _native as N
+
+
+def dsv4_attn_forward(
+    q: torch.Tensor,
+    swa_pool: torch.Tensor,
+    swa_page_table: torch.Tensor,
+    extra_pool: Optional[torch.Tensor],
+    extra_page_table: Optional[torch.Tensor],
+    c4_indices: Optional[torch.Tensor],
+    seq_lens: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    sink: Optional[torch.Tensor],
+    compress_ratio: int,
+    window: int,
+    scale: float,
+    out: Optional[torch.Tensor] = None,
+    lse: Optional[torch.Tensor] = None,
+    return_lse: bool = True,
+    stream: Optional[int] = None,
+) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """SWA + (C4 | C128) attention of every query row; returns (out, lse)."""
+    L = N.load()
+    T, H = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    descs = [N.describe(x) for x in (q, swa_pool, swa_page_table, extra_pool, extra_page_table, c4_indices,
+                                     seq_lens, qo_indptr, sink, out, lse)]
+    st = N.stream_handle(q.device) if stream is None else stream
+    N.check(L.dsv4_attn_forward(
+        *[N.ref(d) for d in descs[:9]], int(compress_ratio), int(window), float(scale),
+        N.ref(descs[9]), N.ref(descs[10]), ctypes.c_void_p(st)))
+    return out, lse
+
+
+def dsv4_attn_gather_slots(
+    swa_page_table: torch.Tensor,
+    extra_page_table: Optional[torch.Tensor],
+    c4_indices: Optional[torch.Tensor],
+    seq_lens: torch.Tensor,
+    qo_indptr: torch.Tensor,
+    num_rows: int,
+    compress_ratio: int,
+    window: int,
+    slots: Optional[torch.Tensor] = None,
+    counts: Optional[torch.Tensor] = None,
+    stream: Optional[int] = None,
+) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Canonical slot list of every row (slots [T, Kmax], counts [T, 2])."""
+    L = N.load()
+    dev = swa_page_table.device
+    if slots is None:
+        extra = 0
+        if compress_ratio == 4:
+            extra = c4_indices.shape[1]
+        elif compress_ratio == 128:
+            extra = 256 * extra_page_table.shape[1]
+        slots = torch.empty((num_rows, window + extra), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((num_rows, 2), dtype=torch.int32, device=dev)
+    descs = [N.describe(x) for x in (swa_page_table, extra_page_table, c4_indices, seq_lens, qo_indptr, slots, counts)]
+    st = N.stream_handle(dev) if stream is None else stream
+    N.check(L.dsv4_attn_gather_slots(
+        *[N.ref(d) for d in descs[:5]], int(num_rows), int(compress_ratio), int(window),
+        N.ref(descs[5]), N.ref(descs[6]), ctypes.c_void_p(st)))
+    return slots, counts
+
+
+def dsv4_abi_version() -> int:
+    return int(N.load().dsv4_abi_version())
+
+
+def dsv4_last_error() -> str:
+    return N.load().dsv4_last_error().decode()
+
+
+def dsv4_attn_set_split_keys(keys_per_split: int) -> None:
+    N.check(N.load().dsv4_attn_set_split_keys(int(keys_per_split)))
+
+
+def dsv4_attn_plan(num_rows, num_heads, compress_ratio, window, c4_width=0, extra_pages=0) -> Tuple[int, int]:
+    s = ctypes.c_int32()
+    c = ctypes.c_int32()
+    N.check(N.load().dsv4_attn_plan(int(num_rows), int(num_heads), int(compress_ratio), int(window), int(c4_width),
+                                    int(extra_pages), ctypes.byref(s), ctypes.byref(c)))
+    return s.value, c.value
+
+
+def dsv4_attn_workspace_reserve(nbytes: int) -> None:
+    N.check(N.load().dsv4_attn_workspace_reserve(int(nbytes)))
+
+
+def dsv4_attn_workspace_release() -> None:
+    N.load().dsv4_attn_workspace_release()
+
+
+def dsv4_attn_timing_enable(enable: bool) -> None:
+    N.check(N.load().dsv4_attn_timing_enable(int(bool(enable))))
+
+
+def dsv4_attn_timing_read() -> Tuple[float, int]:
+    """(summed kernel milliseconds, calls) recorded since the last read."""
+    a = ctypes.c_double()
+    n = ctypes.c_int64()
+    N.check(N.load().dsv4_attn_timing_read(ctypes.byref(a), ctypes.byref(n)))
+    return a.value, n.value

@@ -1,0 +1,536 @@
+// dsv4_api.cpp -- host side of the C ABI declared in include/dsv4_attn.h:
+// argument validation (no device reads), split planning from static bounds,
+// the per-device workspace for split partials, kernel launches on the caller's
+// stream, optional HIP-event timing and the DSV4_VALIDATE contract check.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dsv4_attn.h"
+#include "dsv4_launch.h"
+
+using namespace dsv4;
+
+namespace {
+
+thread_local std::string g_err;
+
+dsv4_status fail(dsv4_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define DSV4_TRY(expr)                         \
+    do {                                       \
+        dsv4_status st_ = (expr);              \
+        if (st_ != DSV4_OK) return st_;        \
+    } while (0)
+
+#define DSV4_HIP(expr)                                                                       \
+    do {                                                                                     \
+        hipError_t e_ = (expr);                                                              \
+        if (e_ != hipSuccess) return fail(DSV4_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+const char* dtype_name(int32_t d) {
+    switch (d) {
+        case DSV4_BF16: return "bf16";
+        case DSV4_F32: return "f32";
+        case DSV4_I32: return "i32";
+        case DSV4_U8: return "u8";
+        default: return "?";
+    }
+}
+
+// Shape / dtype / stride checks of one descriptor.  shape entries < 0 mean
+// "any"; the last dimension must be contiguous.
+dsv4_status check_tensor(const char* name, const dsv4_tensor* t, int32_t dtype, int32_t ndim,
+                         std::initializer_list<int64_t> shape) {
+    if (t == nullptr) return fail(DSV4_ERR_INVALID, "%s: NULL descriptor", name);
+    if (t->data == nullptr) return fail(DSV4_ERR_INVALID, "%s: NULL data pointer", name);
+    if (t->dtype != dtype)
+        return fail(DSV4_ERR_INVALID, "%s: dtype %s, expected %s", name, dtype_name(t->dtype), dtype_name(dtype));
+    if (t->ndim != ndim) return fail(DSV4_ERR_INVALID, "%s: ndim %d, expected %d", name, t->ndim, ndim);
+    int i = 0;
+    int64_t numel = 1;
+    for (int d = 0; d < ndim; ++d) numel *= t->shape[d] > 0 ? t->shape[d] : 0;
+    for (int64_t s : shape) {
+        if (t->shape[i] < 0) return fail(DSV4_ERR_INVALID, "%s: negative extent in dim %d", name, i);
+        if (s >= 0 && t->shape[i] != s)
+            return fail(DSV4_ERR_INVALID, "%s: dim %d is %lld, expected %lld", name, i, (long long)t->shape[i],
+                        (long long)s);
+        ++i;
+    }
+    if (numel == 0) return DSV4_OK;  // empty tensors carry arbitrary strides and are never read
+    if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
+        return fail(DSV4_ERR_INVALID, "%s: last dimension must be contiguous", name);
+    for (int d = 0; d < ndim - 1; ++d)
+        if (t->stride[d] < 0) return fail(DSV4_ERR_INVALID, "%s: negative stride", name);
+    return DSV4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct PoolInfo {
+    bool fp8;
+    int64_t pages;
+    int64_t row_bytes;
+};
+
+dsv4_status check_pool(const char* name, const dsv4_tensor* t, PoolInfo* info) {
+    if (t == nullptr || t->data == nullptr) return fail(DSV4_ERR_INVALID, "%s: NULL", name);
+    if (t->dtype == DSV4_BF16) {
+        DSV4_TRY(check_tensor(name, t, DSV4_BF16, 2, {-1, DSV4_HEAD_DIM}));
+        if (t->stride[0] < DSV4_HEAD_DIM || t->stride[0] % 8 != 0)
+            return fail(DSV4_ERR_INVALID, "%s: row stride must be >= 512 and a multiple of 8", name);
+        if (!aligned16(t->data)) return fail(DSV4_ERR_INVALID, "%s: data must be 16-byte aligned", name);
+        info->fp8 = false;
+        info->pages = t->shape[0] / DSV4_PAGE_SIZE;
+        info->row_bytes = t->stride[0] * 2;
+        return DSV4_OK;
+    }
+    if (t->dtype == DSV4_U8) {
+        DSV4_TRY(check_tensor(name, t, DSV4_U8, 2, {-1, DSV4_FP8_PAGE_BYTES}));
+        if (t->stride[0] != DSV4_FP8_PAGE_BYTES)
+            return fail(DSV4_ERR_INVALID, "%s: packed FP8 pages must be contiguous", name);
+        if (!aligned16(t->data)) return fail(DSV4_ERR_INVALID, "%s: data must be 16-byte aligned", name);
+        info->fp8 = true;
+        info->pages = t->shape[0];
+        info->row_bytes = 0;
+        return DSV4_OK;
+    }
+    return fail(DSV4_ERR_INVALID, "%s: pool dtype must be bf16 rows or u8 packed FP8 pages", name);
+}
+
+struct Metadata {
+    int32_t B = 0, T = 0, R = 0, W = 0, K = 0, P_swa = 0, P_extra = 0;
+    Meta m{};
+};
+
+dsv4_status check_metadata(const dsv4_tensor* swa_page_table, const dsv4_tensor* extra_page_table,
+                           const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens, const dsv4_tensor* qo_indptr,
+                           int32_t T, int32_t compress_ratio, int32_t window, Metadata* md) {
+    if (compress_ratio != 0 && compress_ratio != 4 && compress_ratio != 128)
+        return fail(DSV4_ERR_UNSUPPORTED, "invalid compress_ratio %d (must be 0, 4 or 128)", compress_ratio);
+    if (window < 1) return fail(DSV4_ERR_INVALID, "window must be >= 1 (got %d)", window);
+    if (window > (1 << 20)) return fail(DSV4_ERR_UNSUPPORTED, "window %d above 2^20", window);
+    DSV4_TRY(check_tensor("seq_lens", seq_lens, DSV4_I32, 1, {-1}));
+    const int64_t B = seq_lens->shape[0];
+    if (B < 1) return fail(DSV4_ERR_INVALID, "seq_lens: batch must be >= 1");
+    DSV4_TRY(check_tensor("qo_indptr", qo_indptr, DSV4_I32, 1, {B + 1}));
+    DSV4_TRY(check_tensor("swa_page_table", swa_page_table, DSV4_I32, 2, {B, -1}));
+    if (swa_page_table->shape[1] < 1) return fail(DSV4_ERR_INVALID, "swa_page_table: needs >= 1 page per request");
+    md->B = (int32_t)B;
+    md->T = T;
+    md->R = compress_ratio;
+    md->W = window;
+    md->P_swa = (int32_t)swa_page_table->shape[1];
+    md->m.seq_lens = (const int32_t*)seq_lens->data;
+    md->m.qo_indptr = (const int32_t*)qo_indptr->data;
+    md->m.swa_table = (const int32_t*)swa_page_table->data;
+    md->m.swa_ld = swa_page_table->stride[0];
+    md->m.B = (int32_t)B;
+    md->m.R = compress_ratio;
+    md->m.W = window;
+    if (compress_ratio != 0) {
+        DSV4_TRY(check_tensor("extra_page_table", extra_page_table, DSV4_I32, 2, {B, -1}));
+        if (extra_page_table->shape[1] < 1)
+            return fail(DSV4_ERR_INVALID, "extra_page_table: needs >= 1 page per request");
+        if (extra_page_table->shape[1] > (1 << 22) / DSV4_PAGE_SIZE * 64)
+            return fail(DSV4_ERR_UNSUPPORTED, "extra_page_table: too many pages per request");
+        md->P_extra = (int32_t)extra_page_table->shape[1];
+        md->m.ext_table = (const int32_t*)extra_page_table->data;
+        md->m.ext_ld = extra_page_table->stride[0];
+    }
+    if (compress_ratio == 4) {
+        DSV4_TRY(check_tensor("c4_indices", c4_indices, DSV4_I32, 2, {T, -1}));
+        if (c4_indices->shape[1] < 1) return fail(DSV4_ERR_INVALID, "c4_indices: width must be >= 1");
+        if (c4_indices->shape[1] > (1 << 16)) return fail(DSV4_ERR_UNSUPPORTED, "c4_indices: width above 65536");
+        md->K = (int32_t)c4_indices->shape[1];
+        md->m.c4 = (const int32_t*)c4_indices->data;
+        md->m.c4_ld = c4_indices->stride[0];
+        md->m.K = md->K;
+    }
+    return DSV4_OK;
+}
+
+int64_t extra_bound(int32_t R, int32_t K, int32_t P_extra) {
+    return R == 4 ? K : (R == 128 ? (int64_t)P_extra * DSV4_PAGE_SIZE : 0);
+}
+
+// ---- device properties and workspace ---------------------------------------
+struct DeviceState {
+    int cus = 0;
+    void* ws = nullptr;  // split partials
+    size_t ws_bytes = 0;
+    void* zero_row = nullptr;  // 4 KiB of zeros, read in place of unused keys
+};
+std::mutex g_mu;
+std::vector<DeviceState> g_dev;
+int32_t g_force_split_keys = 0;
+
+DeviceState* device_state(int dev) {
+    if (dev < 0) return nullptr;
+    if ((size_t)dev >= g_dev.size()) g_dev.resize(dev + 1);
+    DeviceState& d = g_dev[dev];
+    if (d.cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        d.cus = n;
+    }
+    return &d;
+}
+
+dsv4_status ensure_workspace(DeviceState* d, size_t bytes) {
+    if (d->ws_bytes >= bytes) return DSV4_OK;
+    if (d->ws != nullptr) {
+        DSV4_HIP(hipDeviceSynchronize());
+        DSV4_HIP(hipFree(d->ws));
+        d->ws = nullptr;
+        d->ws_bytes = 0;
+    }
+    size_t want = std::max(bytes, (size_t)16 << 20);
+    if (hipMalloc(&d->ws, want) != hipSuccess) {
+        d->ws = nullptr;
+        return fail(DSV4_ERR_WORKSPACE, "hipMalloc of %zu workspace bytes failed", want);
+    }
+    d->ws_bytes = want;
+    return DSV4_OK;
+}
+
+dsv4_status ensure_zero_row(DeviceState* d) {
+    if (d->zero_row != nullptr) return DSV4_OK;
+    void* p = nullptr;
+    if (hipMalloc(&p, 4096) != hipSuccess) return fail(DSV4_ERR_WORKSPACE, "hipMalloc of the zero row failed");
+    DSV4_HIP(hipMemset(p, 0, 4096));
+    DSV4_HIP(hipDeviceSynchronize());
+    d->zero_row = p;  // kept for the life of the process
+    return DSV4_OK;
+}
+
+void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, int32_t* splits, int32_t* chunk) {
+    const int64_t head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    int64_t c;
+    if (g_force_split_keys > 0) {
+        c = g_force_split_keys;
+    } else {
+        const int64_t rows = std::max<int64_t>(1, (int64_t)T * head_blocks);
+        int64_t want = (cus + rows - 1) / rows;  // splits per row to fill the chip once
+        const int64_t most = std::max<int64_t>(1, (nmax + 63) / 64);  // keep >= 64 keys per split
+        want = std::min(std::max<int64_t>(want, 1), most);
+        c = (nmax + want - 1) / want;
+        c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
+    }
+    c = std::min<int64_t>(std::max<int64_t>(c, kTileKeys), kMaxSplitKeys);
+    *chunk = (int32_t)c;
+    *splits = (int32_t)std::max<int64_t>(1, (nmax + c - 1) / c);
+}
+
+// ---- timing -------------------------------------------------------------------
+struct TimingRec {
+    hipEvent_t e0, e1;
+};
+bool g_timing = false;
+std::vector<TimingRec> g_timing_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// ---- DSV4_VALIDATE: synchronous host check of device-resident contents ------
+bool validate_enabled() {
+    const char* v = getenv("DSV4_VALIDATE");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+}
+
+template <typename T>
+dsv4_status fetch(const dsv4_tensor* t, std::vector<T>& host, int64_t rows, int64_t cols) {
+    host.assign((size_t)(rows * cols), T{});
+    const int64_t ld = t->ndim == 2 ? t->stride[0] : cols;
+    for (int64_t r = 0; r < rows; ++r)
+        DSV4_HIP(hipMemcpy(host.data() + r * cols, (const T*)t->data + r * ld, sizeof(T) * cols, hipMemcpyDeviceToHost));
+    return DSV4_OK;
+}
+
+dsv4_status validate_contents(const Metadata& md, const dsv4_tensor* swa_page_table,
+                              const dsv4_tensor* extra_page_table, const dsv4_tensor* c4_indices,
+                              const dsv4_tensor* seq_lens, const dsv4_tensor* qo_indptr, int64_t swa_pages,
+                              int64_t extra_pages, hipStream_t stream) {
+    DSV4_HIP(hipStreamSynchronize(stream));
+    std::vector<int32_t> sl, qo, st, et, c4;
+    DSV4_TRY(fetch(seq_lens, sl, 1, md.B));
+    DSV4_TRY(fetch(qo_indptr, qo, 1, md.B + 1));
+    DSV4_TRY(fetch(swa_page_table, st, md.B, md.P_swa));
+    if (md.R) DSV4_TRY(fetch(extra_page_table, et, md.B, md.P_extra));
+    if (md.R == 4) DSV4_TRY(fetch(c4_indices, c4, md.T, md.K));
+    if (qo[0] != 0) return fail(DSV4_ERR_CONTRACT, "qo_indptr[0] = %d, expected 0", qo[0]);
+    for (int r = 0; r < md.B; ++r)
+        if (qo[r + 1] < qo[r]) return fail(DSV4_ERR_CONTRACT, "qo_indptr decreases at %d", r);
+    if (qo[md.B] != md.T) return fail(DSV4_ERR_CONTRACT, "qo_indptr[B] = %d, expected T = %d", qo[md.B], md.T);
+    auto page_ok = [](const std::vector<int32_t>& tab, int64_t ld, int r, int64_t x, int64_t pages) {
+        const int64_t lp = x / DSV4_PAGE_SIZE;
+        if (lp >= ld) return false;
+        const int32_t pg = tab[(size_t)(r * ld + lp)];
+        return pg >= 0 && pg < pages;
+    };
+    for (int r = 0; r < md.B; ++r) {
+        const int64_t nq = qo[r + 1] - qo[r];
+        if (nq > sl[r]) return fail(DSV4_ERR_CONTRACT, "request %d: %lld rows but seq_len %d", r, (long long)nq, sl[r]);
+        for (int64_t t = qo[r]; t < qo[r + 1]; ++t) {
+            const int64_t p = sl[r] - nq + (t - qo[r]);
+            const int64_t lo = std::max<int64_t>(0, p - md.W + 1);
+            if (p < 0) return fail(DSV4_ERR_CONTRACT, "row %lld: negative position", (long long)t);
+            for (int64_t lp = lo / DSV4_PAGE_SIZE; lp <= p / DSV4_PAGE_SIZE; ++lp)
+                if (!page_ok(st, md.P_swa, r, lp * DSV4_PAGE_SIZE, swa_pages))
+                    return fail(DSV4_ERR_CONTRACT, "row %lld: SWA page %lld is not mapped", (long long)t,
+                                (long long)lp);
+            const int64_t vis = md.R ? (p + 1) / md.R : 0;
+            if (md.R == 4) {
+                for (int k = 0; k < md.K; ++k) {
+                    const int64_t c = c4[(size_t)(t * md.K + k)];
+                    if (c < -1 || c >= vis)
+                        return fail(DSV4_ERR_CONTRACT, "row %lld: C4 index %lld outside [-1, %lld)", (long long)t,
+                                    (long long)c, (long long)vis);
+                    if (c >= 0 && !page_ok(et, md.P_extra, r, c, extra_pages))
+                        return fail(DSV4_ERR_CONTRACT, "row %lld: C4 entry %lld has no page", (long long)t,
+                                    (long long)c);
+                }
+            } else if (md.R == 128) {
+                for (int64_t lp = 0; lp * DSV4_PAGE_SIZE < vis; ++lp)
+                    if (!page_ok(et, md.P_extra, r, lp * DSV4_PAGE_SIZE, extra_pages))
+                        return fail(DSV4_ERR_CONTRACT, "row %lld: C128 page %lld is not mapped", (long long)t,
+                                    (long long)lp);
+            }
+        }
+    }
+    return DSV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsv4_last_error(void) { return g_err.c_str(); }
+
+int32_t dsv4_abi_version(void) { return DSV4_ABI_VERSION; }
+
+dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
+    if (keys_per_split < 0 || keys_per_split % kTileKeys != 0 || keys_per_split > kMaxSplitKeys)
+        return fail(DSV4_ERR_INVALID, "keys_per_split must be 0 or a multiple of %d up to %d", kTileKeys,
+                    kMaxSplitKeys);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_force_split_keys = keys_per_split;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
+                           int32_t c4_width, int32_t extra_pages, int32_t* splits, int32_t* keys_per_split) {
+    if (splits == nullptr || keys_per_split == nullptr) return fail(DSV4_ERR_INVALID, "NULL output");
+    if (compress_ratio != 0 && compress_ratio != 4 && compress_ratio != 128)
+        return fail(DSV4_ERR_UNSUPPORTED, "invalid compress_ratio %d (must be 0, 4 or 128)", compress_ratio);
+    if (num_rows < 0 || num_heads < 1 || num_heads > 128 || window < 1)
+        return fail(DSV4_ERR_INVALID, "bad sizes");
+    int dev = 0;
+    int cus = 256;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (hipGetDevice(&dev) == hipSuccess) {
+        DeviceState* d = device_state(dev);
+        if (d) cus = d->cus;
+    }
+    plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages), splits,
+                keys_per_split);
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_attn_workspace_reserve(size_t bytes) {
+    int dev = 0;
+    DSV4_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_mu);
+    return ensure_workspace(device_state(dev), bytes);
+}
+
+void dsv4_attn_workspace_release(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (size_t i = 0; i < g_dev.size(); ++i) {
+        if (g_dev[i].ws == nullptr) continue;
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice((int)i) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(g_dev[i].ws);
+            (void)hipSetDevice(cur);
+        }
+        g_dev[i].ws = nullptr;
+        g_dev[i].ws_bytes = 0;
+    }
+}
+
+dsv4_status dsv4_attn_timing_enable(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_timing = enable != 0;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_attn_timing_read(double* kernel_ms, int64_t* calls) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    double a = 0.0;
+    for (TimingRec& r : g_timing_recs) {
+        DSV4_HIP(hipEventSynchronize(r.e1));
+        float x = 0.f;
+        DSV4_HIP(hipEventElapsedTime(&x, r.e0, r.e1));
+        a += x;
+        g_event_pool.push_back(r.e0);
+        g_event_pool.push_back(r.e1);
+    }
+    if (calls) *calls = (int64_t)g_timing_recs.size();
+    g_timing_recs.clear();
+    if (kernel_ms) *kernel_ms = a;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_attn_gather_slots(const dsv4_tensor* swa_page_table, const dsv4_tensor* extra_page_table,
+                                   const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,
+                                   const dsv4_tensor* qo_indptr, int32_t num_rows, int32_t compress_ratio,
+                                   int32_t window, const dsv4_tensor* slots, const dsv4_tensor* counts,
+                                   void* stream) {
+    if (num_rows < 0) return fail(DSV4_ERR_INVALID, "num_rows must be >= 0");
+    Metadata md;
+    DSV4_TRY(check_metadata(swa_page_table, extra_page_table, c4_indices, seq_lens, qo_indptr, num_rows,
+                            compress_ratio, window, &md));
+    const int64_t need = (int64_t)window + extra_bound(md.R, md.K, md.P_extra);
+    DSV4_TRY(check_tensor("slots", slots, DSV4_I32, 2, {num_rows, -1}));
+    if (slots->shape[1] < need)
+        return fail(DSV4_ERR_INVALID, "slots: width %lld below window + extra bound %lld", (long long)slots->shape[1],
+                    (long long)need);
+    DSV4_TRY(check_tensor("counts", counts, DSV4_I32, 2, {num_rows, 2}));
+    if (counts->stride[0] != 2) return fail(DSV4_ERR_INVALID, "counts must be contiguous");
+    if (num_rows == 0) return DSV4_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled())
+        DSV4_TRY(validate_contents(md, swa_page_table, extra_page_table, c4_indices, seq_lens, qo_indptr,
+                                   INT64_MAX, INT64_MAX, st));
+    GatherArgs g{};
+    g.m = md.m;
+    g.T = num_rows;
+    g.slots = (int32_t*)slots->data;
+    g.slots_ld = slots->stride[0];
+    g.counts = (int32_t*)counts->data;
+    if (g.slots_ld < slots->shape[1]) return fail(DSV4_ERR_INVALID, "slots: rows overlap");
+    DSV4_HIP(launch_gather(g, st));
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
+                              const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
+                              const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,
+                              const dsv4_tensor* qo_indptr, const dsv4_tensor* sink, int32_t compress_ratio,
+                              int32_t window, float scale, const dsv4_tensor* out, const dsv4_tensor* lse,
+                              void* stream) {
+    if (q == nullptr) return fail(DSV4_ERR_INVALID, "q: NULL descriptor");
+    DSV4_TRY(check_tensor("q", q, DSV4_BF16, 3, {-1, -1, DSV4_HEAD_DIM}));
+    const int64_t T = q->shape[0], H = q->shape[1];
+    if (q->stride[1] != 0 && H > 1 && q->stride[1] < DSV4_HEAD_DIM) return fail(DSV4_ERR_INVALID, "q: heads overlap");
+    if (H < 1 || H > 128) return fail(DSV4_ERR_INVALID, "q: %lld heads, expected 1..128", (long long)H);
+    if (T > (1 << 24)) return fail(DSV4_ERR_UNSUPPORTED, "q: more than 2^24 rows");
+    if (T > 0 && (q->stride[0] % 8 || q->stride[1] % 8 || !aligned16(q->data)))
+        return fail(DSV4_ERR_INVALID, "q: rows must be 16-byte aligned (strides multiple of 8)");
+    if (!std::isfinite(scale)) return fail(DSV4_ERR_INVALID, "scale must be finite");
+
+    Metadata md;
+    DSV4_TRY(check_metadata(swa_page_table, extra_page_table, c4_indices, seq_lens, qo_indptr, (int32_t)T,
+                            compress_ratio, window, &md));
+    PoolInfo swa{}, ext{};
+    DSV4_TRY(check_pool("swa_pool", swa_pool, &swa));
+    if (compress_ratio != 0) {
+        DSV4_TRY(check_pool("extra_pool", extra_pool, &ext));
+        if (ext.fp8 != swa.fp8)
+            return fail(DSV4_ERR_UNSUPPORTED, "swa_pool and extra_pool must use the same KV format");
+    }
+    if (sink != nullptr) DSV4_TRY(check_tensor("sink", sink, DSV4_F32, 1, {H}));
+    DSV4_TRY(check_tensor("out", out, DSV4_BF16, 3, {T, H, DSV4_HEAD_DIM}));
+    if (T > 0 && (out->stride[0] % 4 || out->stride[1] % 4 || (reinterpret_cast<uintptr_t>(out->data) & 7u)))
+        return fail(DSV4_ERR_INVALID, "out: rows must be 8-byte aligned (strides multiple of 4)");
+    if (lse != nullptr) DSV4_TRY(check_tensor("lse", lse, DSV4_F32, 2, {T, H}));
+    if (T == 0) return DSV4_OK;
+
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled())
+        DSV4_TRY(validate_contents(md, swa_page_table, extra_page_table, c4_indices, seq_lens, qo_indptr, swa.pages,
+                                   compress_ratio ? ext.pages : 0, st));
+
+    int dev = 0;
+    DSV4_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceState* d = device_state(dev);
+    DSV4_TRY(ensure_zero_row(d));
+
+    AttnArgs a{};
+    a.zero_row = (const uint8_t*)d->zero_row;
+    a.m = md.m;
+    a.q = (const uint16_t*)q->data;
+    a.q_s0 = q->stride[0];
+    a.q_s1 = q->stride[1];
+    a.swa_pool = (const uint8_t*)swa_pool->data;
+    a.swa_row_bytes = swa.row_bytes;
+    a.ext_pool = compress_ratio ? (const uint8_t*)extra_pool->data : a.swa_pool;
+    a.ext_row_bytes = compress_ratio ? ext.row_bytes : swa.row_bytes;
+    a.sink = sink ? (const float*)sink->data : nullptr;
+    a.T = (int32_t)T;
+    a.H = (int32_t)H;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), &a.splits, &a.chunk);
+    a.head_blocks = (int32_t)((H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    a.ext_pages = md.P_extra;
+    const int64_t n_items = (int64_t)a.T * a.head_blocks * a.splits;
+    if (n_items > (int64_t)1 << 30) return fail(DSV4_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)n_items);
+    a.n_items = (int32_t)n_items;
+    a.out = (uint16_t*)out->data;
+    a.out_s0 = out->stride[0];
+    a.out_s1 = out->stride[1];
+    a.lse = lse ? (float*)lse->data : nullptr;
+    a.lse_s0 = lse ? lse->stride[0] : 0;
+    if (a.splits > 1) {
+        const size_t n_part = (size_t)T * a.splits * H;
+        const size_t bytes_o = n_part * DSV4_HEAD_DIM * sizeof(float);
+        DSV4_TRY(ensure_workspace(d, bytes_o + n_part * sizeof(float)));
+        a.ws_o = (float*)d->ws;
+        a.ws_lse = (float*)((char*)d->ws + bytes_o);
+    }
+
+    TimingRec rec{};
+    if (g_timing) {
+        rec.e0 = take_event();
+        rec.e1 = take_event();
+        if (!rec.e0 || !rec.e1) return fail(DSV4_ERR_HIP, "hipEventCreate failed");
+        DSV4_HIP(hipEventRecord(rec.e0, st));
+    }
+    DSV4_HIP(launch_attention(a, swa.fp8, st));
+    if (a.splits > 1) DSV4_HIP(launch_merge(a, st));
+    if (g_timing) {
+        DSV4_HIP(hipEventRecord(rec.e1, st));
+        g_timing_recs.push_back(rec);
+    }
+    return DSV4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,751 @@
+// dsv4_attn_kernels.hip -- gfx950 kernels of the DeepSeek-V4 hybrid sparse MQA
+// decode / verify path.
+//
+//  * gather_kernel: the paged gather stage alone (canonical slot lists).
+//  * attn_dma_kernel (bf16 KV) and attn_regs_kernel (FP8 KV): gather + KV
+//    tile load (+ FP8 decode) + scores + online softmax + PV for one (query
+//    row, 64-head block, key split); with a single split they also apply the
+//    sink and write out / lse.
+//  * merge_kernel: log-sum-exp merge of the split partials with the per-head
+//    sink folded in once (test-matrix page, attention-sink correction).
+//    All 64 heads share each KV row (MQA with one KV head, walk-through page
+//    section 1), so a key tile is fetched from HBM once per workgroup into LDS
+//    and feeds both products on bf16 MFMA (v_mfma_f32_32x32x16_bf16):
+//        S^T[keys, heads]  = K[keys, d] . Q^T[d, heads]
+//        O^T[d, heads]    += K^T[d, keys] . P^T[keys, heads]      (V = K)
+//    The second product reduces over keys.  The bf16 kernel streams key rows
+//    straight from HBM into a 4-stage LDS ring (global_load_lds, 3 tiles in
+//    flight) and reads PV operands with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16).  The FP8 kernel stages rows through registers,
+//    decodes them, and writes the tile twice (row-major for S, 8-key columns
+//    for PV, via an in-register 8x8 transpose).
+//
+// Workgroup = 4 waves (256 lanes).  Wave w = 2*hh + dh owns heads
+// [32*hh, 32*hh+32) of the block and head dims [256*dh, 256*dh+256).  The two
+// dh waves of a head half each reduce S over their half of the dims and sum the
+// halves through LDS; both then run the same online softmax and accumulate O^T
+// for their own 256 dims (8 MFMA tiles of 32x32 = 128 fp32 accumulators).
+//
+// Work items (row, head block, split) are laid out so that consecutive
+// items -- the splits of one row -- go to the same XCD (workgroups are
+// dispatched to the 8 XCDs round robin), which keeps a row's Q in one L2.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "dsv4_launch.h"
+
+namespace dsv4 {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Tile-relative index of the e-th key (e = 0..7) loaded by wave w.  Wave w
+// owns the 8-key group G(w) = {16p + 4h + j, 16p + 8 + 4h + j : j < 4} with
+// p = w >> 1, h = w & 1: exactly the keys that lane half h of the score tile
+// holds for PV k-step p (see the MFMA output layout below), so the transposed
+// group feeds PV with no further shuffling.
+__device__ __forceinline__ int group_key(int w, int e) {
+    return 16 * (w >> 1) + 4 * (w & 1) + (e & 3) + 8 * (e >> 2);
+}
+
+// Row-major tile: 32 rows of 1 KiB; 16-byte chunk c of row k is stored at
+// chunk c ^ row_swz(k).  row_swz is a permutation of 0..15 over any 16
+// consecutive rows (and of 0..7 over any aligned 8), so row reads at one
+// column are conflict-free; it also gives the 4 rows x 2 adjacent chunks
+// that one transposing read touches 8 distinct bank slots.
+__device__ __forceinline__ int row_swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+__device__ __forceinline__ int krow_offset(int k, int chunk) { return k * 1024 + 16 * (chunk ^ row_swz(k)); }
+
+// Column tile: group g (8 keys) x 512 dims x 16 bytes; dim d is stored at
+// d ^ ((d >> 3) & 15), conflict-free for the transposing writes (lanes step
+// 8 dims) and for the PV reads (lanes step 1 dim).
+__device__ __forceinline__ int kt_offset(int g, int d) { return (g * 512 + (d ^ ((d >> 3) & 15))) * 16; }
+
+// Column i (dim 8l+i) of an 8x8 block of bf16: element j = row j's element i.
+__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&rows)[8], int i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_perm(rows[2 * k + 1][i >> 1], rows[2 * k][i >> 1], sel);
+    return c;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Four OCP E4M3FN codes (one per byte) -> four floats, exactly.  The code's
+// exponent/mantissa bits are moved into an IEEE half (same layout, bias 15
+// instead of 7): value(half) * 2^8 = value(e4m3), subnormals included.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
+    const uint32_t even = w & 0x00FF00FFu;          // bytes 0 and 2
+    const uint32_t odd = (w >> 8) & 0x00FF00FFu;    // bytes 1 and 3
+    const uint32_t he = ((even & 0x00800080u) << 8) | ((even & 0x007F007Fu) << 7);
+    const uint32_t ho = ((odd & 0x00800080u) << 8) | ((odd & 0x007F007Fu) << 7);
+    f[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(he & 0xFFFF));
+    f[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(he >> 16));
+    f[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ho & 0xFFFF));
+    f[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ho >> 16));
+}
+
+struct TileRegs {
+    u32x4 v[8];   // bf16: 8 dims of 8 keys; fp8 lanes < 56: 8 codes in v[e].xy
+    float sc[8];  // fp8 per-token scale of each key
+};
+
+
+// vmcnt-only wait (expcnt / lgkmcnt left at their maxima), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// LDS byte address lds_row + 16*i (M0 holds the wave-uniform base).  Issued
+// as inline asm so that the compiler does not treat every later LDS access
+// as dependent on it; callers wait with wait_vmcnt() and a barrier.  M0 is
+// saved and restored around the copy, with the one wait state the hardware
+// needs between an M0 write and an LDS-DMA instruction.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_row) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_row);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+struct Item {
+    int t, hb, s;
+};
+
+// Work item of this workgroup (XCD-aware: consecutive items -- the splits of
+// one row -- share an XCD, since workgroups go to the 8 XCDs round robin).
+__device__ __forceinline__ bool decode_item(const AttnArgs& a, Item& it) {
+    const int per_xcd = (a.n_items + 7) >> 3;
+    const int slot_in_xcd = blockIdx.x >> 3;
+    const int item = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
+    if (slot_in_xcd >= per_xcd || item >= a.n_items) return false;
+    it.s = item % a.splits;
+    const int th = item / a.splits;
+    it.hb = th % a.head_blocks;
+    it.t = th / a.head_blocks;
+    return true;
+}
+
+// Q^T as the B operand of S^T: lane holds head (l & 31) of the wave's half,
+// dims 256*dh + 16*j + 8*(l >> 5) .. +8 for k-step j (zeros past H).
+__device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, bool head_ok, int dh, int l,
+                                       bf16x8 (&qf)[16]) {
+    const uint16_t* qrow = a.q + (int64_t)t * a.q_s0 + (int64_t)(head_ok ? head : 0) * a.q_s1 + dh * 256 + 8 * (l >> 5);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        u32x4 v = head_ok ? *(const u32x4*)(qrow + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+        qf[j] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// Slot list of keys [k0, k0 + n_here) of row t into s_slot.  The page-table
+// row, the C4 indices and the window's page entries are fetched in one round;
+// compressed slots then resolve through the page-table row cached in LDS.
+__device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk, int t, int k0, int n_here,
+                                            int32_t* s_slot, int32_t* s_table, int tid) {
+    const bool cached_table = a.m.R != 0 && a.ext_pages <= kTableCap;
+    if (cached_table)
+        for (int i = tid; i < a.ext_pages; i += 256) s_table[i] = a.m.ext_table[(int64_t)rk.r * a.m.ext_ld + i];
+    int32_t v[kMaxSplitKeys / 256];
+#pragma unroll
+    for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
+        const int i = tid + 256 * u;
+        v[u] = -1;
+        if (i < n_here) {
+            const int e = k0 + i;
+            if (e < rk.n_swa) {
+                const int x = rk.swa_lo + e;
+                v[u] = a.m.swa_table[(int64_t)rk.r * a.m.swa_ld + (x >> 8)] * kPage + (x & (kPage - 1));
+            } else {
+                v[u] = a.m.R == 4 ? a.m.c4[(int64_t)t * a.m.c4_ld + (e - rk.n_swa)] : e - rk.n_swa;
+            }
+        }
+    }
+    __syncthreads();  // s_table ready
+    if (cached_table) {
+#pragma unroll
+        for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
+            const int i = tid + 256 * u;
+            if (i < n_here) {
+                int32_t slot = v[u];
+                if (k0 + i >= rk.n_swa && slot >= 0) slot = s_table[slot >> 8] * kPage + (slot & (kPage - 1));
+                s_slot[i] = slot;
+            }
+        }
+    } else {
+        const int32_t* row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
+#pragma unroll
+        for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
+            const int i = tid + 256 * u;
+            if (i < n_here) {
+                int32_t slot = v[u];
+                if (k0 + i >= rk.n_swa && slot >= 0) slot = row[slot >> 8] * kPage + (slot & (kPage - 1));
+                s_slot[i] = slot;
+            }
+        }
+    }
+    __syncthreads();  // slot list ready
+}
+
+// Sum the S^T partials of the two waves that share a head half (they cover
+// the two dim halves).  Layout [wave][chunk][lane] in 16-byte units keeps the
+// 16-byte accesses of consecutive lanes contiguous (no bank conflicts).
+__device__ __forceinline__ void exchange_partial(float* s_sx, int w, int l, f32x16& sacc) {
+    f32x4* mine = (f32x4*)s_sx + w * 256 + l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    __syncthreads();
+    const f32x4* other = (const f32x4*)s_sx + (w ^ 1) * 256 + l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 o = other[64 * q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[4 * q + j] += o[j];
+    }
+}
+
+// Multiply every output accumulator by alpha in place.  Each register is
+// read out of the accumulation file, scaled and written back by one short
+// asm sequence, so the accumulators never have to live in VGPRs (letting the
+// compiler do it makes the register allocator spill the whole tile).
+// Wait states: one between the read-out and its VALU use, and a few before
+// any later MFMA reads the rewritten registers.
+template <int NB>
+__device__ __forceinline__ void scale_accumulators(f32x16 (&oacc)[NB], float alpha) {
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float x = oacc[mb][e];
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "s_nop 1\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha));
+            oacc[mb][e] = x;
+        }
+    asm volatile("s_nop 4");
+}
+
+// Online-softmax step for one 32-key tile (base 2).  `sacc` holds this
+// wave's S^T accumulators already summed over all 512 dims: register r is
+// head (l & 31), tile key 8*(r >> 2) + 4*(l >> 5) + (r & 3).  Produces the
+// bf16 P^T operands of the two PV k-steps.  The running reference only moves
+// when a score exceeds it by more than 2^8 (probabilities stay <= 256), so
+// the 128 output accumulators are rescaled on a tiny fraction of tiles.
+template <bool kFp8>
+__device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask, float scale_log2, int l,
+                                             const float (&sc_key)[16], float& m_run, float& l_run,
+                                             f32x16 (&oacc)[8], bf16x8 (&pb)[2], bf16x8 (&pbs)[2]) {
+    float sv[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const float x = s_all[r] * scale_log2;
+        sv[r] = ((vmask >> key) & 1ull) ? x : -INFINITY;
+        tmax = fmaxf(tmax, sv[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool grow = tmax > m_run + kRescaleLog2;
+    if (__any(grow)) {
+        const float m_target = grow ? tmax : m_run;
+        const float alpha = fast_exp2(m_run - m_target);  // 0 while nothing was accumulated
+        if (__any(grow && m_run != -INFINITY)) {
+            scale_accumulators(oacc, alpha);
+        }
+        l_run *= alpha;
+        m_run = m_target;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float pr = fast_exp2(sv[r] - m_use);
+        psum += pr;
+        pb[r >> 3][r & 7] = (__bf16)pr;
+        if constexpr (kFp8) pbs[r >> 3][r & 7] = (__bf16)(pr * sc_key[r]);
+    }
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+}
+
+// Epilogue.  Accumulator r of tile mb holds head (l & 31) of the wave's half,
+// dim 256*dh + 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3).  One split: apply
+// the sink and write out / lse.  Several: publish the normalised partial and
+// its base-2 log-sum-exp (-inf for an empty split) for merge_kernel.
+__device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int my_head, bool head_ok, int dh,
+                                             int l, const f32x16 (&oacc)[8], float m_run, float l_run) {
+    if (!head_ok) return;
+    if (a.splits == 1) {
+        const float sig = a.sink != nullptr ? a.sink[my_head] * kLog2e : -INFINITY;
+        const float M = fmaxf(m_run, sig);
+        float f = 0.f, lse2 = -INFINITY;
+        if (M != -INFINITY) {
+            const float em = fast_exp2(m_run - M);
+            const float den = l_run * em + fast_exp2(sig - M);
+            f = em / den;
+            lse2 = M + fast_log2(den);
+        }
+        uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)my_head * a.out_s1;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = dh * 256 + 32 * mb + 8 * qd + 4 * (l >> 5);
+                const f32x16& o = oacc[mb];
+                u32x2 v = {pack_bf16x2(o[4 * qd] * f, o[4 * qd + 1] * f), pack_bf16x2(o[4 * qd + 2] * f, o[4 * qd + 3] * f)};
+                *(u32x2*)(orow + d) = v;
+            }
+        }
+        if (a.lse != nullptr && dh == 0 && l < 32) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
+        return;
+    }
+    const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + my_head;
+    if (l_run > 0.f) {
+        const float inv = 1.f / l_run;
+        float* orow = a.ws_o + part * kHeadDim;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int d = dh * 256 + 32 * mb + 8 * qd + 4 * (l >> 5);
+                const f32x16& o = oacc[mb];
+                f32x4 v = {o[4 * qd] * inv, o[4 * qd + 1] * inv, o[4 * qd + 2] * inv, o[4 * qd + 3] * inv};
+                *(f32x4*)(orow + d) = v;
+            }
+        }
+    }
+    if (dh == 0 && l < 32) a.ws_lse[part] = l_run > 0.f ? m_run + fast_log2(l_run) : -INFINITY;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Gather stage on its own: one workgroup per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
+    __shared__ int wave_count[4];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const RowKeys rk = row_keys(g.m, t, tid & 63);
+    int32_t* out = g.slots + (int64_t)t * g.slots_ld;
+    for (int i = tid; i < rk.n_swa; i += 256) out[i] = list_slot(g.m, rk, t, i);
+    int n_ext = 0;
+    if (g.m.R == 128) {
+        for (int e = tid; e < rk.n_ext; e += 256) out[rk.n_swa + e] = list_slot(g.m, rk, t, rk.n_swa + e);
+        n_ext = rk.n_ext;
+    } else if (g.m.R == 4) {
+        // Stream compaction of the used C4 entries, keeping list order.
+        const int lane = tid & 63, w = tid >> 6;
+        for (int base = 0; base < rk.n_ext; base += 256) {
+            const int e = base + tid;
+            int32_t slot = -1;
+            if (e < rk.n_ext) slot = list_slot(g.m, rk, t, rk.n_swa + e);
+            const bool used = slot >= 0;
+            const uint64_t ball = __ballot(used);
+            const int before = __popcll(ball & ((1ull << lane) - 1ull));
+            if (lane == 0) wave_count[w] = __popcll(ball);
+            __syncthreads();
+            int off = n_ext;
+            for (int j = 0; j < w; ++j) off += wave_count[j];
+            if (used) out[rk.n_swa + off + before] = slot;
+            const int total = wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
+            __syncthreads();
+            n_ext += total;
+        }
+    }
+    for (int i = rk.n_swa + n_ext + tid; i < g.slots_ld; i += 256) out[i] = -1;
+    if (tid == 0) {
+        g.counts[2 * t] = rk.n_swa;
+        g.counts[2 * t + 1] = n_ext;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 KV: key rows stream from HBM into a 4-stage LDS ring with direct
+// global->LDS loads (no VGPR staging), three tiles in flight per workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
+    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
+    __shared__ int32_t s_slot[kMaxSplitKeys];
+    __shared__ int32_t s_table[kTableCap];
+
+    Item it;
+    if (!decode_item(a, it)) return;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63;
+    const int hh = w >> 1, dh = w & 1;
+    const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
+    const bool head_ok = my_head < a.H;
+
+    bf16x8 qf[16];
+    load_q(a, it.t, my_head, head_ok, dh, l, qf);
+
+    const RowKeys rk = row_keys(a.m, it.t, l);
+    const int k0 = it.s * a.chunk;
+    const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
+    build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+
+    // Wave w fetches tile keys 8w .. 8w+7; lane l moves 16 bytes of a row.
+    // Lane l reads logical chunk l ^ row_swz(k) so that the row lands in the
+    // swizzled layout of krow_offset.  Unused keys read the zero row.
+    // The wave's 8 slots are read first (two 16-byte LDS reads) and all 8
+    // copies are then issued back to back.
+    auto fetch_tile = [&](int tile) {
+        uint8_t* dst = &s_tile[tile % kStages][0];
+        const int i0 = tile * kTileKeys + 8 * w;
+        const i32x4 sa = *(const i32x4*)&s_slot[i0];
+        const i32x4 sb = *(const i32x4*)&s_slot[i0 + 4];
+        const uint8_t* src[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = i0 + e;
+            const int32_t slot = i < n_here ? (e < 4 ? sa[e] : sb[e - 4]) : -1;
+            const int k = 8 * w + e;
+            const bool swa = k0 + i < rk.n_swa;
+            src[e] = (slot >= 0 ? (swa ? a.swa_pool : a.ext_pool) + (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes)
+                                : a.zero_row) +
+                     16 * (l ^ row_swz(k));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dma16(src[e], lds_addr(dst + (8 * w + e) * 1024));
+    };
+
+    f32x16 oacc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float no_scale[16] = {};
+
+    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
+    // Retire every compiler-visible load (Q, slot metadata) first, so the only
+    // vector-memory operations in flight below are this wave's row copies
+    // (8 per tile) and the explicit vmcnt waits count exactly those.
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+        if (p < n_tiles) fetch_tile(p);
+
+    for (int i = 0; i < n_tiles; ++i) {
+        // Tiles i+1 and i+2 may still be in flight; wait for this wave's rows of tile i.
+        const int newer = min(kStages - 2, n_tiles - 1 - i);
+        if (newer >= 2) wait_vmcnt<16>();
+        else if (newer == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        const int kv = i * kTileKeys + (l & 31);
+        const bool valid = l < 32 && kv < n_here && s_slot[kv] >= 0;
+        const uint64_t vmask = __ballot(valid);
+        __syncthreads();  // tile i is in LDS for every wave; stage (i-1) % kStages is free
+        if (i + kStages - 1 < n_tiles) fetch_tile(i + kStages - 1);
+
+        const uint8_t* tile = &s_tile[i % kStages][0];
+        // S^T partial over this wave's 256 dims (operands read ahead of the MFMAs).
+        f32x16 sacc = f32x16{};
+        {
+            const int k = l & 31;
+            bf16x8 av[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) av[j] = *(const bf16x8*)(tile + krow_offset(k, dh * 32 + 2 * j + (l >> 5)));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
+        }
+        exchange_partial(s_sx, w, l, sacc);
+
+        bf16x8 pb[2], pbs[2];
+        softmax_tile<false>(sacc, vmask, a.scale_log2, l, no_scale, m_run, l_run, oacc, pb, pbs);
+
+        // O^T[d, heads] += K^T[d, keys] P^T[keys, heads].  The K^T operand of
+        // lane L (dim 32*mb + (L & 31), keys G(pp, L >> 5)) comes from two
+        // transposing reads: source lane S of each 16-lane block points at key
+        // row r_k (k = (S >> 2) & 3) and dims d0 .. d0+3, d0 = 16*((S >> 4) & 1)
+        // + 4*(S & 3); the block returns dim d0 + j of rows r_0..r_3 to lane
+        // 4*(S & 3) + j.
+        {
+            const int a4 = l & 3, kq = (l >> 2) & 3, hq = l >> 5, half = (l >> 4) & 1;
+            bf16x8 kt[16];
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+                const int d0 = dh * 256 + 32 * mb + 16 * half + 4 * a4;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int r0 = 16 * pp + 4 * hq + kq;
+                    const int r1 = r0 + 8;
+                    const uint8_t* p0 = tile + krow_offset(r0, d0 >> 3) + 2 * (d0 & 7);
+                    const uint8_t* p1 = tile + krow_offset(r1, d0 >> 3) + 2 * (d0 & 7);
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+                    kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp)
+                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
+        }
+    }
+    write_result(a, it, my_head, head_ok, dh, l, oacc, m_run, l_run);
+}
+
+// ---------------------------------------------------------------------------
+// Packed FP8 KV: rows staged through registers (one tile ahead), decoded, and
+// written to LDS row-major and as 8-key columns.  E4M3 codes are exact in
+// bf16; the per-token scale multiplies the fp32 non-rotary score partial and
+// is folded into P for the non-rotary PV tiles.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void attn_regs_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_krow[kTileKeys * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t s_kt[4 * 512 * 16];
+    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
+    __shared__ int32_t s_slot[kMaxSplitKeys];
+    __shared__ int32_t s_table[kTableCap];
+    __shared__ __attribute__((aligned(16))) float s_scale[kTileKeys];
+
+    Item it;
+    if (!decode_item(a, it)) return;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63;
+    const int hh = w >> 1, dh = w & 1;
+    const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
+    const bool head_ok = my_head < a.H;
+
+    bf16x8 qf[16];
+    load_q(a, it.t, my_head, head_ok, dh, l, qf);
+
+    const RowKeys rk = row_keys(a.m, it.t, l);
+    const int k0 = it.s * a.chunk;
+    const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
+    build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+
+    TileRegs pre;
+    auto issue_loads = [&](int tb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = tb + group_key(w, e);
+            const int32_t slot = i < n_here ? s_slot[i] : -1;
+            pre.v[e] = u32x4{0u, 0u, 0u, 0u};
+            pre.sc[e] = 0.f;
+            if (slot >= 0) {
+                const bool swa = k0 + i < rk.n_swa;
+                const uint8_t* page = (swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
+                const int rec = slot & 255;
+                const uint8_t* row = page + rec * kFp8RecBytes;
+                if (l < 56) {
+                    const u32x2 c = *(const u32x2*)(row + 8 * l);
+                    pre.v[e] = u32x4{c[0], c[1], 0u, 0u};
+                } else {
+                    pre.v[e] = *(const u32x4*)(row + kNope + 16 * (l - 56));
+                }
+                pre.sc[e] = *(const float*)(page + kFp8ScaleOffset + 4 * rec);
+            }
+        }
+    };
+
+    auto commit_tile = [&]() {
+        u32x4 rows[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (l < 56) {
+                float lo[4], hi[4];
+                e4m3x4_to_f32(pre.v[e][0], lo);
+                e4m3x4_to_f32(pre.v[e][1], hi);
+                rows[e] = u32x4{pack_bf16x2(lo[0] * 256.0f, lo[1] * 256.0f), pack_bf16x2(lo[2] * 256.0f, lo[3] * 256.0f),
+                                pack_bf16x2(hi[0] * 256.0f, hi[1] * 256.0f), pack_bf16x2(hi[2] * 256.0f, hi[3] * 256.0f)};
+            } else {
+                rows[e] = pre.v[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *(u32x4*)(s_krow + krow_offset(group_key(w, e), l)) = rows[e];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *(u32x4*)(s_kt + kt_offset(w, 8 * l + i)) = transpose_col(rows, i);
+        if (l == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_scale[group_key(w, e)] = pre.sc[e];
+        }
+    };
+
+    f32x16 oacc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    if (n_here > 0) issue_loads(0);
+    for (int tb = 0; tb < n_here; tb += kTileKeys) {
+        commit_tile();
+        if (tb + kTileKeys < n_here) issue_loads(tb + kTileKeys);
+        const int kv = tb + (l & 31);
+        const bool valid = l < 32 && kv < n_here && s_slot[kv] >= 0;
+        const uint64_t vmask = __ballot(valid);
+        __syncthreads();
+
+        // S^T partial over this wave's 256 dims; non-rotary k-steps (dims < 448)
+        // and the rotary k-steps of the dh = 1 wave (j >= 12) accumulate apart.
+        f32x16 sacc = f32x16{};
+        float sc_key[16];
+        {
+            const int k = l & 31;
+            f32x16 sacc_r = f32x16{};
+            bf16x8 av[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) av[j] = *(const bf16x8*)(s_krow + krow_offset(k, dh * 32 + 2 * j + (l >> 5)));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (dh == 1 && j >= 12)
+                    sacc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc_r, 0, 0, 0);
+                else
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const f32x4 sc4 = *(const f32x4*)(s_scale + 8 * qd + 4 * (l >> 5));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc_key[4 * qd + j] = sc4[j];
+                    sacc[4 * qd + j] = sacc[4 * qd + j] * sc4[j] + sacc_r[4 * qd + j];
+                }
+            }
+        }
+        exchange_partial(s_sx, w, l, sacc);
+
+        bf16x8 pb[2], pbs[2];
+        softmax_tile<true>(sacc, vmask, a.scale_log2, l, sc_key, m_run, l_run, oacc, pb, pbs);
+
+        {
+            bf16x8 kt[16];
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp)
+                    kt[2 * mb + pp] = *(const bf16x8*)(s_kt + kt_offset(2 * pp + (l >> 5), dh * 256 + 32 * mb + (l & 31)));
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+                const bool nope = dh == 0 || mb < 6;  // dims < 448
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp)
+                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], nope ? pbs[pp] : pb[pp], oacc[mb], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    write_result(a, it, my_head, head_ok, dh, l, oacc, m_run, l_run);
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split partials + sink: one wave per (row, head), 8 dims per lane;
+// every split's lse and partial row are loaded before any is combined, so a
+// row's merge costs one round of loads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+    constexpr int kMaxSplitsPerPass = 16;
+    const int t = blockIdx.x;
+    const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (head >= a.H) return;
+    const int S = a.splits;
+    const float* lp = a.ws_lse + (int64_t)t * S * a.H + head;
+    const float* ob = a.ws_o + ((int64_t)t * S * a.H + head) * kHeadDim + 8 * l;
+    const int64_t ostride = (int64_t)a.H * kHeadDim;
+    const float sig = a.sink != nullptr ? a.sink[head] * kLog2e : -INFINITY;
+    float M = sig;
+    for (int k = l; k < S; k += 64) M = fmaxf(M, lp[(int64_t)k * a.H]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float Z = 0.f;
+    if (M != -INFINITY) {
+        Z = fast_exp2(sig - M);
+        for (int k0 = 0; k0 < S; k0 += kMaxSplitsPerPass) {
+            float wgt[kMaxSplitsPerPass];
+            f32x4 x0[kMaxSplitsPerPass], x1[kMaxSplitsPerPass];
+#pragma unroll
+            for (int j = 0; j < kMaxSplitsPerPass; ++j) {
+                const int k = k0 + j;
+                const float v = k < S ? lp[(int64_t)k * a.H] : -INFINITY;
+                wgt[j] = v == -INFINITY ? 0.f : fast_exp2(v - M);
+                x0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                x1[j] = x0[j];
+                if (wgt[j] != 0.f) {  // an empty split never wrote its partial
+                    x0[j] = *(const f32x4*)(ob + k * ostride);
+                    x1[j] = *(const f32x4*)(ob + k * ostride + 4);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kMaxSplitsPerPass; ++j) {
+                Z += wgt[j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[e] += wgt[j] * x0[j][e];
+                    acc[4 + e] += wgt[j] * x1[j][e];
+                }
+            }
+        }
+    }
+    const float f = Z > 0.f ? 1.f / Z : 0.f;
+    uint16_t* orow = a.out + (int64_t)t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
+    u32x4 v = {pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f),
+               pack_bf16x2(acc[4] * f, acc[5] * f), pack_bf16x2(acc[6] * f, acc[7] * f)};
+    *(u32x4*)orow = v;
+    if (a.lse != nullptr && l == 0)
+        a.lse[(int64_t)t * a.lse_s0 + head] = (M == -INFINITY) ? -INFINITY : (M + fast_log2(Z)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t stream) {
+    const int per_xcd = (a.n_items + 7) / 8;
+    const dim3 grid((unsigned)(8 * per_xcd));
+    if (fp8)
+        hipLaunchKernelGGL(attn_regs_kernel, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(attn_dma_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.T, (unsigned)((a.H + 3) / 4));
+    hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& g, hipStream_t stream) {
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)g.T), dim3(256), 0, stream, g);
+    return hipGetLastError();
+}
+
+}  // namespace dsv4

@@ -1,0 +1,55 @@
+// dsv4_launch.h -- argument blocks and launch entry points of the HIP kernels
+// (internal to the library; the public ABI is include/dsv4_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsv4_device.h"
+
+namespace dsv4 {
+
+constexpr int kTileKeys = 32;        // keys per LDS tile
+constexpr int kMaxSplitKeys = 1024;  // keys one workgroup may own (LDS slot list)
+constexpr int kHeadsPerBlock = 64;   // query heads per workgroup (two halves of 32)
+constexpr int kTableCap = 1024;      // extra page-table entries a workgroup caches in LDS
+constexpr int kStages = 4;           // bf16 key tiles resident in LDS (3 in flight + 1 in use)
+
+struct AttnArgs {
+    Meta m;
+    const uint16_t* q;  // bf16 [T, H, 512]
+    int64_t q_s0, q_s1;
+    const uint8_t* swa_pool;  // bf16 rows or packed FP8 pages
+    int64_t swa_row_bytes;    // bf16: bytes between rows (>= 1024)
+    const uint8_t* ext_pool;
+    int64_t ext_row_bytes;
+    const float* sink;        // [H] or null
+    int32_t T, H;
+    float scale_log2;         // scale * log2(e)
+    int32_t chunk;            // keys per split (multiple of kTileKeys)
+    int32_t splits;           // splits per (row, head block)
+    int32_t head_blocks;      // ceil(H / 64)
+    int32_t n_items;          // T * head_blocks * splits work items
+    int32_t ext_pages;        // extra page-table width (0 when R == 0)
+    uint16_t* out;            // bf16 [T, H, 512]
+    int64_t out_s0, out_s1;
+    float* lse;               // [T, H] or null
+    int64_t lse_s0;
+    float* ws_o;              // [T, splits, H, 512] normalised partial outputs
+    float* ws_lse;            // [T, splits, H] base-2 partial log-sum-exp
+    const uint8_t* zero_row;  // >= 1 KiB of zeros, read in place of unused keys
+};
+
+struct GatherArgs {
+    Meta m;
+    int32_t T;
+    int32_t* slots;  // [T, slots_ld]
+    int64_t slots_ld;
+    int32_t* counts;  // [T, 2]
+};
+
+hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& g, hipStream_t stream);
+
+}  // namespace dsv4

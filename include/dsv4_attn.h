@@ -1,0 +1,192 @@
+/*
+ * dsv4_attn.h -- C ABI of the MI355X (gfx950) DeepSeek-V4 hybrid sparse MQA
+ * attention library, decode and target-verify.
+ *
+ * The operation (sources: "SGLang DeepSeek-V4 attention test capability
+ * matrix" page; "DeepSeek-V4 Attention: Query, cache write and history
+ * addressing" page; the Day-0 overview page, section "what V4 changed"):
+ *
+ *   Query row t of request r sits at position p = seq_lens[r] - n_q + (t -
+ *   qo_indptr[r]), n_q = qo_indptr[r+1] - qo_indptr[r] (walk-through, sections
+ *   1 and 4).  Its keys are the sliding window x = max(0, p-W+1) .. p of the
+ *   SWA cache, followed by, for compress_ratio R (overview "hybrid sparse
+ *   attention"; walk-through section 5):
+ *     R = 0   -- nothing;
+ *     R = 4   -- the C4 entries named by c4_indices[t][0..K-1] (-1 = none),
+ *                every named entry must be visible: 0 <= c < (p+1)/4;
+ *     R = 128 -- every visible C128 entry c = 0 .. (p+1)/128 - 1.
+ *   Logical position x (token or compressed entry) of request r lives in slot
+ *   table[r][x / 256] * 256 + x % 256 of its pool (page size 256, asserted by
+ *   the test-matrix page).  One KV head serves all H query heads and the value
+ *   of a key is the key row itself (V = K, walk-through section 3).  A per-head
+ *   sink logit joins the softmax as a virtual key with value zero (test-matrix
+ *   page, "attention-sink correction"); it is NOT multiplied by `scale`:
+ *
+ *     s_k   = scale * <q[t,h,:], K_k>
+ *     out   = sum_k e^{s_k} K_k / (sum_k e^{s_k} + e^{sink[h]})
+ *     lse   = ln(sum_k e^{s_k} + e^{sink[h]})          (natural log)
+ *
+ * Head geometry: 512 = 448 non-rotary + 64 rotary dims (test-matrix page,
+ * "input and config coverage"); Q arrives with RoPE applied, and the output
+ * keeps the rotary dims (inverse RoPE comes after attention).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are non-owning descriptors; the caller keeps ownership of all
+ *    memory and of the stream.  No pointer is retained after return.
+ *  - Device pointers unless stated.  Shapes/strides are in elements; the last
+ *    dimension must be contiguous (stride 1).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *    The host never reads device memory, so seq_lens, qo_indptr, page tables
+ *    and indices may change between calls without a host sync.
+ *  - Host-checkable errors (shape, dtype, stride, NULL, unsupported option)
+ *    return before any launch with a message in dsv4_last_error().  Device
+ *    contents (index ranges, page ids, qo_indptr[B] == T, n_q <= seq_len) are
+ *    a caller contract; with DSV4_VALIDATE=1 in the environment the library
+ *    copies them to the host (synchronously) and checks them first.
+ *  - Calls on one device that share the library workspace must not overlap
+ *    (serialise them on one stream or across streams).
+ */
+#ifndef DSV4_ATTN_H_
+#define DSV4_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSV4_ABI_VERSION 1
+
+/* Element types of a descriptor. */
+enum {
+    DSV4_BF16 = 1, /* bfloat16, 2 bytes */
+    DSV4_F32 = 2,  /* float32 */
+    DSV4_I32 = 3,  /* int32 */
+    DSV4_U8 = 4    /* raw bytes (packed FP8 KV pages) */
+};
+
+typedef enum {
+    DSV4_OK = 0,
+    DSV4_ERR_INVALID = 1,     /* bad shape, dtype, stride, NULL, range */
+    DSV4_ERR_UNSUPPORTED = 2, /* compress_ratio not in {0,4,128}, mixed pool formats, ... */
+    DSV4_ERR_WORKSPACE = 3,   /* workspace allocation failed */
+    DSV4_ERR_HIP = 4,         /* a HIP runtime call or launch failed */
+    DSV4_ERR_CONTRACT = 5     /* DSV4_VALIDATE=1 found a device-content violation */
+} dsv4_status;
+
+typedef struct dsv4_tensor {
+    void* data;
+    int32_t dtype;     /* DSV4_* */
+    int32_t ndim;      /* 1..4 */
+    int64_t shape[4];
+    int64_t stride[4]; /* in elements */
+} dsv4_tensor;
+
+/*
+ * KV pool formats (both pools of one call must use the same one):
+ *  - bf16:  DSV4_BF16 [S, 512], S = pages * 256, row stride a multiple of 8.
+ *  - fp8:   DSV4_U8 [pages, 149504] contiguous.  Each 256-token page holds 256
+ *           records of 576 bytes [448 x OCP E4M3FN non-rotary | 64 x bf16
+ *           rotary], then 256 fp32 per-token scales (non-rotary value = code x
+ *           scale), then 1 KiB of padding: 584 bytes per token (test-matrix
+ *           page, "packed FP8 nope + BF16 rope", 584 bytes/token).
+ */
+#define DSV4_HEAD_DIM 512
+#define DSV4_PAGE_SIZE 256
+#define DSV4_FP8_PAGE_BYTES 149504
+
+/*
+ * dsv4_attn_forward -- SWA + (C4 | C128) attention for all query rows in one
+ * call (overview page, kernel section: one call covers SWA and the extra
+ * attention with shared metadata).
+ *
+ *  q                bf16 [T, H, 512], 1 <= H <= 128, inner strides multiples of 8
+ *  swa_pool         KV pool (format above) holding the SWA cache
+ *  swa_page_table   i32 [B, P_swa]: logical page x/256 -> physical page
+ *  extra_pool       KV pool of compressed entries; ignored (may be NULL) if R == 0
+ *  extra_page_table i32 [B, P_extra]; ignored (may be NULL) if R == 0
+ *  c4_indices       i32 [T, K] logical compressed positions, -1 = unused;
+ *                   required iff R == 4, ignored otherwise
+ *  seq_lens         i32 [B]: total length including this pass's rows
+ *  qo_indptr        i32 [B+1]: qo_indptr[0] = 0, non-decreasing, [B] = T
+ *  sink             f32 [H] logits, or NULL (no sink)
+ *  compress_ratio   0, 4 or 128 (else DSV4_ERR_UNSUPPORTED)
+ *  window           W >= 1 (128 in DeepSeek-V4)
+ *  scale            multiplies q.k (e.g. 512^-0.5); not applied to sink
+ *  out              bf16 [T, H, 512], written (round to nearest even)
+ *  lse              f32 [T, H] natural-log normaliser including the sink, or NULL
+ *  stream           hipStream_t
+ */
+dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
+                              const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
+                              const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,
+                              const dsv4_tensor* qo_indptr, const dsv4_tensor* sink, int32_t compress_ratio,
+                              int32_t window, float scale, const dsv4_tensor* out, const dsv4_tensor* lse,
+                              void* stream);
+
+/*
+ * dsv4_attn_gather_slots -- the paged gather stage on its own: for every row,
+ * the physical slots the attention reads, in canonical order (SWA positions
+ * ascending, then C4 entries in index-list order with -1 skipped, or C128
+ * entries ascending).  Same metadata arguments and contract as
+ * dsv4_attn_forward (reference: the per-q-token SWA / C4 / C128 page-index
+ * metadata of the test-matrix page, "reference implementation notes").
+ *
+ *  num_rows  T (rows of c4_indices / of the pass)
+ *  slots     i32 [T, Kmax], Kmax >= window + (R==4 ? K : R==128 ? 256*P_extra : 0);
+ *            entries past the row's count are set to -1
+ *  counts    i32 [T, 2]: (number of SWA slots, number of extra slots)
+ */
+dsv4_status dsv4_attn_gather_slots(const dsv4_tensor* swa_page_table, const dsv4_tensor* extra_page_table,
+                                   const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,
+                                   const dsv4_tensor* qo_indptr, int32_t num_rows, int32_t compress_ratio,
+                                   int32_t window, const dsv4_tensor* slots, const dsv4_tensor* counts,
+                                   void* stream);
+
+/* Message of the last non-OK return on this thread ("" if none). */
+const char* dsv4_last_error(void);
+
+/* ABI version of the loaded library (DSV4_ABI_VERSION). */
+int32_t dsv4_abi_version(void);
+
+/*
+ * Library workspace for split-KV partial results, one per device, grown on
+ * demand by dsv4_attn_forward (hipMalloc, which
+ * synchronises the device; call once with the largest sizes before capturing
+ * a HIP graph).
+ * dsv4_attn_workspace_reserve pre-allocates at least `bytes` on the current
+ * device; dsv4_attn_workspace_release frees it after synchronising.
+ */
+dsv4_status dsv4_attn_workspace_reserve(size_t bytes);
+void dsv4_attn_workspace_release(void);
+
+/*
+ * Tuning / test hook: force the number of keys handled by one split
+ * (a positive multiple of 32), or 0 for the automatic plan.  Process-wide.
+ */
+dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
+
+/*
+ * Plan that dsv4_attn_forward would use for these sizes: number of splits
+ * per row and keys per split.  Host-only, no device access.
+ */
+dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
+                           int32_t c4_width, int32_t extra_pages, int32_t* splits, int32_t* keys_per_split);
+
+/*
+ * Kernel timing on the caller's stream with HIP events.  While enabled, every
+ * dsv4_attn_forward records an event before its first kernel and after its
+ * last one (the split kernel, and the merge kernel when a row is split).
+ * dsv4_attn_timing_read waits for the recorded events, returns the summed
+ * milliseconds and the number of calls recorded, then clears the record.
+ * Do not enable while capturing a HIP graph.
+ */
+dsv4_status dsv4_attn_timing_enable(int32_t enable);
+dsv4_status dsv4_attn_timing_read(double* kernel_ms, int64_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV4_ATTN_H_ */

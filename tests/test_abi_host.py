@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI (CPU only, nothing is launched).
+
+* the library loads and exports every function include/dsv4_attn.h declares;
+* every argument error is reported with its status code and a message before
+  any device work (descriptors carry dummy device pointers that the host side
+  must never dereference).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HEADER = os.path.join(ROOT, "include", "dsv4_attn.h")
+
+from hybrid_sparse_mqa_amd import _native as N  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(N.LIB_PATH), reason="HIP library not built")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FAKE = 0x7F0000000000  # never dereferenced by the host side
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsv4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.load()
+    names = declared_functions()
+    assert "dsv4_attn_forward" in names and "dsv4_attn_gather_slots" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+
+
+def test_abi_version():
+    assert N.load().dsv4_abi_version() == 1
+
+
+def desc(dtype, shape, stride=None, data=FAKE):
+    d = N.Tensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride = [1] * len(shape)
+        for i in range(len(shape) - 2, -1, -1):
+            stride[i] = stride[i + 1] * shape[i + 1]
+    for i, (s, st) in enumerate(zip(shape, stride)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def base_args(R=4, T=4, H=64, B=2, K=512, fp8=False):
+    pool = desc(N.DSV4_U8, [8, 149504]) if fp8 else desc(N.DSV4_BF16, [8 * 256, 512])
+    return dict(
+        q=desc(N.DSV4_BF16, [T, H, 512]),
+        swa_pool=pool,
+        swa_page_table=desc(N.DSV4_I32, [B, 4]),
+        extra_pool=pool if R else None,
+        extra_page_table=desc(N.DSV4_I32, [B, 3]) if R else None,
+        c4_indices=desc(N.DSV4_I32, [T, K]) if R == 4 else None,
+        seq_lens=desc(N.DSV4_I32, [B]),
+        qo_indptr=desc(N.DSV4_I32, [B + 1]),
+        sink=desc(N.DSV4_F32, [H]),
+        compress_ratio=R,
+        window=128,
+        scale=512 ** -0.5,
+        out=desc(N.DSV4_BF16, [T, H, 512]),
+        lse=desc(N.DSV4_F32, [T, H]),
+    )
+
+
+def call(**kw):
+    L = N.load()
+    keys = ["q", "swa_pool", "swa_page_table", "extra_pool", "extra_page_table", "c4_indices", "seq_lens",
+            "qo_indptr", "sink"]
+    args = [N.ref(kw[k]) for k in keys]
+    rc = L.dsv4_attn_forward(*args, kw["compress_ratio"], kw["window"], kw["scale"], N.ref(kw["out"]),
+                             N.ref(kw["lse"]), None)
+    return rc, L.dsv4_last_error().decode()
+
+
+def mutate(**changes):
+    kw = base_args(**changes.pop("base", {}))
+    kw.update(changes)
+    return kw
+
+
+CASES = [
+    ("ratio 3", mutate(compress_ratio=3), UNSUPPORTED, "compress_ratio"),
+    ("ratio 64", mutate(compress_ratio=64), UNSUPPORTED, "compress_ratio"),
+    ("head_dim 576", mutate(q=desc(N.DSV4_BF16, [4, 64, 576])), INVALID, "q"),
+    ("no heads", mutate(q=desc(N.DSV4_BF16, [4, 0, 512]), out=desc(N.DSV4_BF16, [4, 0, 512])), INVALID, "heads"),
+    ("129 heads", mutate(base=dict(H=129)), INVALID, "heads"),
+    ("window 0", mutate(window=0), INVALID, "window"),
+    ("c4 missing", mutate(c4_indices=None), INVALID, "c4_indices"),
+    ("extra pool missing", mutate(extra_pool=None), INVALID, "extra_pool"),
+    ("extra table missing", mutate(extra_page_table=None), INVALID, "extra_page_table"),
+    ("q dtype", mutate(q=desc(N.DSV4_F32, [4, 64, 512])), INVALID, "dtype"),
+    ("q strided last dim", mutate(q=desc(N.DSV4_BF16, [4, 64, 512], [65536, 1024, 2])), INVALID, "contiguous"),
+    ("q misaligned", mutate(q=desc(N.DSV4_BF16, [4, 64, 512], data=FAKE + 2)), INVALID, "aligned"),
+    ("qo_indptr length", mutate(qo_indptr=desc(N.DSV4_I32, [2])), INVALID, "qo_indptr"),
+    ("table batch", mutate(swa_page_table=desc(N.DSV4_I32, [3, 4])), INVALID, "swa_page_table"),
+    ("c4 rows", mutate(c4_indices=desc(N.DSV4_I32, [5, 512])), INVALID, "c4_indices"),
+    ("sink heads", mutate(sink=desc(N.DSV4_F32, [63])), INVALID, "sink"),
+    ("out shape", mutate(out=desc(N.DSV4_BF16, [4, 64, 448])), INVALID, "out"),
+    ("lse dtype", mutate(lse=desc(N.DSV4_BF16, [4, 64])), INVALID, "lse"),
+    ("pool width", mutate(swa_pool=desc(N.DSV4_BF16, [2048, 576])), INVALID, "swa_pool"),
+    ("pool dtype", mutate(swa_pool=desc(N.DSV4_F32, [2048, 512])), INVALID, "swa_pool"),
+    ("fp8 page bytes", mutate(swa_pool=desc(N.DSV4_U8, [8, 149000])), INVALID, "swa_pool"),
+    ("mixed formats", mutate(extra_pool=desc(N.DSV4_U8, [8, 149504])), UNSUPPORTED, "same KV format"),
+    ("seq_lens dtype", mutate(seq_lens=desc(N.DSV4_F32, [2])), INVALID, "seq_lens"),
+    ("null q data", mutate(q=desc(N.DSV4_BF16, [4, 64, 512], data=0)), INVALID, "NULL"),
+    ("scale nan", mutate(scale=float("nan")), INVALID, "scale"),
+]
+
+
+@pytest.mark.parametrize("name,kw,code,msg", CASES, ids=[c[0] for c in CASES])
+def test_forward_argument_errors(name, kw, code, msg):
+    rc, err = call(**kw)
+    assert rc == code, (rc, err)
+    assert msg.lower() in err.lower(), err
+
+
+def test_ratio_zero_ignores_extra_arguments_and_empty_batch_is_ok():
+    kw = base_args(R=0, T=0)
+    rc, err = call(**kw)
+    assert rc == OK, err
+
+
+def test_gather_slots_argument_errors():
+    L = N.load()
+    kw = base_args(R=128)
+    small = desc(N.DSV4_I32, [4, 128 + 767])  # needs window + 256 * 3 = 896
+    counts = desc(N.DSV4_I32, [4, 2])
+    rc = L.dsv4_attn_gather_slots(N.ref(kw["swa_page_table"]), N.ref(kw["extra_page_table"]), None,
+                                  N.ref(kw["seq_lens"]), N.ref(kw["qo_indptr"]), 4, 128, 128, N.ref(small),
+                                  N.ref(counts), None)
+    assert rc == INVALID and "width" in L.dsv4_last_error().decode()
+    rc = L.dsv4_attn_gather_slots(N.ref(kw["swa_page_table"]), N.ref(kw["extra_page_table"]), None,
+                                  N.ref(kw["seq_lens"]), N.ref(kw["qo_indptr"]), 4, 5, 128, N.ref(small),
+                                  N.ref(counts), None)
+    assert rc == UNSUPPORTED
+
+
+def test_plan_is_host_only_and_sane():
+    L = N.load()
+    s = ctypes.c_int32()
+    c = ctypes.c_int32()
+    assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, ctypes.byref(s), ctypes.byref(c)) == 0
+    assert c.value % 32 == 0 and s.value * c.value >= 128 + 1024
+    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, ctypes.byref(s), ctypes.byref(c)) == 0
+    assert s.value * c.value >= 640 and (s.value - 1) * c.value < 640
+    assert L.dsv4_attn_plan(32, 64, 7, 128, 512, 8, ctypes.byref(s), ctypes.byref(c)) == UNSUPPORTED
+    assert L.dsv4_attn_set_split_keys(33) == INVALID
+    assert L.dsv4_attn_set_split_keys(64) == 0
+    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, ctypes.byref(s), ctypes.byref(c)) == 0
+    assert c.value == 64 and s.value == 10
+    assert L.dsv4_attn_set_split_keys(0) == 0

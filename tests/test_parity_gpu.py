@@ -1,0 +1,372 @@
+"""GPU parity of the HIP path against the fp64 oracle (run with -m gpu).
+
+* gather stage: slot lists and counts bit-exact, every row, all workloads;
+* attention: every row of small cases (page edges, window edges, verify,
+  multi-request, ragged, H from 1 to 128, W 1/3/128, bf16 and FP8) and sampled
+  rows of the five full-size workloads in the benchmark's launch plan;
+* invariants on the GPU: physical page permutation is bit-identical, forced
+  split sizes agree, repeated calls are bit-identical;
+* sink variants, spike tests at every visibility edge, the full E4M3 code
+  table, empty passes, strided tensors, validate mode.
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as oracle_mod
+from synth import make_case, make_config
+from tests import gpu_util as G
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_mod.Oracle()
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------------
+# gather stage
+# --------------------------------------------------------------------------
+def check_gather(orc, case, rows=None):
+    slots, counts = G.run_gather(case)
+    rows = range(case.T) if rows is None else rows
+    for t in rows:
+        swa, ext = orc.gather(case, t)
+        assert counts[t, 0] == len(swa) and counts[t, 1] == len(ext), (t, counts[t], len(swa), len(ext))
+        ref = np.concatenate([swa, ext])
+        assert np.array_equal(slots[t, : len(ref)], ref), t
+        assert np.all(slots[t, len(ref):] == -1)
+
+
+SMALL = [  # (seq_lens, n_q, R, W, H, kv, extra kwargs)
+    ([200], 1, 0, 128, 8, "bf16", {}),
+    ([255], 1, 0, 128, 64, "bf16", {}),
+    ([256], 1, 0, 128, 64, "bf16", {}),
+    ([257], 1, 0, 128, 64, "bf16", {}),
+    ([128], 1, 0, 128, 64, "bf16", {}),
+    ([260], 4, 0, 128, 64, "bf16", {}),
+    ([256], 16, 0, 128, 16, "bf16", {}),
+    ([32, 96], 1, 0, 128, 64, "bf16", {}),
+    ([300, 5, 1], [3, 1, 1], 0, 3, 33, "bf16", {}),
+    ([64], 1, 4, 128, 64, "bf16", {}),
+    ([80], 16, 4, 128, 64, "bf16", {}),
+    ([67, 99], 3, 4, 128, 64, "bf16", dict(pad_mode="scatter", n_sel=7)),
+    ([3000, 700], [4, 2], 4, 128, 128, "bf16", dict(pad_mode="scatter")),
+    ([128], 1, 128, 128, 64, "bf16", {}),
+    ([144], 16, 128, 128, 64, "bf16", {}),
+    ([131, 163, 2000], 3, 128, 128, 100, "bf16", {}),
+    ([9000], 2, 128, 1, 1, "bf16", {}),
+    ([5000, 12], [4, 0], 4, 128, 64, "fp8", {}),
+    ([600, 90], [1, 3], 128, 128, 8, "fp8", {}),
+    ([200], 1, 0, 128, 64, "fp8", {}),
+]
+SMALL_IDS = [f"{i}-R{c[2]}-W{c[3]}-H{c[4]}-{c[5]}" for i, c in enumerate(SMALL)]
+
+
+def small_case(i, **over):
+    sl, nq, R, W, H, kv, extra = SMALL[i]
+    kw = dict(seq_lens=sl, n_q=nq, R=R, W=W, H=H, kv=kv, seed=500 + i, K=512 if R == 4 else 512)
+    kw.update(extra)
+    kw.update(over)
+    return make_case(**kw)
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)), ids=SMALL_IDS)
+def test_gather_small_bit_exact(orc, i):
+    check_gather(orc, small_case(i))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_gather_workloads_bit_exact(orc, n):
+    log(f"gather workload {n}")
+    check_gather(orc, make_config(n))
+
+
+# --------------------------------------------------------------------------
+# attention, small cases, every row
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("i", range(len(SMALL)), ids=SMALL_IDS)
+def test_forward_small(orc, i):
+    case = small_case(i)
+    log(f"forward small {SMALL_IDS[i]} T={case.T}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=SMALL_IDS[i])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_forward_random(orc, seed):
+    rng = np.random.default_rng(seed)
+    R = int(rng.choice([0, 4, 128]))
+    B = int(rng.integers(1, 5))
+    nq = rng.integers(0, 5, size=B)
+    sl = np.maximum(rng.integers(1, 4000, size=B), nq)
+    if R == 128:
+        sl = sl + 128
+    case = make_case(seq_lens=sl, n_q=nq, H=int(rng.choice([1, 7, 32, 64, 65, 128])), R=R,
+                     W=int(rng.choice([1, 3, 128, 200])), kv=str(rng.choice(["bf16", "fp8"])),
+                     sink=bool(rng.random() < 0.8), seed=700 + seed,
+                     K=int(rng.choice([64, 512, 600])), pad_mode=str(rng.choice(["tail", "scatter"])))
+    log(f"forward random seed={seed} R={R} T={case.T} H={case.H} W={case.W} kv={case.kv}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"random {seed}")
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, benchmark launch plan, sampled rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_forward_workloads_sampled(orc, n):
+    case = make_config(n)
+    rng = np.random.default_rng(n)
+    rows = sorted(set([0, case.T - 1] + list(rng.choice(case.T, size=min(case.T, 6), replace=False))))
+    log(f"forward workload {n} ({case.name}) rows={rows}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case, rows=rows)
+    e = G.compare(out, lse, ro, rl, rows=rows, what=case.name)
+    log(f"  max abs err {e[0]:.3g}  lse err {e[1]:.3g}  rel L2 {e[2]:.3g}")
+
+
+# --------------------------------------------------------------------------
+# invariants on the GPU
+# --------------------------------------------------------------------------
+def permute_pages(case, seed):
+    rng = np.random.default_rng(seed)
+    fp8 = case.kv == "fp8"
+
+    def perm(pool, table):
+        n = pool.shape[0] if fp8 else pool.shape[0] // 256
+        pi = rng.permutation(n)
+        pages = pool if fp8 else pool.reshape(n, 256, 512)
+        new = np.empty_like(pages)
+        new[pi] = pages
+        return (new if fp8 else new.reshape(-1, 512)), pi[table].astype(np.int32)
+
+    swa, st = perm(case.swa_pool, case.swa_page_table)
+    ext, et = case.extra_pool, case.extra_page_table
+    if ext is not None:
+        ext, et = perm(ext, et)
+    return dataclasses.replace(case, swa_pool=swa, swa_page_table=st, extra_pool=ext, extra_page_table=et)
+
+
+@pytest.mark.parametrize("i", [5, 12, 15, 18])
+def test_page_permutation_bit_identical(i):
+    case = small_case(i)
+    a_out, a_lse = G.run_forward(case)
+    b_out, b_lse = G.run_forward(permute_pages(case, 99))
+    assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+
+
+def test_repeat_bit_identical():
+    case = small_case(12)
+    g = G.to_gpu(case)
+    a = G.run_forward(case, g)
+    b = G.run_forward(case, g)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("keys", [32, 64, 96, 160, 256, 1024])
+def test_forced_split_sizes(orc, keys):
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
+
+    case = small_case(12)
+    ro, rl, _ = orc.attention(case)
+    try:
+        dsv4_attn_set_split_keys(keys)
+        out, lse = G.run_forward(case)
+    finally:
+        dsv4_attn_set_split_keys(0)
+    G.compare(out, lse, ro, rl, what=f"split {keys}")
+
+
+# --------------------------------------------------------------------------
+# sink variants
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["none", "-1e30", "zero", "normal", "+30"])
+def test_sink_variants(orc, variant):
+    kw = {}
+    if variant == "none":
+        kw = dict(sink=False)
+    elif variant == "normal":
+        kw = dict(sink=True)
+    else:
+        kw = dict(sink=True, sink_value={"-1e30": -1e30, "zero": 0.0, "+30": 30.0}[variant])
+    case = make_case(seq_lens=[700, 300], n_q=[2, 1], H=64, R=128, seed=31, **kw)
+    out, lse = G.run_forward(case)
+    ro, rl, rns = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"sink {variant}")
+    if variant in ("none", "-1e30"):
+        assert np.allclose(lse.cpu().numpy(), rns, atol=G.LSE_ATOL, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# spike tests: a key pointing along q[t, 0] must dominate head 0 exactly when
+# it is visible to the row
+# --------------------------------------------------------------------------
+def _spike(case, t, pool_name, table, r, x):
+    """Overwrite logical position x of request r with 8 * q[t, 0]."""
+    slot = int(table[r, x // 256]) * 256 + x % 256
+    row = case.q[t, 0].copy()
+    big = (torch.from_numpy(row.view(np.int16)).view(torch.bfloat16).float() * 8).to(torch.bfloat16)
+    getattr(case, pool_name)[slot] = big.view(torch.int16).numpy().view(np.uint16)
+
+
+SPIKES = [
+    # (name, R, seq_lens, n_q, where, visible)
+    ("window first", 0, [1000], 1, "tok:p-W+1", True),
+    ("window before", 0, [1000], 1, "tok:p-W", False),
+    ("verify next row", 0, [1000], 4, "tok:p+1", False),
+    ("c128 last visible", 128, [1026], 4, "cmp:vis-1", True),
+    ("c128 first hidden", 128, [1026], 4, "cmp:vis", False),
+    ("c4 listed", 4, [3000], 2, "c4:listed", True),
+    ("c4 unlisted", 4, [3000], 2, "c4:unlisted", False),
+]
+
+
+@pytest.mark.parametrize("name,R,sl,nq,where,visible", SPIKES, ids=[s[0] for s in SPIKES])
+def test_spikes(orc, name, R, sl, nq, where, visible):
+    case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=77, n_sel=300)
+    t = 0  # first row of the request
+    p = int(case.seq_lens[0]) - nq + 0
+    kind, pos = where.split(":")
+    if kind == "tok":
+        x = {"p-W+1": p - case.W + 1, "p-W": p - case.W, "p+1": p + 1}[pos]
+        _spike(case, t, "swa_pool", case.swa_page_table, 0, x)
+    elif kind == "cmp":
+        vis = (p + 1) // 128
+        x = vis - 1 if pos == "vis-1" else vis
+        assert x < int(case.seq_lens[0]) // 128
+        _spike(case, t, "extra_pool", case.extra_page_table, 0, x)
+    else:
+        listed = case.c4_indices[t][case.c4_indices[t] >= 0]
+        if pos == "listed":
+            x = int(listed[17])
+        else:
+            vis = (p + 1) // 4
+            x = int(np.setdiff1d(np.arange(vis), listed)[3])
+        _spike(case, t, "extra_pool", case.extra_page_table, 0, x)
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=name)
+    dominated = rl[t, 0] > 50.0
+    assert dominated == visible, (name, rl[t, 0])
+
+
+# --------------------------------------------------------------------------
+# FP8: every finite E4M3 code through the dequant path
+# --------------------------------------------------------------------------
+def test_fp8_all_codes(orc):
+    from synth.workloads import FP8_SCALE_OFFSET
+
+    case = make_case(seq_lens=[2000], n_q=2, H=64, R=128, kv="fp8", seed=3)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for pool in (case.swa_pool, case.extra_pool):
+        n_pages = pool.shape[0]
+        rec = pool[:, :FP8_SCALE_OFFSET].reshape(n_pages, 256, 576)
+        fill = np.resize(codes, (n_pages, 256, 448))  # every record cycles through all 254 codes
+        live =~np.all(rec[:, :, :448] == 0xFF, axis=2)  # poisoned records stay poisoned
+        rec[:, :, :448] = np.where(live[:, :, None], fill, rec[:, :, :448])
+        pool[:, :FP8_SCALE_OFFSET] = rec.reshape(n_pages, -1)
+        sc = np.full((n_pages, 256), 1.0 / 64, np.float32)
+        old = pool[:, FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 1024].copy().view(np.float32)
+        sc = np.where(np.isnan(old), old, sc)
+        pool[:, FP8_SCALE_OFFSET:FP8_SCALE_OFFSET + 1024] = sc.view(np.uint8)
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what="fp8 codes")
+
+
+# --------------------------------------------------------------------------
+# shapes and modes
+# --------------------------------------------------------------------------
+def test_empty_pass():
+    case = make_case(seq_lens=[10, 20], n_q=[0, 0], H=8, R=0, seed=1)
+    out, lse = G.run_forward(case)
+    assert out.shape == (0, 8, 512) and lse.shape == (0, 8)
+
+
+def test_without_lse_and_strided(orc):
+    case = small_case(12)
+    g = G.to_gpu(case)
+    big_q = torch.zeros((case.T, case.H + 3, 520), dtype=torch.bfloat16, device="cuda")
+    big_q[:, 1:case.H + 1, :512] = g["q"]
+    g["q"] = big_q[:, 1:case.H + 1, :512]
+    out_big = torch.full((case.T, case.H, 520), 7.0, dtype=torch.bfloat16, device="cuda")
+    out, lse = G.run_forward(case, g, out=out_big[:, :, :512], return_lse=False)
+    assert lse is None
+    assert torch.all(out_big[:, :, 512:] == 7.0)
+    ro, rl, _ = orc.attention(case)
+    ref_out, ref_lse = G.run_forward(case)
+    assert torch.equal(out_big[:, :, :512], ref_out)
+
+
+def test_validate_mode_rejects_bad_index(monkeypatch):
+    from hybrid_sparse_mqa_amd import Dsv4Error
+
+    case = make_case(seq_lens=[300], n_q=1, H=8, R=4, seed=1, n_sel=4)
+    case.c4_indices[0, 1] = 10 ** 6
+    monkeypatch.setenv("DSV4_VALIDATE", "1")
+    with pytest.raises(Dsv4Error, match="ERR_CONTRACT"):
+        G.run_forward(case)
+
+
+# --------------------------------------------------------------------------
+# split arrival counters and graph capture
+# --------------------------------------------------------------------------
+def test_interleaved_calls_reset_split_counters():
+    """Alternating cases with different split plans must stay bit-identical:
+    every merging workgroup leaves its arrival counter at zero."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
+
+    cases = [small_case(12), small_case(15), make_case(seq_lens=[2000] * 9, n_q=1, H=64, R=128, seed=4)]
+    gs = [G.to_gpu(c) for c in cases]
+    first = [G.run_forward(c, g) for c, g in zip(cases, gs)]
+    for rep in range(3):
+        for keys in (0, 64, 0):
+            try:
+                dsv4_attn_set_split_keys(keys)
+                for c, g, ref in zip(cases, gs, first):
+                    out, lse = G.run_forward(c, g)
+                    if keys == 0:
+                        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+            finally:
+                dsv4_attn_set_split_keys(0)
+
+
+def test_graph_capture_replays_match_eager():
+    """A captured forward replays correctly several times, with eager calls
+    (and synchronisations) in between."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_forward
+
+    case = make_case(seq_lens=[3000, 5000, 700], n_q=[1, 4, 2], H=64, R=4, seed=12)
+    g = G.to_gpu(case)
+    ref_out, ref_lse = G.run_forward(case, g)
+    out = torch.zeros_like(ref_out)
+    lse = torch.zeros_like(ref_lse)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            dsv4_attn_forward(g["q"], g["swa_pool"], g["swa_page_table"], g["extra_pool"], g["extra_page_table"],
+                              g["c4_indices"], g["seq_lens"], g["qo_indptr"], g["sink"], case.R, case.W, case.scale,
+                              out=out, lse=lse)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), rep
+        other = G.run_forward(small_case(12))  # eager work between replays
+        assert torch.isfinite(other[0].float()).all()
