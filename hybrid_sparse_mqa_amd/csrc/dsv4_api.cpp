@@ -511,9 +511,9 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     a.lse_s0 = lse ? lse->stride[0] : 0;
     if (a.splits > 1) {
         const size_t n_part = (size_t)T * a.splits * H;
-        const size_t bytes_o = n_part * DSV4_HEAD_DIM * sizeof(float);
+        const size_t bytes_o = n_part * DSV4_HEAD_DIM * sizeof(uint16_t);
         DSV4_TRY(ensure_workspace(d, bytes_o + n_part * sizeof(float)));
-        a.ws_o = (float*)d->ws;
+        a.ws_o = (uint16_t*)d->ws;
         a.ws_lse = (float*)((char*)d->ws + bytes_o);
     }
 

@@ -110,6 +110,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -216,6 +217,22 @@ __device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk
     __syncthreads();  // slot list ready
 }
 
+// bf16 kernel: the row address of every key [k0, k0 + n_here) of the split
+// (zero_row for unused C4 entries and for the padding up to the last tile),
+// built once so that copying a tile needs no address arithmetic.
+__device__ __forceinline__ void build_row_addresses(const AttnArgs& a, const RowKeys& rk, int k0, int n_here,
+                                                    const int32_t* s_slot, uint64_t* s_addr, int tid) {
+    const int n_pad = (n_here + kTileKeys - 1) / kTileKeys * kTileKeys;
+    for (int i = tid; i < n_pad; i += 256) {
+        const int32_t slot = i < n_here ? s_slot[i] : -1;
+        const bool swa = k0 + i < rk.n_swa;
+        const uint8_t* row = slot >= 0 ? (swa ? a.swa_pool : a.ext_pool) + (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes)
+                                       : a.zero_row;
+        s_addr[i] = (uint64_t)(uintptr_t)row;
+    }
+    __syncthreads();
+}
+
 // Sum the S^T partials of the two waves that share a head half (they cover
 // the two dim halves).  Layout [wave][chunk][lane] in 16-byte units keeps the
 // 16-byte accesses of consecutive lanes contiguous (no bank conflicts).
@@ -304,8 +321,10 @@ __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask
 
 // Epilogue.  Accumulator r of tile mb holds head (l & 31) of the wave's half,
 // dim 256*dh + 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3).  One split: apply
-// the sink and write out / lse.  Several: publish the normalised partial and
-// its base-2 log-sum-exp (-inf for an empty split) for merge_kernel.
+// the sink and write out / lse.  Several: publish the normalised partial (in
+// bf16: it is a convex combination of key rows, so 8 significant bits keep it
+// within the output's own rounding) and its base-2 log-sum-exp (-inf for an
+// empty split) for merge_kernel.
 __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int my_head, bool head_ok, int dh,
                                              int l, const f32x16 (&oacc)[8], float m_run, float l_run) {
     if (!head_ok) return;
@@ -336,15 +355,16 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, 
     const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + my_head;
     if (l_run > 0.f) {
         const float inv = 1.f / l_run;
-        float* orow = a.ws_o + part * kHeadDim;
+        uint16_t* orow = a.ws_o + part * kHeadDim;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const int d = dh * 256 + 32 * mb + 8 * qd + 4 * (l >> 5);
                 const f32x16& o = oacc[mb];
-                f32x4 v = {o[4 * qd] * inv, o[4 * qd + 1] * inv, o[4 * qd + 2] * inv, o[4 * qd + 3] * inv};
-                *(f32x4*)(orow + d) = v;
+                u32x2 v = {pack_bf16x2(o[4 * qd] * inv, o[4 * qd + 1] * inv),
+                           pack_bf16x2(o[4 * qd + 2] * inv, o[4 * qd + 3] * inv)};
+                *(u32x2*)(orow + d) = v;
             }
         }
     }
@@ -403,6 +423,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
     __shared__ int32_t s_slot[kMaxSplitKeys];
     __shared__ int32_t s_table[kTableCap];
+    __shared__ __attribute__((aligned(16))) uint64_t s_addr[kMaxSplitKeys];
 
     Item it;
     if (!decode_item(a, it)) return;
@@ -419,30 +440,23 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
     const int k0 = it.s * a.chunk;
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
     build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+    build_row_addresses(a, rk, k0, n_here, s_slot, s_addr, tid);
+    const uint64_t zero_row = (uint64_t)(uintptr_t)a.zero_row;
 
     // Wave w fetches tile keys 8w .. 8w+7; lane l moves 16 bytes of a row.
     // Lane l reads logical chunk l ^ row_swz(k) so that the row lands in the
     // swizzled layout of krow_offset.  Unused keys read the zero row.
-    // The wave's 8 slots are read first (two 16-byte LDS reads) and all 8
-    // copies are then issued back to back.
+    // Wave w copies tile keys 8w .. 8w+7: their row addresses come from LDS
+    // (four 16-byte broadcast reads) and lane l moves logical chunk
+    // l ^ row_swz(k) so that each row lands in the swizzled layout.
     auto fetch_tile = [&](int tile) {
         uint8_t* dst = &s_tile[tile % kStages][0];
-        const int i0 = tile * kTileKeys + 8 * w;
-        const i32x4 sa = *(const i32x4*)&s_slot[i0];
-        const i32x4 sb = *(const i32x4*)&s_slot[i0 + 4];
-        const uint8_t* src[8];
+        const u64x2* ap = (const u64x2*)&s_addr[tile * kTileKeys + 8 * w];
+        const u64x2 a01 = ap[0], a23 = ap[1], a45 = ap[2], a67 = ap[3];
+        const uint64_t rows[8] = {a01[0], a01[1], a23[0], a23[1], a45[0], a45[1], a67[0], a67[1]};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = i0 + e;
-            const int32_t slot = i < n_here ? (e < 4 ? sa[e] : sb[e - 4]) : -1;
-            const int k = 8 * w + e;
-            const bool swa = k0 + i < rk.n_swa;
-            src[e] = (slot >= 0 ? (swa ? a.swa_pool : a.ext_pool) + (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes)
-                                : a.zero_row) +
-                     16 * (l ^ row_swz(k));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dma16(src[e], lds_addr(dst + (8 * w + e) * 1024));
+        for (int e = 0; e < 8; ++e)
+            dma16((const uint8_t*)(uintptr_t)rows[e] + 16 * (l ^ row_swz(8 * w + e)), lds_addr(dst + (8 * w + e) * 1024));
     };
 
     f32x16 oacc[8];
@@ -466,9 +480,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
         if (newer >= 2) wait_vmcnt<16>();
         else if (newer == 1) wait_vmcnt<8>();
         else wait_vmcnt<0>();
-        const int kv = i * kTileKeys + (l & 31);
-        const bool valid = l < 32 && kv < n_here && s_slot[kv] >= 0;
-        const uint64_t vmask = __ballot(valid);
+        const uint64_t vmask = __ballot(l < 32 && s_addr[i * kTileKeys + (l & 31)] != zero_row);
         __syncthreads();  // tile i is in LDS for every wave; stage (i-1) % kStages is free
         if (i + kStages - 1 < n_tiles) fetch_tile(i + kStages - 1);
 
@@ -678,7 +690,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     if (head >= a.H) return;
     const int S = a.splits;
     const float* lp = a.ws_lse + (int64_t)t * S * a.H + head;
-    const float* ob = a.ws_o + ((int64_t)t * S * a.H + head) * kHeadDim + 8 * l;
+    const uint16_t* ob = a.ws_o + ((int64_t)t * S * a.H + head) * kHeadDim + 8 * l;
     const int64_t ostride = (int64_t)a.H * kHeadDim;
     const float sig = a.sink != nullptr ? a.sink[head] * kLog2e : -INFINITY;
     float M = sig;
@@ -691,26 +703,22 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
         Z = fast_exp2(sig - M);
         for (int k0 = 0; k0 < S; k0 += kMaxSplitsPerPass) {
             float wgt[kMaxSplitsPerPass];
-            f32x4 x0[kMaxSplitsPerPass], x1[kMaxSplitsPerPass];
+            u32x4 x[kMaxSplitsPerPass];
 #pragma unroll
             for (int j = 0; j < kMaxSplitsPerPass; ++j) {
                 const int k = k0 + j;
                 const float v = k < S ? lp[(int64_t)k * a.H] : -INFINITY;
                 wgt[j] = v == -INFINITY ? 0.f : fast_exp2(v - M);
-                x0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                x1[j] = x0[j];
-                if (wgt[j] != 0.f) {  // an empty split never wrote its partial
-                    x0[j] = *(const f32x4*)(ob + k * ostride);
-                    x1[j] = *(const f32x4*)(ob + k * ostride + 4);
-                }
+                x[j] = u32x4{0u, 0u, 0u, 0u};
+                if (wgt[j] != 0.f) x[j] = *(const u32x4*)(ob + k * ostride);  // an empty split wrote nothing
             }
 #pragma unroll
             for (int j = 0; j < kMaxSplitsPerPass; ++j) {
                 Z += wgt[j];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[e] += wgt[j] * x0[j][e];
-                    acc[4 + e] += wgt[j] * x1[j][e];
+                    acc[2 * e] += wgt[j] * __builtin_bit_cast(float, x[j][e] << 16);
+                    acc[2 * e + 1] += wgt[j] * __builtin_bit_cast(float, x[j][e] & 0xFFFF0000u);
                 }
             }
         }

@@ -35,7 +35,7 @@ struct AttnArgs {
     int64_t out_s0, out_s1;
     float* lse;               // [T, H] or null
     int64_t lse_s0;
-    float* ws_o;              // [T, splits, H, 512] normalised partial outputs
+    uint16_t* ws_o;           // bf16 [T, splits, H, 512] normalised partial outputs
     float* ws_lse;            // [T, splits, H] base-2 partial log-sum-exp
     const uint8_t* zero_row;  // >= 1 KiB of zeros, read in place of unused keys
 };
