@@ -7,10 +7,13 @@ over one batch of a synthetic workload already resident in HBM.  To keep the
 several GPU copies of the inputs (same values, different addresses) whose
 referenced bytes together exceed the cache several times.
 
-Prints ONE JSON line: tokens (query rows) per second of the whole job, plus
-a roofline object for the dominant kernel (algorithmic bytes per launch over
-its average duration from HIP events recorded on the launch stream) and the
-fp64 oracle timed on the host cores on a bounded sample of the same workload.
+Prints ONE JSON line: tokens (query rows) per second of the whole job over a
+timed HIP-graph replay of exactly --steps calls; a roofline object for the
+dominant kernel (the split kernel: the bytes it must read -- Q, C4 index
+lists and every unique KV row -- over its average duration from HIP events
+recorded on its stream inside the timed replay); the whole path's achieved
+GB/s (all algorithmic bytes over split + merge kernel time); and the fp64
+oracle timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -102,11 +105,11 @@ def cpu_baseline(case, target_s: float):
     rows = np.sort(rng.choice(case.T, size=n, replace=False)).astype(np.int32)
     reps = 0
     t0 = time.perf_counter()
-    while True:  # repeat small samples until the timing is stable (>= 3 s)
+    while True:  # repeat the sample until about target_s seconds of CPU work
         orc.attention(case, rows=rows)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= min(3.0, target_s) or dt >= target_s:
+        if dt >= target_s:
             break
     used = min(threads, n)
     return {
@@ -129,6 +132,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-keys", type=int, default=0, help="force keys per split (0 = library plan)")
+    ap.add_argument("--sample-every", type=int, default=10,
+                    help="time the kernels of every N-th call of the timed replay with HIP events")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -191,8 +196,7 @@ def main() -> int:
           f"sets={n_sets} ({'cold' if cold else 'warm'}) algorithmic {ab['total'] / 1e6:.2f} MB/call",
           file=sys.stderr, flush=True)
 
-    # Eager calls: per-call kernel time from the library's HIP events on the
-    # launch stream, and the wall time of the Python-driven loop.
+    # Eager calls, for context: host-driven loop time and per-call kernel time.
     n_eager = min(args.steps, 100)
     dsv4_attn_timing_read()  # clear
     dsv4_attn_timing_enable(True)
@@ -203,50 +207,56 @@ def main() -> int:
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
     dsv4_attn_timing_enable(False)
-    kern_ms, calls = dsv4_attn_timing_read()
-    kernel_avg_ms = kern_ms / max(calls, 1)
+    e_split, e_merge, e_calls = dsv4_attn_timing_read()
 
-    # Timed region: exactly `steps` steps replayed from HIP graphs (one graph
-    # holds one call per input set; a second holds the remainder), bracketed by
-    # HIP events on the replay stream.
+    # Timed region: one replay of a HIP graph holding exactly `steps` calls
+    # (rotating over the input sets).  Every `sample_every`-th call is captured
+    # with the library's timing on, which adds event-record nodes before its
+    # split kernel, between split and merge kernel and after the merge kernel,
+    # on the stream the kernels run on; the replay itself is bracketed by two
+    # more events.  (Instrumenting every call would add the event nodes' own
+    # cost to every step.)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    graphs = []
-    full, rem = divmod(args.steps, n_sets)
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
-        for count in ([n_sets] if full else []) + ([rem] if rem else []):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for i in range(count):
-                    step(i)
-            graphs.append((g, count))
-        for g, _ in graphs:  # warm replay
-            g.replay()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                sampled = i % args.sample_every == args.sample_every // 2
+                if sampled:
+                    dsv4_attn_timing_enable(True)
+                step(i)
+                if sampled:
+                    dsv4_attn_timing_enable(False)
+        g.replay()  # warm replay (untimed)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(stream)
-        for _ in range(full):
-            graphs[0][0].replay()
-        if rem:
-            graphs[-1][0].replay()
+        g.replay()
         ev1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     event_ms = ev0.elapsed_time(ev1)
+    split_ms, merge_ms, calls = dsv4_attn_timing_read()  # the timed replay's sampled calls
+    expected = sum(1 for i in range(args.steps) if i % args.sample_every == args.sample_every // 2)
+    if calls != expected or calls == 0:
+        print(f"[bench] expected {expected} sampled calls, the library recorded {calls}", file=sys.stderr)
+        return 1
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = case.T / (ms_per_step / 1e3)
-    graph_kernel_ms = event_ms / args.steps   # kernel + in-graph launch gap per step
-    achieved = ab["total"] / (graph_kernel_ms * 1e-3) / 1e9
-    main_bytes = ab["total"]
+    split_avg_ms = split_ms / calls
+    merge_avg_ms = merge_ms / calls
+    kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
+    achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
+    kernel_name = "attn_regs_kernel" if case.kv == "fp8" else "attn_dma_kernel"
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE)).get(case.name)
+        rec = json.load(open(TRAFFIC_FILE)).get(f"{kernel_name}/{case.name}")
         if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("split_keys", 0) == args.split_keys:
             traffic = rec.get("hbm_bytes_per_launch")
 
@@ -266,19 +276,28 @@ def main() -> int:
         "config": dict(describe_workload(args.config, case), splits=int(splits), keys_per_split=int(chunk),
                        input_sets=int(n_sets), cache="cold-rotated" if cold else "warm-rotated",
                        timed="HIP graph replay", parallelism="single GPU"),
-        "achieved_gbs_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9,
-        "kernel_ms": {"attn_fused_kernel_graph_events": graph_kernel_ms,
-                      "attn_fused_kernel_eager_events": kernel_avg_ms},
-        "eager_ms_per_call": eager_ms,
+        "path": {
+            "algorithmic_bytes_per_call": ab["total"],
+            "achieved_gbs_kernels": ab["total"] / ((split_avg_ms + merge_avg_ms) * 1e-3) / 1e9,
+            "achieved_gbs_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9,
+            "split_kernel_ms": split_avg_ms,
+            "merge_kernel_ms": merge_avg_ms,
+            "graph_event_ms_per_step": event_ms / args.steps,
+            "timed_calls_sampled": calls,
+            "eager_ms_per_call": eager_ms,
+            "eager_split_kernel_ms": e_split / max(e_calls, 1),
+            "eager_merge_kernel_ms": e_merge / max(e_calls, 1),
+        },
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_fused_kernel",
+            "kernel": kernel_name,
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": main_bytes,
+            "algorithmic_bytes_per_launch": kernel_bytes,
+            "avg_launch_ms": split_avg_ms,
         },
         "cpu_baseline": None,
     }

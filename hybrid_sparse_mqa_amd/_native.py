@@ -72,7 +72,8 @@ def load() -> ctypes.CDLL:
         L.dsv4_attn_timing_enable.restype = ctypes.c_int
         L.dsv4_attn_timing_enable.argtypes = [ctypes.c_int32]
         L.dsv4_attn_timing_read.restype = ctypes.c_int
-        L.dsv4_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.dsv4_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_int64)]
         _lib = L
         return L
 

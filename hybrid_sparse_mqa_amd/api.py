@@ -112,9 +112,10 @@ def dsv4_attn_timing_enable(enable: bool) -> None:
     N.check(N.load().dsv4_attn_timing_enable(int(bool(enable))))
 
 
-def dsv4_attn_timing_read() -> Tuple[float, int]:
-    """(summed kernel milliseconds, calls) recorded since the last read."""
+def dsv4_attn_timing_read() -> Tuple[float, float, int]:
+    """(summed split-kernel ms, summed merge-kernel ms, calls) recorded since the last read."""
     a = ctypes.c_double()
+    b = ctypes.c_double()
     n = ctypes.c_int64()
-    N.check(N.load().dsv4_attn_timing_read(ctypes.byref(a), ctypes.byref(n)))
-    return a.value, n.value
+    N.check(N.load().dsv4_attn_timing_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)))
+    return a.value, b.value, n.value

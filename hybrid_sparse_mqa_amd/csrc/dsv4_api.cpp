@@ -240,12 +240,34 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, int32_t* splits, i
 }
 
 // ---- timing -------------------------------------------------------------------
+// e0 before the split kernel, e1 between it and the merge kernel, e2 after
+// the merge kernel (e1 == e2 in time when no row is split).
 struct TimingRec {
-    hipEvent_t e0, e1;
+    hipEvent_t e0, e1, e2;
 };
 bool g_timing = false;
 std::vector<TimingRec> g_timing_recs;
 std::vector<hipEvent_t> g_event_pool;
+
+// Inside stream capture a record becomes an event-record node appended to the
+// captured graph after the stream's current dependencies, so each replay
+// re-records it; reading after a replay gives that replay's times.  The null
+// stream cannot be captured.
+hipError_t record_event(hipEvent_t e, hipStream_t st) {
+    if (st == nullptr) return hipEventRecord(e, st);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    unsigned long long id = 0;
+    hipGraph_t graph = nullptr;
+    const hipGraphNode_t* deps = nullptr;
+    size_t n_deps = 0;
+    hipError_t err = hipStreamGetCaptureInfo_v2(st, &cs, &id, &graph, &deps, &n_deps);
+    if (err != hipSuccess) return err;
+    if (cs != hipStreamCaptureStatusActive) return hipEventRecord(e, st);
+    hipGraphNode_t node = nullptr;
+    err = hipGraphAddEventRecordNode(&node, graph, deps, n_deps, e);
+    if (err != hipSuccess) return err;
+    return hipStreamUpdateCaptureDependencies(st, &node, 1, hipStreamSetCaptureDependencies);
+}
 
 hipEvent_t take_event() {
     if (!g_event_pool.empty()) {
@@ -391,20 +413,24 @@ dsv4_status dsv4_attn_timing_enable(int32_t enable) {
     return DSV4_OK;
 }
 
-dsv4_status dsv4_attn_timing_read(double* kernel_ms, int64_t* calls) {
+dsv4_status dsv4_attn_timing_read(double* split_ms, double* merge_ms, int64_t* calls) {
     std::lock_guard<std::mutex> lk(g_mu);
-    double a = 0.0;
+    double a = 0.0, b = 0.0;
     for (TimingRec& r : g_timing_recs) {
-        DSV4_HIP(hipEventSynchronize(r.e1));
-        float x = 0.f;
+        DSV4_HIP(hipEventSynchronize(r.e2));
+        float x = 0.f, y = 0.f;
         DSV4_HIP(hipEventElapsedTime(&x, r.e0, r.e1));
+        DSV4_HIP(hipEventElapsedTime(&y, r.e1, r.e2));
         a += x;
+        b += y;
         g_event_pool.push_back(r.e0);
         g_event_pool.push_back(r.e1);
+        g_event_pool.push_back(r.e2);
     }
     if (calls) *calls = (int64_t)g_timing_recs.size();
     g_timing_recs.clear();
-    if (kernel_ms) *kernel_ms = a;
+    if (split_ms) *split_ms = a;
+    if (merge_ms) *merge_ms = b;
     return DSV4_OK;
 }
 
@@ -521,13 +547,15 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     if (g_timing) {
         rec.e0 = take_event();
         rec.e1 = take_event();
-        if (!rec.e0 || !rec.e1) return fail(DSV4_ERR_HIP, "hipEventCreate failed");
-        DSV4_HIP(hipEventRecord(rec.e0, st));
+        rec.e2 = take_event();
+        if (!rec.e0 || !rec.e1 || !rec.e2) return fail(DSV4_ERR_HIP, "hipEventCreate failed");
+        DSV4_HIP(record_event(rec.e0, st));
     }
     DSV4_HIP(launch_attention(a, swa.fp8, st));
+    if (g_timing) DSV4_HIP(record_event(rec.e1, st));
     if (a.splits > 1) DSV4_HIP(launch_merge(a, st));
     if (g_timing) {
-        DSV4_HIP(hipEventRecord(rec.e1, st));
+        DSV4_HIP(record_event(rec.e2, st));
         g_timing_recs.push_back(rec);
     }
     return DSV4_OK;

@@ -683,7 +683,7 @@ __global__ __launch_bounds__(256, 1) void attn_regs_kernel(AttnArgs a) {
 // row's merge costs one round of loads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-    constexpr int kMaxSplitsPerPass = 16;
+    constexpr int kPass = 16;
     const int t = blockIdx.x;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
@@ -692,33 +692,46 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const float* lp = a.ws_lse + (int64_t)t * S * a.H + head;
     const uint16_t* ob = a.ws_o + ((int64_t)t * S * a.H + head) * kHeadDim + 8 * l;
     const int64_t ostride = (int64_t)a.H * kHeadDim;
+    // The partials of the first kPass splits, the splits' log-sum-exps (lane k
+    // holds split k's) and the sink are all requested before any is used, so
+    // the merge costs one memory round trip.  An empty split left its partial
+    // slot stale: its weight is zero and the select below drops it.
+    u32x4 x[kPass];
+#pragma unroll
+    for (int j = 0; j < kPass; ++j) {
+        x[j] = u32x4{0u, 0u, 0u, 0u};
+        if (j < S) x[j] = *(const u32x4*)(ob + j * ostride);
+    }
+    const float lse0 = l < S ? lp[(int64_t)l * a.H] : -INFINITY;
     const float sig = a.sink != nullptr ? a.sink[head] * kLog2e : -INFINITY;
-    float M = sig;
-    for (int k = l; k < S; k += 64) M = fmaxf(M, lp[(int64_t)k * a.H]);
+    float M = lse0;
+    for (int k = l + 64; k < S; k += 64) M = fmaxf(M, lp[(int64_t)k * a.H]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    M = fmaxf(M, sig);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float Z = 0.f;
     if (M != -INFINITY) {
         Z = fast_exp2(sig - M);
-        for (int k0 = 0; k0 < S; k0 += kMaxSplitsPerPass) {
-            float wgt[kMaxSplitsPerPass];
-            u32x4 x[kMaxSplitsPerPass];
+        for (int k0 = 0; k0 < S; k0 += kPass) {
+            float lv = lse0;
+            if (k0 > 0) {
+                lv = k0 + l < S ? lp[(int64_t)(k0 + l) * a.H] : -INFINITY;
 #pragma unroll
-            for (int j = 0; j < kMaxSplitsPerPass; ++j) {
-                const int k = k0 + j;
-                const float v = k < S ? lp[(int64_t)k * a.H] : -INFINITY;
-                wgt[j] = v == -INFINITY ? 0.f : fast_exp2(v - M);
-                x[j] = u32x4{0u, 0u, 0u, 0u};
-                if (wgt[j] != 0.f) x[j] = *(const u32x4*)(ob + k * ostride);  // an empty split wrote nothing
+                for (int j = 0; j < kPass; ++j)
+                    if (k0 + j < S) x[j] = *(const u32x4*)(ob + (k0 + j) * ostride);
             }
 #pragma unroll
-            for (int j = 0; j < kMaxSplitsPerPass; ++j) {
-                Z += wgt[j];
+            for (int j = 0; j < kPass; ++j) {
+                const float v = __shfl(lv, j);
+                const float w = (k0 + j < S && v != -INFINITY) ? fast_exp2(v - M) : 0.f;
+                Z += w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += wgt[j] * __builtin_bit_cast(float, x[j][e] << 16);
-                    acc[2 * e + 1] += wgt[j] * __builtin_bit_cast(float, x[j][e] & 0xFFFF0000u);
+                    const float lo = __builtin_bit_cast(float, x[j][e] << 16);
+                    const float hi = __builtin_bit_cast(float, x[j][e] & 0xFFFF0000u);
+                    acc[2 * e] += w != 0.f ? w * lo : 0.f;
+                    acc[2 * e + 1] += w != 0.f ? w * hi : 0.f;
                 }
             }
         }

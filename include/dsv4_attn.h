@@ -176,14 +176,17 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
 
 /*
  * Kernel timing on the caller's stream with HIP events.  While enabled, every
- * dsv4_attn_forward records an event before its first kernel and after its
- * last one (the split kernel, and the merge kernel when a row is split).
- * dsv4_attn_timing_read waits for the recorded events, returns the summed
- * milliseconds and the number of calls recorded, then clears the record.
- * Do not enable while capturing a HIP graph.
+ * dsv4_attn_forward records an event before the split kernel, one between it
+ * and the merge kernel, and one after the merge kernel (which only runs when
+ * a row is split).  Calls made while the stream is being captured into a HIP
+ * graph record external event nodes instead, re-recorded on every replay.
+ * dsv4_attn_timing_read waits for the recorded events and returns the summed
+ * milliseconds of the split kernels and of the merge kernels (either pointer
+ * may be NULL) and the number of calls recorded, then clears the record; for
+ * graph-captured calls it reports the most recent replay.
  */
 dsv4_status dsv4_attn_timing_enable(int32_t enable);
-dsv4_status dsv4_attn_timing_read(double* kernel_ms, int64_t* calls);
+dsv4_status dsv4_attn_timing_read(double* split_ms, double* merge_ms, int64_t* calls);
 
 #ifdef __cplusplus
 }

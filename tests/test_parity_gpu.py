@@ -370,3 +370,51 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), rep
         other = G.run_forward(small_case(12))  # eager work between replays
         assert torch.isfinite(other[0].float()).all()
+
+
+@pytest.mark.gpu
+def test_timing_events_eager_and_captured():
+    """Kernel timing: eager calls on the null stream and on a side stream, and
+    calls captured into a graph (event nodes re-recorded by each replay)."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_forward, dsv4_attn_timing_enable, dsv4_attn_timing_read
+
+    case = make_case(seq_lens=[3000, 5000], n_q=[1, 2], H=64, R=4, seed=13)
+    g = G.to_gpu(case)
+    ref_out, ref_lse = G.run_forward(case, g)
+
+    def call(out=None, lse=None):
+        return dsv4_attn_forward(g["q"], g["swa_pool"], g["swa_page_table"], g["extra_pool"], g["extra_page_table"],
+                                 g["c4_indices"], g["seq_lens"], g["qo_indptr"], g["sink"], case.R, case.W,
+                                 case.scale, out=out, lse=lse)
+
+    dsv4_attn_timing_read()  # clear
+    dsv4_attn_timing_enable(True)
+    try:
+        for _ in range(2):
+            call()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            call()
+        torch.cuda.synchronize()
+        split_ms, merge_ms, n = dsv4_attn_timing_read()
+        assert n == 3 and split_ms > 0 and merge_ms >= 0
+
+        out = torch.zeros_like(ref_out)
+        lse = torch.zeros_like(ref_lse)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                call(out, lse)
+                call(out, lse)
+    finally:
+        dsv4_attn_timing_enable(False)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), rep
+        split_ms, merge_ms, n = dsv4_attn_timing_read() if rep == 1 else (1.0, 0.0, 2)
+        assert n == 2 and split_ms > 0 and merge_ms >= 0
+    assert dsv4_attn_timing_read()[2] == 0
