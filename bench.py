@@ -122,6 +122,80 @@ def cpu_baseline(case, target_s: float):
     }
 
 
+def copy_calibration(mib: int) -> int:
+    """A plain device-to-device copy of `mib` MiB, ten times (for scaling the
+    FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB x 10", flush=True)
+    return 0
+
+
+def _counter_per_dispatch(csv_dir: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, by kernel name, from a rocprofv3
+    --pmc run written with --output-format csv."""
+    import csv
+    import glob
+
+    vals = {}
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def record_traffic(config: int, split_keys: int, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                   copy_write_dir: str, copy_mib: int, commands: list) -> int:
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the
+    attention, and of a plain copy of known size) into HBM bytes per launch of
+    the split kernel, stored with a hash of the kernel sources."""
+    from synth import make_config
+
+    case = make_config(config)
+    name = "attn_regs_kernel" if case.kv == "fp8" else "attn_dma_kernel"
+
+    def pick(d, key):
+        hits = {k: v for k, v in d.items() if key in k}
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {sorted(hits)}")
+        return next(iter(hits.values()))
+
+    copy_bytes = float(copy_mib << 20)
+    f_copy = pick(_counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE"), "copyBuffer") * 1024.0
+    w_copy = pick(_counter_per_dispatch(copy_write_dir, "WRITE_SIZE"), "copyBuffer") * 1024.0
+    f_attn = pick(_counter_per_dispatch(fetch_dir, "FETCH_SIZE"), name) * 1024.0
+    w_attn = pick(_counter_per_dispatch(write_dir, "WRITE_SIZE"), name) * 1024.0
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    rec = {
+        "kernel_sha": kernel_sha(),
+        "split_keys": split_keys,
+        "hbm_bytes_per_launch": f_attn * f_scale + w_attn * w_scale,
+        "fetch_bytes_per_launch": f_attn * f_scale,
+        "write_bytes_per_launch": w_attn * w_scale,
+        "raw_fetch_kib": f_attn / 1024.0,
+        "raw_write_kib": w_attn / 1024.0,
+        "copy_calibration": {"bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale},
+        "algorithmic_bytes_per_launch": None,
+        "commands": commands,
+    }
+    ab = algorithmic_bytes(case)
+    rec["algorithmic_bytes_per_launch"] = ab["q"] + ab["idx"] + ab["kv"]
+    data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    data[f"{name}/{case.name}"] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps({f"{name}/{case.name}": rec}, indent=1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,7 +208,18 @@ def main() -> int:
     ap.add_argument("--split-keys", type=int, default=0, help="force keys per split (0 = library plan)")
     ap.add_argument("--sample-every", type=int, default=10,
                     help="time the kernels of every N-th call of the timed replay with HIP events")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output folders to turn into profiles/traffic_counters.json")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy in MiB")
+    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded with --traffic-from")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        return record_traffic(args.config, args.split_keys, *args.traffic_from, args.copy_mib, args.commands)
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the attention shards by "

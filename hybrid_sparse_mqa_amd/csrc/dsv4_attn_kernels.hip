@@ -168,50 +168,63 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, bool 
     }
 }
 
-// Slot list of keys [k0, k0 + n_here) of row t into s_slot.  The page-table
-// row, the C4 indices and the window's page entries are fetched in one round;
-// compressed slots then resolve through the page-table row cached in LDS.
+// Slot list of keys [k0, k0 + n_here) of row t into s_slot.  One round of
+// loads fetches the request's extra page-table row (cached in LDS) and, per
+// key, its window page entry or its C4 index; every address is clamped into
+// range so that no load sits under a per-lane branch and all of them are in
+// flight together.  Compressed slots then resolve through the LDS table (or,
+// for a table longer than kTableCap pages, through one more round of loads).
 __device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk, int t, int k0, int n_here,
                                             int32_t* s_slot, int32_t* s_table, int tid) {
+    constexpr int kU = kMaxSplitKeys / 256;
+    constexpr int kTU = kTableCap / 256;
     const bool cached_table = a.m.R != 0 && a.ext_pages <= kTableCap;
-    if (cached_table)
-        for (int i = tid; i < a.ext_pages; i += 256) s_table[i] = a.m.ext_table[(int64_t)rk.r * a.m.ext_ld + i];
-    int32_t v[kMaxSplitKeys / 256];
-#pragma unroll
-    for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
-        const int i = tid + 256 * u;
-        v[u] = -1;
-        if (i < n_here) {
-            const int e = k0 + i;
-            if (e < rk.n_swa) {
-                const int x = rk.swa_lo + e;
-                v[u] = a.m.swa_table[(int64_t)rk.r * a.m.swa_ld + (x >> 8)] * kPage + (x & (kPage - 1));
-            } else {
-                v[u] = a.m.R == 4 ? a.m.c4[(int64_t)t * a.m.c4_ld + (e - rk.n_swa)] : e - rk.n_swa;
-            }
-        }
-    }
-    __syncthreads();  // s_table ready
+    const int32_t* ext_row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
+    const int32_t* swa_row = a.m.swa_table + (int64_t)rk.r * a.m.swa_ld;
+    const int32_t* c4_row = a.m.R == 4 ? a.m.c4 + (int64_t)t * a.m.c4_ld : swa_row;
+    int32_t tab[kTU];
     if (cached_table) {
 #pragma unroll
-        for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
-            const int i = tid + 256 * u;
-            if (i < n_here) {
-                int32_t slot = v[u];
-                if (k0 + i >= rk.n_swa && slot >= 0) slot = s_table[slot >> 8] * kPage + (slot & (kPage - 1));
-                s_slot[i] = slot;
-            }
-        }
-    } else {
-        const int32_t* row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
+        for (int j = 0; j < kTU; ++j) tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+    }
+    // Raw loads first (all kU of them, clamped), arithmetic after, so that no
+    // wait for one load comes before the next load is issued.
+    int32_t raw[kU];
 #pragma unroll
-        for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
-            const int i = tid + 256 * u;
-            if (i < n_here) {
-                int32_t slot = v[u];
-                if (k0 + i >= rk.n_swa && slot >= 0) slot = row[slot >> 8] * kPage + (slot & (kPage - 1));
-                s_slot[i] = slot;
-            }
+    for (int u = 0; u < kU; ++u) {
+        const int e = k0 + tid + 256 * u;
+        const int x = rk.swa_lo + min(e, rk.n_swa - 1);
+        const int c = min(max(e - rk.n_swa, 0), max(a.m.K - 1, 0));
+        raw[u] = *((e < rk.n_swa || a.m.R != 4) ? swa_row + (x >> 8) : c4_row + c);  // K >= 1 when R == 4
+    }
+    int32_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int e = k0 + tid + 256 * u;
+        const int x = rk.swa_lo + min(e, rk.n_swa - 1);
+        v[u] = e < rk.n_swa ? raw[u] * kPage + (x & (kPage - 1)) : (a.m.R == 4 ? raw[u] : e - rk.n_swa);
+    }
+#pragma unroll
+    for (int j = 0; j < kTU; ++j)
+        if (cached_table && tid + 256 * j < a.ext_pages) s_table[tid + 256 * j] = tab[j];
+    __syncthreads();  // s_table ready
+    // A table too long for LDS: one more round of (clamped) loads.
+    int32_t pg[kU] = {};
+    if (a.m.R != 0 && !cached_table) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const bool ext = k0 + tid + 256 * u >= rk.n_swa && v[u] >= 0;
+            pg[u] = ext_row[ext ? min(v[u] >> 8, a.ext_pages - 1) : 0];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int i = tid + 256 * u;
+        if (i < n_here) {
+            int32_t slot = v[u];
+            if (k0 + i >= rk.n_swa && slot >= 0)
+                slot = (cached_table ? s_table[slot >> 8] : pg[u]) * kPage + (slot & (kPage - 1));
+            s_slot[i] = slot;
         }
     }
     __syncthreads();  // slot list ready
@@ -433,9 +446,6 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
     const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
     const bool head_ok = my_head < a.H;
 
-    bf16x8 qf[16];
-    load_q(a, it.t, my_head, head_ok, dh, l, qf);
-
     const RowKeys rk = row_keys(a.m, it.t, l);
     const int k0 = it.s * a.chunk;
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
@@ -466,13 +476,41 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
     const float no_scale[16] = {};
 
     const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
-    // Retire every compiler-visible load (Q, slot metadata) first, so the only
-    // vector-memory operations in flight below are this wave's row copies
-    // (8 per tile) and the explicit vmcnt waits count exactly those.
+    // Retire every compiler-visible load (slot metadata) first, so the only
+    // vector-memory operations in flight below are this wave's copies into
+    // LDS (16 for Q, then 8 per tile) and the explicit vmcnt waits count
+    // exactly those.
     wait_vmcnt<0>();
+    // Q travels the same way as the keys: the block's 64 head rows (zero rows
+    // past H) are copied into ring stages 2-3, in the swizzled row layout,
+    // ahead of tiles 0 and 1, so Q and the first keys arrive together.  Once
+    // every wave holds its Q operands, stages 2-3 return to the ring.
+    bf16x8 qf[16];
+    if (n_tiles > 0) {
+        uint8_t* qs = &s_tile[2][0];
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p)
-        if (p < n_tiles) fetch_tile(p);
+        for (int e = 0; e < 16; ++e) {
+            const int k = 16 * w + e;
+            const int head = it.hb * kHeadsPerBlock + k;
+            const uint8_t* src = head < a.H ? (const uint8_t*)(a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1)
+                                            : a.zero_row;
+            dma16(src + 16 * (l ^ row_swz(k)), lds_addr(qs + k * 1024));
+        }
+        fetch_tile(0);
+        if (n_tiles > 1) {
+            fetch_tile(1);
+            wait_vmcnt<8>();  // Q and tile 0
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        const int qrow = hh * 32 + (l & 31);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qf[j] = *(const bf16x8*)(qs + krow_offset(qrow, dh * 32 + 2 * j + (l >> 5)));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave has its Q: stages 2-3 are free
+        if (n_tiles > 2) fetch_tile(2);
+    }
 
     for (int i = 0; i < n_tiles; ++i) {
         // Tiles i+1 and i+2 may still be in flight; wait for this wave's rows of tile i.
@@ -692,50 +730,64 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const float* lp = a.ws_lse + (int64_t)t * S * a.H + head;
     const uint16_t* ob = a.ws_o + ((int64_t)t * S * a.H + head) * kHeadDim + 8 * l;
     const int64_t ostride = (int64_t)a.H * kHeadDim;
-    // The partials of the first kPass splits, the splits' log-sum-exps (lane k
-    // holds split k's) and the sink are all requested before any is used, so
-    // the merge costs one memory round trip.  An empty split left its partial
-    // slot stale: its weight is zero and the select below drops it.
-    u32x4 x[kPass];
-#pragma unroll
-    for (int j = 0; j < kPass; ++j) {
-        x[j] = u32x4{0u, 0u, 0u, 0u};
-        if (j < S) x[j] = *(const u32x4*)(ob + j * ostride);
-    }
-    const float lse0 = l < S ? lp[(int64_t)l * a.H] : -INFINITY;
-    const float sig = a.sink != nullptr ? a.sink[head] * kLog2e : -INFINITY;
-    float M = lse0;
-    for (int k = l + 64; k < S; k += 64) M = fmaxf(M, lp[(int64_t)k * a.H]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    M = fmaxf(M, sig);
+    // The sink is read from a valid address either way (the zero row when
+    // there is none) so that its load does not hold up the others.
+    const float sink_raw = a.sink != nullptr ? a.sink[head] : *(const float*)a.zero_row;
+    const float sig = a.sink != nullptr ? sink_raw * kLog2e : -INFINITY;
+    // Running base-2 merge of the splits; the sink joins at the end.
+    float M = -INFINITY, Z = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float Z = 0.f;
-    if (M != -INFINITY) {
-        Z = fast_exp2(sig - M);
-        for (int k0 = 0; k0 < S; k0 += kPass) {
-            float lv = lse0;
-            if (k0 > 0) {
-                lv = k0 + l < S ? lp[(int64_t)(k0 + l) * a.H] : -INFINITY;
+    auto pass = [&](int k0) {
+        // Every load of the pass is issued before any is used, with split
+        // indices clamped into range (a clamped duplicate gets weight zero),
+        // so a pass costs one memory round trip.  An empty split left its
+        // partial stale: its weight is zero and the select below drops it.
+        u32x4 x[kPass];
 #pragma unroll
-                for (int j = 0; j < kPass; ++j)
-                    if (k0 + j < S) x[j] = *(const u32x4*)(ob + (k0 + j) * ostride);
-            }
+        for (int j = 0; j < kPass; ++j) x[j] = *(const u32x4*)(ob + min(k0 + j, S - 1) * ostride);
+        const float lse_l = lp[(int64_t)min(k0 + (l & (kPass - 1)), S - 1) * a.H];
+        float lv[kPass];
+        float pm = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < kPass; ++j) {
-                const float v = __shfl(lv, j);
-                const float w = (k0 + j < S && v != -INFINITY) ? fast_exp2(v - M) : 0.f;
-                Z += w;
+        for (int j = 0; j < kPass; ++j) {
+            lv[j] = k0 + j < S ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lse_l), j))
+                               : -INFINITY;
+            pm = fmaxf(pm, lv[j]);
+        }
+        const float Mn = fmaxf(M, pm);
+        if (Mn == -INFINITY) return;  // nothing seen yet
+        const float r = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+        Z *= r;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float lo = __builtin_bit_cast(float, x[j][e] << 16);
-                    const float hi = __builtin_bit_cast(float, x[j][e] & 0xFFFF0000u);
-                    acc[2 * e] += w != 0.f ? w * lo : 0.f;
-                    acc[2 * e + 1] += w != 0.f ? w * hi : 0.f;
-                }
+        for (int e = 0; e < 8; ++e) acc[e] *= r;
+        M = Mn;
+#pragma unroll
+        for (int j = 0; j < kPass; ++j) {
+            const float w = lv[j] == -INFINITY ? 0.f : fast_exp2(lv[j] - M);
+            Z += w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = __builtin_bit_cast(float, x[j][e] << 16);
+                const float hi = __builtin_bit_cast(float, x[j][e] & 0xFFFF0000u);
+                acc[2 * e] += w != 0.f ? w * lo : 0.f;
+                acc[2 * e + 1] += w != 0.f ? w * hi : 0.f;
             }
         }
+    };
+    if (S <= kPass) {
+        pass(0);  // the usual case: one round trip, no loop
+    } else {
+        for (int k0 = 0; k0 < S; k0 += kPass) pass(k0);
     }
+    // The sink: one more logit with value zero.
+    const float Mf = fmaxf(M, sig);
+    if (Mf != -INFINITY) {
+        const float r = M == -INFINITY ? 0.f : fast_exp2(M - Mf);
+        Z = Z * r + fast_exp2(sig - Mf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= r;
+    }
+    M = Mf;
     const float f = Z > 0.f ? 1.f / Z : 0.f;
     uint16_t* orow = a.out + (int64_t)t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
     u32x4 v = {pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f),

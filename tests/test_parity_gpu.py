@@ -91,6 +91,26 @@ def test_gather_workloads_bit_exact(orc, n):
     check_gather(orc, make_config(n))
 
 
+def widen_extra_table(case, pages):
+    """Pad each request's extra page-table row to `pages` columns with the
+    poison page: the keys do not change, but the row no longer fits the
+    split kernels' LDS copy of the table (1024 pages)."""
+    et = case.extra_page_table
+    wide = np.full((et.shape[0], pages), case.poison_extra_page, dtype=np.int32)
+    wide[:, : et.shape[1]] = et
+    return dataclasses.replace(case, extra_page_table=wide)
+
+
+@pytest.mark.parametrize("i", [9, 12, 14, 17])
+def test_extra_table_wider_than_lds_copy(orc, i):
+    case = widen_extra_table(small_case(i), 1100)
+    log(f"wide extra table {SMALL_IDS[i]}")
+    check_gather(orc, case)
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"wide-{SMALL_IDS[i]}")
+
+
 # --------------------------------------------------------------------------
 # attention, small cases, every row
 # --------------------------------------------------------------------------
