@@ -271,6 +271,9 @@ __device__ __forceinline__ void exchange_partial(float* s_sx, int w, int l, f32x
 // any later MFMA reads the rewritten registers.
 template <int NB>
 __device__ __forceinline__ void scale_accumulators(f32x16 (&oacc)[NB], float alpha) {
+    // Enough wait states for the last MFMA that wrote an accumulator to
+    // retire before the first read-out.
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3");
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
@@ -720,8 +723,11 @@ __global__ __launch_bounds__(256, 1) void attn_regs_kernel(AttnArgs a) {
 // every split's lse and partial row are loaded before any is combined, so a
 // row's merge costs one round of loads.
 // ---------------------------------------------------------------------------
+// kPass: splits per pass (the smallest of 2, 4, 8, 16 that covers the
+// splits, so no load is wasted on a clamped duplicate; more than 16 splits
+// take several passes).
+template <int kPass>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-    constexpr int kPass = 16;
     const int t = blockIdx.x;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
@@ -812,7 +818,14 @@ hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t stream) {
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.T, (unsigned)((a.H + 3) / 4));
-    hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, stream, a);
+    if (a.splits <= 2)
+        hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, a);
+    else if (a.splits <= 4)
+        hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, stream, a);
+    else if (a.splits <= 8)
+        hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
