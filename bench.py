@@ -266,7 +266,8 @@ def main() -> int:
     if args.split_keys:
         dsv4_attn_set_split_keys(args.split_keys)
     splits, chunk = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
-                                   0 if case.extra_page_table is None else case.extra_page_table.shape[1])
+                                   0 if case.extra_page_table is None else case.extra_page_table.shape[1],
+                                   kv_fp8=case.kv == "fp8")
 
     def step(i):
         s = sets[i % n_sets]

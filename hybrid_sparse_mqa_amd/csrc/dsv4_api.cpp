@@ -221,7 +221,15 @@ dsv4_status ensure_zero_row(DeviceState* d) {
     return DSV4_OK;
 }
 
-void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, int32_t* splits, int32_t* chunk) {
+// Keys per split: enough splits per row to fill the chip once, with at
+// least 64 keys per split for bf16 pools (32 for packed FP8, whose kernel
+// stages one tile through registers and is latency-bound on few rows); for
+// bf16 at least 128 keys (4 tiles) when that still occupies half the compute
+// units, which spreads the fixed per-workgroup cost (metadata, Q, partial
+// write) over more tiles.  (Measured on MI355X: C4 decode with 32 rows x 640
+// keys runs 26.1 us with 7 splits and 25.0 us with 5; FP8 C4 decode with 8
+// rows runs 28.0 us with 10 splits and 24.7 us with 20.)
+void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, bool fp8, int32_t* splits, int32_t* chunk) {
     const int64_t head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
     int64_t c;
     if (g_force_split_keys > 0) {
@@ -229,8 +237,13 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, int32_t* splits, i
     } else {
         const int64_t rows = std::max<int64_t>(1, (int64_t)T * head_blocks);
         int64_t want = (cus + rows - 1) / rows;  // splits per row to fill the chip once
-        const int64_t most = std::max<int64_t>(1, (nmax + 63) / 64);  // keep >= 64 keys per split
+        const int64_t min_keys = fp8 ? 32 : 64;
+        const int64_t most = std::max<int64_t>(1, (nmax + min_keys - 1) / min_keys);
         want = std::min(std::max<int64_t>(want, 1), most);
+        if (!fp8) {
+            const int64_t w128 = std::min(want, std::max<int64_t>(1, (nmax + 127) / 128));
+            if (rows * w128 * 2 >= cus) want = w128;
+        }
         c = (nmax + want - 1) / want;
         c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
     }
@@ -367,7 +380,8 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
 }
 
 dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
-                           int32_t c4_width, int32_t extra_pages, int32_t* splits, int32_t* keys_per_split) {
+                           int32_t c4_width, int32_t extra_pages, int32_t kv_fp8, int32_t* splits,
+                           int32_t* keys_per_split) {
     if (splits == nullptr || keys_per_split == nullptr) return fail(DSV4_ERR_INVALID, "NULL output");
     if (compress_ratio != 0 && compress_ratio != 4 && compress_ratio != 128)
         return fail(DSV4_ERR_UNSUPPORTED, "invalid compress_ratio %d (must be 0, 4 or 128)", compress_ratio);
@@ -380,8 +394,8 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
         DeviceState* d = device_state(dev);
         if (d) cus = d->cus;
     }
-    plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages), splits,
-                keys_per_split);
+    plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages),
+                kv_fp8 != 0, splits, keys_per_split);
     return DSV4_OK;
 }
 
@@ -524,7 +538,8 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     a.T = (int32_t)T;
     a.H = (int32_t)H;
     a.scale_log2 = scale * 1.4426950408889634f;
-    plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), &a.splits, &a.chunk);
+    plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), swa.fp8, &a.splits,
+                &a.chunk);
     a.head_blocks = (int32_t)((H + kHeadsPerBlock - 1) / kHeadsPerBlock);
     a.ext_pages = md.P_extra;
     const int64_t n_items = (int64_t)a.T * a.head_blocks * a.splits;

@@ -169,10 +169,13 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
 
 /*
  * Plan that dsv4_attn_forward would use for these sizes: number of splits
- * per row and keys per split.  Host-only, no device access.
+ * per row and keys per split.  kv_fp8 is nonzero for packed FP8 pools (the
+ * two formats run different kernels and are planned differently).
+ * Host-only, no device access.
  */
 dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
-                           int32_t c4_width, int32_t extra_pages, int32_t* splits, int32_t* keys_per_split);
+                           int32_t c4_width, int32_t extra_pages, int32_t kv_fp8, int32_t* splits,
+                           int32_t* keys_per_split);
 
 /*
  * Kernel timing on the caller's stream with HIP events.  While enabled, every
