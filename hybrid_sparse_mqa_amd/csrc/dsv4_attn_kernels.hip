@@ -294,27 +294,41 @@ __device__ __forceinline__ void scale_accumulators(f32x16 (&oacc)[NB], float alp
 
 // Online-softmax step for one 32-key tile (base 2).  `sacc` holds this
 // wave's S^T accumulators already summed over all 512 dims: register r is
-// head (l & 31), tile key 8*(r >> 2) + 4*(l >> 5) + (r & 3).  Produces the
-// bf16 P^T operands of the two PV k-steps.  The running reference only moves
+// head (l & 31), tile key 8*(r >> 2) + 4*(l >> 5) + (r & 3), so lanes l and
+// l ^ 32 hold the two halves of a head's keys.  Produces the bf16 P^T
+// operands of the two PV k-steps.  The running reference m_run only moves
 // when a score exceeds it by more than 2^8 (probabilities stay <= 256), so
-// the 128 output accumulators are rescaled on a tiny fraction of tiles.
+// the output accumulators are rescaled on a tiny fraction of tiles, and only
+// then do the two lanes of a head agree on a new reference (one cross-lane
+// exchange).  l_run is this lane's share of the denominator (its 16 keys per
+// tile); the two shares are added once, in write_result.  A tile whose 32
+// keys are all valid skips the masking.
 template <bool kFp8>
 __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask, float scale_log2, int l,
                                              const float (&sc_key)[16], float& m_run, float& l_run,
                                              f32x16 (&oacc)[8], bf16x8 (&pb)[2], bf16x8 (&pbs)[2]) {
     float sv[16];
     float tmax = -INFINITY;
+    if ((uint32_t)vmask == 0xFFFFFFFFu) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-        const float x = s_all[r] * scale_log2;
-        sv[r] = ((vmask >> key) & 1ull) ? x : -INFINITY;
-        tmax = fmaxf(tmax, sv[r]);
+        for (int r = 0; r < 16; ++r) {
+            sv[r] = s_all[r] * scale_log2;
+            tmax = fmaxf(tmax, sv[r]);
+        }
+    } else {
+        const uint32_t mine = (uint32_t)(vmask >> (4 * (l >> 5)));  // bit 8q + j: key 8q + 4*(l >> 5) + j
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int bit = 8 * (r >> 2) + (r & 3);
+            const float x = s_all[r] * scale_log2;
+            sv[r] = ((mine >> bit) & 1u) ? x : -INFINITY;
+            tmax = fmaxf(tmax, sv[r]);
+        }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool grow = tmax > m_run + kRescaleLog2;
-    if (__any(grow)) {
-        const float m_target = grow ? tmax : m_run;
+    if (__any(tmax > m_run + kRescaleLog2)) {
+        const float hmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the head's tile maximum
+        const bool grow = hmax > m_run + kRescaleLog2;
+        const float m_target = grow ? hmax : m_run;
         const float alpha = fast_exp2(m_run - m_target);  // 0 while nothing was accumulated
         if (__any(grow && m_run != -INFINITY)) {
             scale_accumulators(oacc, alpha);
@@ -331,7 +345,6 @@ __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask
         pb[r >> 3][r & 7] = (__bf16)pr;
         if constexpr (kFp8) pbs[r >> 3][r & 7] = (__bf16)(pr * sc_key[r]);
     }
-    psum += __shfl_xor(psum, 32);
     l_run += psum;
 }
 
@@ -342,7 +355,8 @@ __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask
 // within the output's own rounding) and its base-2 log-sum-exp (-inf for an
 // empty split) for merge_kernel.
 __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int my_head, bool head_ok, int dh,
-                                             int l, const f32x16 (&oacc)[8], float m_run, float l_run) {
+                                             int l, const f32x16 (&oacc)[8], float m_run, float l_half) {
+    const float l_run = l_half + __shfl_xor(l_half, 32);  // both halves of the head's keys
     if (!head_ok) return;
     if (a.splits == 1) {
         const float sig = a.sink != nullptr ? a.sink[my_head] * kLog2e : -INFINITY;
@@ -538,18 +552,18 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
         }
         exchange_partial(s_sx, w, l, sacc);
 
-        bf16x8 pb[2], pbs[2];
-        softmax_tile<false>(sacc, vmask, a.scale_log2, l, no_scale, m_run, l_run, oacc, pb, pbs);
-
         // O^T[d, heads] += K^T[d, keys] P^T[keys, heads].  The K^T operand of
         // lane L (dim 32*mb + (L & 31), keys G(pp, L >> 5)) comes from two
         // transposing reads: source lane S of each 16-lane block points at key
         // row r_k (k = (S >> 2) & 3) and dims d0 .. d0+3, d0 = 16*((S >> 4) & 1)
         // + 4*(S & 3); the block returns dim d0 + j of rows r_0..r_3 to lane
-        // 4*(S & 3) + j.
+        // 4*(S & 3) + j.  These reads do not depend on P: they are issued
+        // before the softmax and land while it runs (the schedule barriers
+        // keep the compiler from sinking them past it).
+        bf16x8 kt[16];
         {
             const int a4 = l & 3, kq = (l >> 2) & 3, hq = l >> 5, half = (l >> 4) & 1;
-            bf16x8 kt[16];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
                 const int d0 = dh * 256 + 32 * mb + 16 * half + 4 * a4;
@@ -564,12 +578,16 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
                     kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
             }
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp)
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+
+        bf16x8 pb[2], pbs[2];
+        softmax_tile<false>(sacc, vmask, a.scale_log2, l, no_scale, m_run, l_run, oacc, pb, pbs);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+                oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
     }
     write_result(a, it, my_head, head_ok, dh, l, oacc, m_run, l_run);
 }
