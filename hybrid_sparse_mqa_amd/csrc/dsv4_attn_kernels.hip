@@ -352,53 +352,74 @@ __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask
 // dim 256*dh + 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3).  One split: apply
 // the sink and write out / lse.  Several: publish the normalised partial (in
 // bf16: it is a convex combination of key rows, so 8 significant bits keep it
-// within the output's own rounding) and its base-2 log-sum-exp (-inf for an
-// empty split) for merge_kernel.
-__device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int my_head, bool head_ok, int dh,
-                                             int l, const f32x16 (&oacc)[8], float m_run, float l_half) {
+// within the output's own rounding; an empty split publishes zeros) and its
+// base-2 log-sum-exp (-inf for an empty split) for merge_kernel.
+// The bf16 rows are first assembled in LDS (stage_lo / stage_hi for the two
+// head halves: 32 head rows of
+// 1 KiB, 16-byte chunk c of row r at chunk c ^ r), so that every global
+// store instruction writes one whole 1 KiB row.  The caller's LDS must be
+// free: the first barrier below waits until every wave is done with it.
+__device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int hh, int dh, int l,
+                                             const f32x16 (&oacc)[8], float m_run, float l_half,
+                                             uint8_t* stage_lo, uint8_t* stage_hi) {
+    uint8_t* stage = hh ? stage_hi : stage_lo;
     const float l_run = l_half + __shfl_xor(l_half, 32);  // both halves of the head's keys
-    if (!head_ok) return;
+    const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
+    const bool head_ok = my_head < a.H;
+    float f = 0.f, lse2 = -INFINITY;
     if (a.splits == 1) {
-        const float sig = a.sink != nullptr ? a.sink[my_head] * kLog2e : -INFINITY;
+        const float sig = a.sink != nullptr && head_ok ? a.sink[my_head] * kLog2e : -INFINITY;
         const float M = fmaxf(m_run, sig);
-        float f = 0.f, lse2 = -INFINITY;
         if (M != -INFINITY) {
             const float em = fast_exp2(m_run - M);
             const float den = l_run * em + fast_exp2(sig - M);
             f = em / den;
             lse2 = M + fast_log2(den);
         }
-        uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)my_head * a.out_s1;
+    } else if (l_run > 0.f) {
+        f = 1.f / l_run;
+        lse2 = m_run + fast_log2(l_run);
+    }
+    __syncthreads();  // every wave is done with the LDS the rows are staged in
+    {
+        const int r = l & 31;
+        uint8_t* base = stage + r * 1024 + 8 * (l >> 5);
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const int d = dh * 256 + 32 * mb + 8 * qd + 4 * (l >> 5);
+                const int c = dh * 32 + 4 * mb + qd;
                 const f32x16& o = oacc[mb];
-                u32x2 v = {pack_bf16x2(o[4 * qd] * f, o[4 * qd + 1] * f), pack_bf16x2(o[4 * qd + 2] * f, o[4 * qd + 3] * f)};
-                *(u32x2*)(orow + d) = v;
-            }
-        }
-        if (a.lse != nullptr && dh == 0 && l < 32) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
-        return;
-    }
-    const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + my_head;
-    if (l_run > 0.f) {
-        const float inv = 1.f / l_run;
-        uint16_t* orow = a.ws_o + part * kHeadDim;
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int d = dh * 256 + 32 * mb + 8 * qd + 4 * (l >> 5);
-                const f32x16& o = oacc[mb];
-                u32x2 v = {pack_bf16x2(o[4 * qd] * inv, o[4 * qd + 1] * inv),
-                           pack_bf16x2(o[4 * qd + 2] * inv, o[4 * qd + 3] * inv)};
-                *(u32x2*)(orow + d) = v;
+                *(u32x2*)(base + 16 * (c ^ r)) = u32x2{pack_bf16x2(o[4 * qd] * f, o[4 * qd + 1] * f),
+                                                       pack_bf16x2(o[4 * qd + 2] * f, o[4 * qd + 3] * f)};
             }
         }
     }
-    if (dh == 0 && l < 32) a.ws_lse[part] = l_run > 0.f ? m_run + fast_log2(l_run) : -INFINITY;
+    __syncthreads();
+    // Wave (hh, dh) stores rows 16*dh .. 16*dh+15 of its half; lane l moves
+    // the row's 16-byte chunk l.
+#pragma unroll 4
+    for (int e = 0; e < 16; ++e) {
+        const int r = 16 * dh + e;
+        const int head = it.hb * kHeadsPerBlock + hh * 32 + r;
+        if (head >= a.H) break;
+        const u32x4 v = *(const u32x4*)(stage + r * 1024 + 16 * (l ^ r));
+        if (a.splits == 1) {
+            uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
+            *(u32x2*)orow = u32x2{v[0], v[1]};  // out rows need only 8-byte alignment
+            *(u32x2*)(orow + 4) = u32x2{v[2], v[3]};
+        } else {
+            const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + head;
+            *(u32x4*)(a.ws_o + part * kHeadDim + 8 * l) = v;
+        }
+    }
+    if (head_ok && dh == 0 && l < 32) {
+        if (a.splits == 1) {
+            if (a.lse != nullptr) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
+        } else {
+            a.ws_lse[((int64_t)it.t * a.splits + it.s) * a.H + my_head] = lse2;
+        }
+    }
 }
 
 }  // namespace
@@ -460,8 +481,6 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63;
     const int hh = w >> 1, dh = w & 1;
-    const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
-    const bool head_ok = my_head < a.H;
 
     const RowKeys rk = row_keys(a.m, it.t, l);
     const int k0 = it.s * a.chunk;
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
             for (int pp = 0; pp < 2; ++pp)
                 oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
     }
-    write_result(a, it, my_head, head_ok, dh, l, oacc, m_run, l_run);
+    write_result(a, it, hh, dh, l, oacc, m_run, l_run, &s_tile[0][0], &s_tile[1][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,7 +752,7 @@ __global__ __launch_bounds__(256, 1) void attn_regs_kernel(AttnArgs a) {
         }
         __syncthreads();
     }
-    write_result(a, it, my_head, head_ok, dh, l, oacc, m_run, l_run);
+    write_result(a, it, hh, dh, l, oacc, m_run, l_run, s_krow, s_kt);
 }
 
 // ---------------------------------------------------------------------------
