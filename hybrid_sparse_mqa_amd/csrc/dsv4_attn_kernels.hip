@@ -57,10 +57,12 @@ __device__ __forceinline__ int group_key(int w, int e) {
 
 // Row-major tile: 32 rows of 1 KiB; 16-byte chunk c of row k is stored at
 // chunk c ^ row_swz(k).  row_swz is a permutation of 0..15 over any 16
-// consecutive rows (and of 0..7 over any aligned 8), so row reads at one
-// column are conflict-free; it also gives the 4 rows x 2 adjacent chunks
-// that one transposing read touches 8 distinct bank slots.
-__device__ __forceinline__ int row_swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+// consecutive rows, so 16 lanes reading one column of 16 rows hit 16
+// distinct 16-byte bank groups; and the 4 rows k = 4q .. 4q+3 are spread
+// by 4 chunks each, so the 4 rows x 4 chunks that 32 lanes of a
+// transposing read touch (rows 4q + j, chunks 4m .. 4m+3) land in 16
+// distinct bank groups.
+__device__ __forceinline__ int row_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int krow_offset(int k, int chunk) { return k * 1024 + 16 * (chunk ^ row_swz(k)); }
 
 // Column tile: group g (8 keys) x 512 dims x 16 bytes; dim d is stored at
@@ -556,7 +558,6 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
         else wait_vmcnt<0>();
         const uint64_t vmask = __ballot(l < 32 && s_addr[i * kTileKeys + (l & 31)] != zero_row);
         __syncthreads();  // tile i is in LDS for every wave; stage (i-1) % kStages is free
-        if (i + kStages - 1 < n_tiles) fetch_tile(i + kStages - 1);
 
         const uint8_t* tile = &s_tile[i % kStages][0];
         // S^T partial over this wave's 256 dims (operands read ahead of the MFMAs).
@@ -569,6 +570,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
         }
+        if (i + kStages - 1 < n_tiles) fetch_tile(i + kStages - 1);
         exchange_partial(s_sx, w, l, sacc);
 
         // O^T[d, heads] += K^T[d, keys] P^T[keys, heads].  The K^T operand of
