@@ -160,7 +160,12 @@ def record_traffic(config: int, split_keys: int, fetch_dir: str, write_dir: str,
     from synth import make_config
 
     case = make_config(config)
-    name = "attn_regs_kernel" if case.kv == "fp8" else "attn_dma_kernel"
+    from hybrid_sparse_mqa_amd import dsv4_attn_plan
+
+    _, _, hpw = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
+                               0 if case.extra_page_table is None else case.extra_page_table.shape[1],
+                               kv_fp8=case.kv == "fp8")
+    name = "attn_fp8_kernel" if case.kv == "fp8" else "attn_team_kernel" if hpw == 32 else "attn_wide_kernel"
 
     def pick(d, key):
         hits = {k: v for k, v in d.items() if key in k}
@@ -265,7 +270,7 @@ def main() -> int:
 
     if args.split_keys:
         dsv4_attn_set_split_keys(args.split_keys)
-    splits, chunk = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
+    splits, chunk, heads_per_wg = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
                                    0 if case.extra_page_table is None else case.extra_page_table.shape[1],
                                    kv_fp8=case.kv == "fp8")
 
@@ -338,7 +343,8 @@ def main() -> int:
     merge_avg_ms = merge_ms / calls
     kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
     achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
-    kernel_name = "attn_regs_kernel" if case.kv == "fp8" else "attn_dma_kernel"
+    kernel_name = ("attn_fp8_kernel" if case.kv == "fp8" else
+                   "attn_team_kernel" if heads_per_wg == 32 else "attn_wide_kernel")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -360,6 +366,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": dict(describe_workload(args.config, case), splits=int(splits), keys_per_split=int(chunk),
+                       heads_per_workgroup=int(heads_per_wg),
                        input_sets=int(n_sets), cache="cold-rotated" if cold else "warm-rotated",
                        timed="HIP graph replay", parallelism="single GPU"),
         "path": {

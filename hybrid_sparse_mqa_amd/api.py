@@ -92,14 +92,21 @@ def dsv4_attn_set_split_keys(keys_per_split: int) -> None:
     N.check(N.load().dsv4_attn_set_split_keys(int(keys_per_split)))
 
 
+def dsv4_attn_set_heads_per_workgroup(heads: int) -> None:
+    N.check(N.load().dsv4_attn_set_heads_per_workgroup(int(heads)))
+
+
 def dsv4_attn_plan(num_rows, num_heads, compress_ratio, window, c4_width=0, extra_pages=0,
-                   kv_fp8=False) -> Tuple[int, int]:
-    """(splits per row, keys per split) that dsv4_attn_forward would use."""
+                   kv_fp8=False) -> Tuple[int, int, int]:
+    """(splits per row and head block, keys per split, heads per workgroup)
+    that dsv4_attn_forward would use."""
     s = ctypes.c_int32()
     c = ctypes.c_int32()
+    h = ctypes.c_int32()
     N.check(N.load().dsv4_attn_plan(int(num_rows), int(num_heads), int(compress_ratio), int(window), int(c4_width),
-                                    int(extra_pages), int(bool(kv_fp8)), ctypes.byref(s), ctypes.byref(c)))
-    return s.value, c.value
+                                    int(extra_pages), int(bool(kv_fp8)), ctypes.byref(s), ctypes.byref(c),
+                                    ctypes.byref(h)))
+    return s.value, c.value, h.value
 
 
 def dsv4_attn_workspace_reserve(nbytes: int) -> None:

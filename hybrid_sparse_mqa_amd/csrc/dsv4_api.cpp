@@ -181,6 +181,7 @@ struct DeviceState {
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
 int32_t g_force_split_keys = 0;
+int32_t g_force_heads_per_workgroup = 0;  // 0: automatic; 32 or 64 for bf16 pools
 
 DeviceState* device_state(int dev) {
     if (dev < 0) return nullptr;
@@ -229,8 +230,40 @@ dsv4_status ensure_zero_row(DeviceState* d) {
 // write) over more tiles.  (Measured on MI355X: C4 decode with 32 rows x 640
 // keys runs 26.1 us with 7 splits and 25.0 us with 5; FP8 C4 decode with 8
 // rows runs 28.0 us with 10 splits and 24.7 us with 20.)
-void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, bool fp8, int32_t* splits, int32_t* chunk) {
-    const int64_t head_blocks = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+// Kernel layout.  bf16 pools take the team kernel (32-head blocks, two teams
+// of waves on alternate tiles) when doubling the head blocks buys out most of
+// the key splitting: when the rows alone, in 64-head blocks, fill less than a
+// quarter of the chip (short key splits whose partials and merge dominate),
+// or when 32-head blocks fill the whole chip without any split.  Otherwise
+// the wide kernel (64-head blocks, one tile per step, three tiles in flight)
+// moves keys faster.  Measured on MI355X, graph replay, cold inputs: C4
+// decode 32 rows x 640 keys 23.9 -> 22.7 us (team), C4 verify 128 rows
+// 37.5 -> 36.6 us (team), C128 decode 64 rows x 1152 keys 36.2 (wide) vs
+// 38.0 us (team).
+Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
+    if (fp8) return Layout::kFp8;
+    if (g_force_heads_per_workgroup == kTeamHeadsPerBlock) return Layout::kTeam;
+    if (g_force_heads_per_workgroup == kWideHeadsPerBlock) return Layout::kWide;
+    const int64_t wide_rows = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
+    const int64_t team_rows = (int64_t)T * ((H + kTeamHeadsPerBlock - 1) / kTeamHeadsPerBlock);
+    if (wide_rows * 4 < cus || team_rows >= cus) return Layout::kTeam;
+    return Layout::kWide;
+}
+
+int32_t heads_per_block(Layout layout) { return layout == Layout::kTeam ? kTeamHeadsPerBlock : kWideHeadsPerBlock; }
+
+// Keys per split: enough splits per row to fill the chip once, with at
+// least 64 keys per split for bf16 pools (32 for packed FP8, whose kernel
+// stages one tile through registers and is latency-bound on few rows); for
+// bf16 at least 128 keys (4 tiles) when that still occupies half the compute
+// units, which spreads the fixed per-workgroup cost (metadata, Q, partial
+// write) over more tiles.  The team kernel takes whole tile pairs.
+// (Measured on MI355X: FP8 C4 decode with 8 rows runs 28.0 us with 10
+// splits and 24.7 us with 20.)
+void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int32_t* splits, int32_t* chunk) {
+    const bool fp8 = layout == Layout::kFp8;
+    const int64_t hpb = heads_per_block(layout);
+    const int64_t head_blocks = (H + hpb - 1) / hpb;
     int64_t c;
     if (g_force_split_keys > 0) {
         c = g_force_split_keys;
@@ -245,7 +278,8 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, bool fp8, int32_t*
             if (rows * w128 * 2 >= cus) want = w128;
         }
         c = (nmax + want - 1) / want;
-        c = (c + kTileKeys - 1) / kTileKeys * kTileKeys;
+        const int64_t unit = layout == Layout::kTeam ? 2 * kTileKeys : kTileKeys;
+        c = (c + unit - 1) / unit * unit;
     }
     c = std::min<int64_t>(std::max<int64_t>(c, kTileKeys), kMaxSplitKeys);
     *chunk = (int32_t)c;
@@ -379,9 +413,18 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
     return DSV4_OK;
 }
 
+dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads) {
+    if (heads != 0 && heads != kTeamHeadsPerBlock && heads != kWideHeadsPerBlock)
+        return fail(DSV4_ERR_INVALID, "heads per workgroup must be 0, %d or %d", kTeamHeadsPerBlock,
+                    kWideHeadsPerBlock);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_force_heads_per_workgroup = heads;
+    return DSV4_OK;
+}
+
 dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
                            int32_t c4_width, int32_t extra_pages, int32_t kv_fp8, int32_t* splits,
-                           int32_t* keys_per_split) {
+                           int32_t* keys_per_split, int32_t* heads_per_workgroup) {
     if (splits == nullptr || keys_per_split == nullptr) return fail(DSV4_ERR_INVALID, "NULL output");
     if (compress_ratio != 0 && compress_ratio != 4 && compress_ratio != 128)
         return fail(DSV4_ERR_UNSUPPORTED, "invalid compress_ratio %d (must be 0, 4 or 128)", compress_ratio);
@@ -394,8 +437,10 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
         DeviceState* d = device_state(dev);
         if (d) cus = d->cus;
     }
+    const Layout layout = choose_layout(cus, num_rows, num_heads, kv_fp8 != 0);
     plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages),
-                kv_fp8 != 0, splits, keys_per_split);
+                layout, splits, keys_per_split);
+    if (heads_per_workgroup != nullptr) *heads_per_workgroup = heads_per_block(layout);
     return DSV4_OK;
 }
 
@@ -538,9 +583,10 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     a.T = (int32_t)T;
     a.H = (int32_t)H;
     a.scale_log2 = scale * 1.4426950408889634f;
-    plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), swa.fp8, &a.splits,
+    const Layout layout = choose_layout(d->cus, a.T, a.H, swa.fp8);
+    plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), layout, &a.splits,
                 &a.chunk);
-    a.head_blocks = (int32_t)((H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    a.head_blocks = (int32_t)((H + heads_per_block(layout) - 1) / heads_per_block(layout));
     a.ext_pages = md.P_extra;
     const int64_t n_items = (int64_t)a.T * a.head_blocks * a.splits;
     if (n_items > (int64_t)1 << 30) return fail(DSV4_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)n_items);
@@ -566,7 +612,7 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
         if (!rec.e0 || !rec.e1 || !rec.e2) return fail(DSV4_ERR_HIP, "hipEventCreate failed");
         DSV4_HIP(record_event(rec.e0, st));
     }
-    DSV4_HIP(launch_attention(a, swa.fp8, st));
+    DSV4_HIP(launch_attention(a, layout, st));
     if (g_timing) DSV4_HIP(record_event(rec.e1, st));
     if (a.splits > 1) DSV4_HIP(launch_merge(a, st));
     if (g_timing) {

@@ -2,33 +2,37 @@
 // decode / verify path.
 //
 //  * gather_kernel: the paged gather stage alone (canonical slot lists).
-//  * attn_dma_kernel (bf16 KV) and attn_regs_kernel (FP8 KV): gather + KV
-//    tile load (+ FP8 decode) + scores + online softmax + PV for one (query
-//    row, 64-head block, key split); with a single split they also apply the
-//    sink and write out / lse.
+//  * split kernels -- gather + KV tile load (+ FP8 decode) + scores + online
+//    softmax + PV for one (query row, head block, key split); with a single
+//    split they also apply the sink and write out / lse:
+//      attn_wide_kernel  bf16 KV, 64-head blocks, one 32-key tile per step;
+//      attn_team_kernel  bf16 KV, 32-head blocks, two teams of two waves
+//                        taking alternate tiles (fewer splits for the same
+//                        parallelism);
+//      attn_fp8_kernel   packed FP8 KV, 64-head blocks.
 //  * merge_kernel: log-sum-exp merge of the split partials with the per-head
 //    sink folded in once (test-matrix page, attention-sink correction).
-//    All 64 heads share each KV row (MQA with one KV head, walk-through page
-//    section 1), so a key tile is fetched from HBM once per workgroup into LDS
-//    and feeds both products on bf16 MFMA (v_mfma_f32_32x32x16_bf16):
+//    All query heads share each KV row (MQA with one KV head, walk-through
+//    page section 1), so a key tile is fetched from HBM once per workgroup into
+//    LDS and feeds both products on bf16 MFMA (v_mfma_f32_32x32x16_bf16):
 //        S^T[keys, heads]  = K[keys, d] . Q^T[d, heads]
 //        O^T[d, heads]    += K^T[d, keys] . P^T[keys, heads]      (V = K)
-//    The second product reduces over keys.  The bf16 kernel streams key rows
-//    straight from HBM into a 4-stage LDS ring (global_load_lds, 3 tiles in
-//    flight) and reads PV operands with the gfx950 transposing LDS read
-//    (ds_read_b64_tr_b16).  The FP8 kernel stages rows through registers,
-//    decodes them, and writes the tile twice (row-major for S, 8-key columns
-//    for PV, via an in-register 8x8 transpose).
+//    The second product reduces over keys.  The bf16 kernels stream key rows
+//    straight from HBM into a 4-stage LDS ring (global_load_lds) and read PV
+//    operands with the gfx950 transposing LDS read (ds_read_b64_tr_b16).  The
+//    FP8 kernel stages rows through registers, decodes them, and writes the
+//    tile twice (row-major for S, 8-key columns for PV, via an in-register
+//    8x8 transpose).
 //
-// Workgroup = 4 waves (256 lanes).  Wave w = 2*hh + dh owns heads
-// [32*hh, 32*hh+32) of the block and head dims [256*dh, 256*dh+256).  The two
-// dh waves of a head half each reduce S over their half of the dims and sum the
-// halves through LDS; both then run the same online softmax and accumulate O^T
-// for their own 256 dims (8 MFMA tiles of 32x32 = 128 fp32 accumulators).
+// Every wave owns 32 heads x 256 head dims of a tile: the two waves that share
+// a head set each reduce S over their half of the dims and sum the halves
+// through LDS; both then run the same online softmax and accumulate O^T for
+// their own 256 dims (8 MFMA tiles of 32x32 = 128 fp32 accumulators).
 //
 // Work items (row, head block, split) are laid out so that consecutive
-// items -- the splits of one row -- go to the same XCD (workgroups are
-// dispatched to the 8 XCDs round robin), which keeps a row's Q in one L2.
+// items -- the head blocks and splits of one row -- go to the same XCD
+// (workgroups are dispatched to the 8 XCDs round robin), which keeps a row's
+// Q and key rows shared in one L2.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -366,7 +370,7 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, 
                                              uint8_t* stage_lo, uint8_t* stage_hi) {
     uint8_t* stage = hh ? stage_hi : stage_lo;
     const float l_run = l_half + __shfl_xor(l_half, 32);  // both halves of the head's keys
-    const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
+    const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
     const bool head_ok = my_head < a.H;
     float f = 0.f, lse2 = -INFINITY;
     if (a.splits == 1) {
@@ -403,7 +407,7 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, 
 #pragma unroll 4
     for (int e = 0; e < 16; ++e) {
         const int r = 16 * dh + e;
-        const int head = it.hb * kHeadsPerBlock + hh * 32 + r;
+        const int head = it.hb * kWideHeadsPerBlock + hh * 32 + r;
         if (head >= a.H) break;
         const u32x4 v = *(const u32x4*)(stage + r * 1024 + 16 * (l ^ r));
         if (a.splits == 1) {
@@ -468,10 +472,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 KV: key rows stream from HBM into a 4-stage LDS ring with direct
-// global->LDS loads (no VGPR staging), three tiles in flight per workgroup.
+// bf16 KV, wide layout: one workgroup per (row, block of 64 heads, key
+// split); wave w = 2*hh + dh owns heads [32*hh, 32*hh + 32) and head dims
+// [256*dh, 256*dh + 256) of every tile.  Key rows stream from HBM into a
+// 4-stage LDS ring with direct global->LDS loads (no VGPR staging), three
+// tiles in flight.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
     __shared__ int32_t s_slot[kMaxSplitKeys];
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int k = 16 * w + e;
-            const int head = it.hb * kHeadsPerBlock + k;
+            const int head = it.hb * kWideHeadsPerBlock + k;
             const uint8_t* src = head < a.H ? (const uint8_t*)(a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1)
                                             : a.zero_row;
             dma16(src + 16 * (l ^ row_swz(k)), lds_addr(qs + k * 1024));
@@ -614,12 +621,231 @@ __global__ __launch_bounds__(256, 1) void attn_dma_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 KV, team layout: one workgroup per (row, block of 32 heads, key split).  Key rows
+// stream from HBM into a 4-stage LDS ring with direct global->LDS loads (no
+// VGPR staging).  The four waves form two teams of two: team p takes the
+// split's tiles 2j + p, so a pair of tiles is processed per step, and within
+// a team wave dh owns head dims [256*dh, 256*dh + 256) of all 32 heads (its
+// partner holds the other half of each score).  Each team keeps its own
+// online softmax; the two are merged in the epilogue.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void attn_team_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
+    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
+    __shared__ int32_t s_slot[kMaxSplitKeys];
+    __shared__ int32_t s_table[kTableCap];
+    __shared__ __attribute__((aligned(16))) uint64_t s_addr[kMaxSplitKeys];
+
+    Item it;
+    if (!decode_item(a, it)) return;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;  // wave-uniform
+    const int team = w >> 1, dh = w & 1;
+    const int head0 = it.hb * kTeamHeadsPerBlock;
+
+    const RowKeys rk = row_keys(a.m, it.t, l);
+    const int k0 = it.s * a.chunk;
+    const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
+    build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+    build_row_addresses(a, rk, k0, n_here, s_slot, s_addr, tid);
+    const uint64_t zero_row = (uint64_t)(uintptr_t)a.zero_row;
+
+    // Wave w copies tile keys 8w .. 8w+7: their row addresses come from LDS
+    // (four 16-byte broadcast reads) and lane l moves logical chunk
+    // l ^ row_swz(k) so that each row lands in the swizzled layout.
+    auto fetch_tile = [&](int tile) {
+        uint8_t* dst = &s_tile[tile % kStages][0];
+        const u64x2* ap = (const u64x2*)&s_addr[tile * kTileKeys + 8 * w];
+        const u64x2 a01 = ap[0], a23 = ap[1], a45 = ap[2], a67 = ap[3];
+        const uint64_t rows[8] = {a01[0], a01[1], a23[0], a23[1], a45[0], a45[1], a67[0], a67[1]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            dma16((const uint8_t*)(uintptr_t)rows[e] + 16 * (l ^ row_swz(8 * w + e)), lds_addr(dst + (8 * w + e) * 1024));
+    };
+
+    f32x16 oacc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float no_scale[16] = {};
+
+    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
+    const int n_pairs = (n_tiles + 1) / 2;
+    // Retire every compiler-visible load (slot metadata) first, so the only
+    // vector-memory operations in flight below are this wave's copies into
+    // LDS (8 for Q, then 8 per tile) and the explicit vmcnt waits count
+    // exactly those.
+    wait_vmcnt<0>();
+    // Q travels the same way as the keys: the block's 32 head rows (zero rows
+    // past H) go to ring stage 3, in the swizzled row layout, together with
+    // tiles 0 and 1.  Once every wave holds its Q operands, stage 3 returns
+    // to the ring and tiles 2 and 3 are requested.
+    bf16x8 qf[16];
+    if (n_tiles > 0) {
+        uint8_t* qs = &s_tile[3][0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = 8 * w + e;
+            const int head = head0 + k;
+            const uint8_t* src = head < a.H ? (const uint8_t*)(a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1)
+                                            : a.zero_row;
+            dma16(src + 16 * (l ^ row_swz(k)), lds_addr(qs + k * 1024));
+        }
+        fetch_tile(0);
+        if (n_tiles > 1) fetch_tile(1);
+        wait_vmcnt<0>();
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qf[j] = *(const bf16x8*)(qs + krow_offset(l & 31, dh * 32 + 2 * j + (l >> 5)));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave has its Q: stage 3 is free
+        if (n_tiles > 2) fetch_tile(2);
+        if (n_tiles > 3) fetch_tile(3);
+    }
+
+    for (int j = 0; j < n_pairs; ++j) {
+        if (j > 0) {
+            // The pair fetched at the previous step is the only one in flight.
+            wait_vmcnt<0>();
+            __syncthreads();  // tiles 2j, 2j+1 are in LDS for every wave; pair j-1's stages are free
+            if (2 * j + 2 < n_tiles) fetch_tile(2 * j + 2);
+            if (2 * j + 3 < n_tiles) fetch_tile(2 * j + 3);
+        }
+        // Team 1 has no tile when the split's tile count is odd and this is
+        // the last pair: it then runs on team 0's tile under an empty key
+        // mask, so every probability is zero, its reference does not move and
+        // the PV products add zero times finite keys.
+        const int ti = 2 * j + team;
+        const bool busy = ti < n_tiles;
+        const uint8_t* tile = &s_tile[(busy ? ti : 2 * j) % kStages][0];
+        const uint64_t vmask = __ballot(busy && l < 32 && s_addr[ti * kTileKeys + (l & 31)] != zero_row);
+
+        // S^T partial over this wave's 256 dims (operands read ahead of the MFMAs).
+        f32x16 sacc = f32x16{};
+        {
+            const int k = l & 31;
+            bf16x8 av[16];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) av[jj] = *(const bf16x8*)(tile + krow_offset(k, dh * 32 + 2 * jj + (l >> 5)));
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[jj], qf[jj], sacc, 0, 0, 0);
+        }
+        exchange_partial(s_sx, w, l, sacc);
+
+        {
+            // O^T[d, heads] += K^T[d, keys] P^T[keys, heads].  The K^T operand
+            // of lane L (dim 32*mb + (L & 31), keys G(pp, L >> 5)) comes from
+            // two transposing reads: source lane S of each 16-lane block points
+            // at key row r_k (k = (S >> 2) & 3) and dims d0 .. d0+3, d0 =
+            // 16*((S >> 4) & 1) + 4*(S & 3); the block returns dim d0 + j of
+            // rows r_0..r_3 to lane 4*(S & 3) + j.  These reads do not depend
+            // on P: they are issued before the softmax and land while it runs
+            // (the schedule barriers keep the compiler from sinking them).
+            bf16x8 kt[16];
+            {
+                const int a4 = l & 3, kq = (l >> 2) & 3, hq = l >> 5, half = (l >> 4) & 1;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) {
+                    const int d0 = dh * 256 + 32 * mb + 16 * half + 4 * a4;
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int r0 = 16 * pp + 4 * hq + kq;
+                        const int r1 = r0 + 8;
+                        const uint8_t* p0 = tile + krow_offset(r0, d0 >> 3) + 2 * (d0 & 7);
+                        const uint8_t* p1 = tile + krow_offset(r1, d0 >> 3) + 2 * (d0 & 7);
+                        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+                        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+                        kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            bf16x8 pb[2], pbs[2];
+            softmax_tile<false>(sacc, vmask, a.scale_log2, l, no_scale, m_run, l_run, oacc, pb, pbs);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp)
+                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
+        }
+    }
+
+    // Epilogue.  Accumulator r of tile mb holds head (l & 31), dim 256*dh +
+    // 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3), unnormalised, with the
+    // team's running reference m_run and (per lane) half of its denominator.
+    // Each team's fp32 rows go to LDS (team p: 32 rows of 2 KiB at byte
+    // 65536*p, 16-byte chunk c of row r at chunk c ^ r), then wave w merges
+    // rows 8w .. 8w+7 of the two teams, lane l owning dims 8l .. 8l+7, and
+    // writes either the output with the sink folded in (one split) or the
+    // normalised bf16 partial and its base-2 log-sum-exp (several).
+    {
+        const float l_sum = l_run + __shfl_xor(l_run, 32);  // both halves of the head's keys
+        float (*s_ml)[2][kTeamHeadsPerBlock] = (float (*)[2][kTeamHeadsPerBlock])s_sx;  // [team][m, l][head]
+        __syncthreads();  // every wave is done with the ring and the exchange buffer
+        uint8_t* stage = &s_tile[0][0] + 65536 * team;
+        const int r = l & 31;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const int c = dh * 64 + 8 * mb + 2 * qd + (l >> 5);
+                const f32x16& o = oacc[mb];
+                *(f32x4*)(stage + r * 2048 + 16 * (c ^ r)) = f32x4{o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]};
+            }
+        if (dh == 0 && l < 32) {
+            s_ml[team][0][r] = l_sum > 0.f ? m_run : -INFINITY;
+            s_ml[team][1][r] = l_sum;
+        }
+        __syncthreads();
+        for (int e = 0; e < 8; ++e) {
+            const int rr = 8 * w + e;
+            const int head = head0 + rr;
+            if (head >= a.H) break;
+            const float m0 = s_ml[0][0][rr], l0 = s_ml[0][1][rr];
+            const float m1 = s_ml[1][0][rr], l1 = s_ml[1][1][rr];
+            const float sig = (a.splits == 1 && a.sink != nullptr) ? a.sink[head] * kLog2e : -INFINITY;
+            const float M = fmaxf(fmaxf(m0, m1), sig);
+            float e0 = 0.f, e1 = 0.f, Z = 0.f;
+            if (M != -INFINITY) {
+                e0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - M);
+                e1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+                Z = l0 * e0 + l1 * e1 + (sig == -INFINITY ? 0.f : fast_exp2(sig - M));
+            }
+            const float f = Z > 0.f ? 1.f / Z : 0.f;
+            const float w0 = e0 * f, w1 = e1 * f;
+            const uint8_t* row0 = &s_tile[0][0] + rr * 2048;
+            const uint8_t* row1 = row0 + 65536;
+            const f32x4 a0 = *(const f32x4*)(row0 + 16 * ((2 * l) ^ rr));
+            const f32x4 a1 = *(const f32x4*)(row0 + 16 * ((2 * l + 1) ^ rr));
+            const f32x4 b0 = *(const f32x4*)(row1 + 16 * ((2 * l) ^ rr));
+            const f32x4 b1 = *(const f32x4*)(row1 + 16 * ((2 * l + 1) ^ rr));
+            const u32x4 v = {pack_bf16x2(a0[0] * w0 + b0[0] * w1, a0[1] * w0 + b0[1] * w1),
+                             pack_bf16x2(a0[2] * w0 + b0[2] * w1, a0[3] * w0 + b0[3] * w1),
+                             pack_bf16x2(a1[0] * w0 + b1[0] * w1, a1[1] * w0 + b1[1] * w1),
+                             pack_bf16x2(a1[2] * w0 + b1[2] * w1, a1[3] * w0 + b1[3] * w1)};
+            const float lse2 = Z > 0.f ? M + fast_log2(Z) : -INFINITY;
+            if (a.splits == 1) {
+                uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
+                *(u32x2*)orow = u32x2{v[0], v[1]};  // out rows need only 8-byte alignment
+                *(u32x2*)(orow + 4) = u32x2{v[2], v[3]};
+                if (a.lse != nullptr && l == 0) a.lse[(int64_t)it.t * a.lse_s0 + head] = lse2 * kLn2;
+            } else {
+                const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + head;
+                *(u32x4*)(a.ws_o + part * kHeadDim + 8 * l) = v;
+                if (l == 0) a.ws_lse[part] = lse2;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Packed FP8 KV: rows staged through registers (one tile ahead), decoded, and
 // written to LDS row-major and as 8-key columns.  E4M3 codes are exact in
 // bf16; the per-token scale multiplies the fp32 non-rotary score partial and
 // is folded into P for the non-rotary PV tiles.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void attn_regs_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_krow[kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[4 * 512 * 16];
     __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
@@ -632,7 +858,7 @@ __global__ __launch_bounds__(256, 1) void attn_regs_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63;
     const int hh = w >> 1, dh = w & 1;
-    const int my_head = it.hb * kHeadsPerBlock + hh * 32 + (l & 31);
+    const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
     const bool head_ok = my_head < a.H;
 
     bf16x8 qf[16];
@@ -845,13 +1071,20 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t stream) {
+hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream) {
     const int per_xcd = (a.n_items + 7) / 8;
     const dim3 grid((unsigned)(8 * per_xcd));
-    if (fp8)
-        hipLaunchKernelGGL(attn_regs_kernel, grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(attn_dma_kernel, grid, dim3(256), 0, stream, a);
+    switch (layout) {
+        case Layout::kFp8:
+            hipLaunchKernelGGL(attn_fp8_kernel, grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kTeam:
+            hipLaunchKernelGGL(attn_team_kernel, grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kWide:
+            hipLaunchKernelGGL(attn_wide_kernel, grid, dim3(256), 0, stream, a);
+            break;
+    }
     return hipGetLastError();
 }
 

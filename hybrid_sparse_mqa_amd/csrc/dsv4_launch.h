@@ -11,9 +11,15 @@ namespace dsv4 {
 
 constexpr int kTileKeys = 32;        // keys per LDS tile
 constexpr int kMaxSplitKeys = 1024;  // keys one workgroup may own (LDS slot list)
-constexpr int kHeadsPerBlock = 64;   // query heads per workgroup (two halves of 32)
+constexpr int kWideHeadsPerBlock = 64;  // query heads per workgroup, wide bf16 and FP8 kernels
+constexpr int kTeamHeadsPerBlock = 32;  // query heads per workgroup, team bf16 kernel
+
+// Which split kernel runs: bf16 with 64 heads per workgroup (one tile per
+// step), bf16 with 32 heads per workgroup (two teams, a tile pair per step),
+// or packed FP8 (64 heads per workgroup).
+enum class Layout { kWide, kTeam, kFp8 };
 constexpr int kTableCap = 1024;      // extra page-table entries a workgroup caches in LDS
-constexpr int kStages = 4;           // bf16 key tiles resident in LDS (3 in flight + 1 in use)
+constexpr int kStages = 4;           // bf16 key tiles resident in LDS
 
 struct AttnArgs {
     Meta m;
@@ -28,7 +34,7 @@ struct AttnArgs {
     float scale_log2;         // scale * log2(e)
     int32_t chunk;            // keys per split (multiple of kTileKeys)
     int32_t splits;           // splits per (row, head block)
-    int32_t head_blocks;      // ceil(H / 64)
+    int32_t head_blocks;      // ceil(H / heads per block of the kernel)
     int32_t n_items;          // T * head_blocks * splits work items
     int32_t ext_pages;        // extra page-table width (0 when R == 0)
     uint16_t* out;            // bf16 [T, H, 512]
@@ -48,7 +54,7 @@ struct GatherArgs {
     int32_t* counts;  // [T, 2]
 };
 
-hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& g, hipStream_t stream);
 

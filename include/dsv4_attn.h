@@ -168,14 +168,24 @@ void dsv4_attn_workspace_release(void);
 dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
 
 /*
- * Plan that dsv4_attn_forward would use for these sizes: number of splits
- * per row and keys per split.  kv_fp8 is nonzero for packed FP8 pools (the
- * two formats run different kernels and are planned differently).
- * Host-only, no device access.
+ * Tuning / test hook: force the bf16 kernel variant by its query heads per
+ * workgroup (32: two teams of waves on alternate tiles; 64: one tile per
+ * step), or 0 for the automatic choice.  Packed FP8 pools always use 64.
+ * Process-wide.
+ */
+dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads);
+
+/*
+ * Plan that dsv4_attn_forward would use for these sizes: number of key
+ * splits per (row, head block), keys per split, and query heads per
+ * workgroup (32 or 64; the kernel variant).  kv_fp8 is nonzero for packed
+ * FP8 pools (the two formats run different kernels and are planned
+ * differently).  heads_per_workgroup may be NULL.  Host-only, no device
+ * access.
  */
 dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
                            int32_t c4_width, int32_t extra_pages, int32_t kv_fp8, int32_t* splits,
-                           int32_t* keys_per_split);
+                           int32_t* keys_per_split, int32_t* heads_per_workgroup);
 
 /*
  * Kernel timing on the caller's stream with HIP events.  While enabled, every

@@ -153,15 +153,27 @@ def test_plan_is_host_only_and_sane():
     L = N.load()
     s = ctypes.c_int32()
     c = ctypes.c_int32()
-    assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c)) == 0
+    assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), None) == 0
     assert c.value % 32 == 0 and s.value * c.value >= 128 + 1024
     for fp8 in (0, 1):
-        assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, fp8, ctypes.byref(s), ctypes.byref(c)) == 0
+        assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, fp8, ctypes.byref(s), ctypes.byref(c), None) == 0
         assert s.value * c.value >= 640 and (s.value - 1) * c.value < 640
         assert c.value >= (32 if fp8 else 128)
-    assert L.dsv4_attn_plan(32, 64, 7, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c)) == UNSUPPORTED
+    assert L.dsv4_attn_plan(32, 64, 7, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), None) == UNSUPPORTED
     assert L.dsv4_attn_set_split_keys(33) == INVALID
     assert L.dsv4_attn_set_split_keys(64) == 0
-    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c)) == 0
+    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), None) == 0
     assert c.value == 64 and s.value == 10
     assert L.dsv4_attn_set_split_keys(0) == 0
+    h = ctypes.c_int32()
+    # 32 rows of 64 heads fill a quarter of the chip at most: team kernel (32 heads per workgroup)
+    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
+    assert h.value in (32, 64)
+    assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
+    assert h.value == 64  # packed FP8 always runs 64-head blocks
+    for forced in (32, 64):
+        assert L.dsv4_attn_set_heads_per_workgroup(forced) == 0
+        assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
+        assert h.value == forced
+    assert L.dsv4_attn_set_heads_per_workgroup(48) == INVALID
+    assert L.dsv4_attn_set_heads_per_workgroup(0) == 0

@@ -123,6 +123,41 @@ def test_forward_small(orc, i):
     G.compare(out, lse, ro, rl, what=SMALL_IDS[i])
 
 
+@pytest.fixture
+def heads_per_workgroup(request):
+    """Force one bf16 kernel variant for the test, then restore the automatic choice."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_heads_per_workgroup
+
+    dsv4_attn_set_heads_per_workgroup(request.param)
+    yield request.param
+    dsv4_attn_set_heads_per_workgroup(0)
+
+
+@pytest.mark.parametrize("heads_per_workgroup", [32, 64], indirect=True)
+@pytest.mark.parametrize("i", [0, 3, 5, 8, 11, 12, 14, 15, 16], ids=[SMALL_IDS[i] for i in [0, 3, 5, 8, 11, 12, 14, 15, 16]])
+def test_forward_small_each_bf16_kernel(orc, i, heads_per_workgroup):
+    case = small_case(i)
+    log(f"forward small {SMALL_IDS[i]} heads/workgroup={heads_per_workgroup}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"{SMALL_IDS[i]}-hpw{heads_per_workgroup}")
+
+
+@pytest.mark.parametrize("heads_per_workgroup", [32, 64], indirect=True)
+@pytest.mark.parametrize("keys", [32, 96, 160])
+def test_forced_split_sizes_each_bf16_kernel(orc, keys, heads_per_workgroup):
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
+
+    case = make_case(seq_lens=[3000, 700, 5], n_q=[2, 3, 1], H=100, R=4, seed=31, pad_mode="scatter")
+    ro, rl, _ = orc.attention(case)
+    dsv4_attn_set_split_keys(keys)
+    try:
+        out, lse = G.run_forward(case)
+    finally:
+        dsv4_attn_set_split_keys(0)
+    G.compare(out, lse, ro, rl, what=f"split{keys}-hpw{heads_per_workgroup}")
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_forward_random(orc, seed):
     rng = np.random.default_rng(seed)
