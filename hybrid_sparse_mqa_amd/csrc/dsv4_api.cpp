@@ -244,13 +244,21 @@ Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
     if (fp8) return Layout::kFp8;
     if (g_force_heads_per_workgroup == kTeamHeadsPerBlock) return Layout::kTeam;
     if (g_force_heads_per_workgroup == kWideHeadsPerBlock) return Layout::kWide;
+    if (g_force_heads_per_workgroup == kNarrowHeadsPerBlock) return Layout::kNarrow;
     const int64_t wide_rows = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
     const int64_t team_rows = (int64_t)T * ((H + kTeamHeadsPerBlock - 1) / kTeamHeadsPerBlock);
     if (wide_rows * 4 < cus || team_rows >= cus) return Layout::kTeam;
     return Layout::kWide;
 }
 
-int32_t heads_per_block(Layout layout) { return layout == Layout::kTeam ? kTeamHeadsPerBlock : kWideHeadsPerBlock; }
+int32_t heads_per_block(Layout layout) {
+    return layout == Layout::kTeam ? kTeamHeadsPerBlock
+                                   : (layout == Layout::kNarrow ? kNarrowHeadsPerBlock : kWideHeadsPerBlock);
+}
+
+// Keys per LDS tile and most keys per split of each split kernel.
+int32_t tile_keys(Layout layout) { return layout == Layout::kNarrow ? kNarrowTileKeys : kTileKeys; }
+int32_t max_split_keys(Layout layout) { return layout == Layout::kNarrow ? kNarrowMaxSplitKeys : kMaxSplitKeys; }
 
 // Keys per split: enough splits per row to fill the chip once, with at
 // least 64 keys per split for bf16 pools (32 for packed FP8, whose kernel
@@ -278,10 +286,11 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
             if (rows * w128 * 2 >= cus) want = w128;
         }
         c = (nmax + want - 1) / want;
-        const int64_t unit = layout == Layout::kTeam ? 2 * kTileKeys : kTileKeys;
+        const int64_t unit = layout == Layout::kTeam ? 2 * kTileKeys : tile_keys(layout);
         c = (c + unit - 1) / unit * unit;
     }
-    c = std::min<int64_t>(std::max<int64_t>(c, kTileKeys), kMaxSplitKeys);
+    c = (c + tile_keys(layout) - 1) / tile_keys(layout) * tile_keys(layout);
+    c = std::min<int64_t>(std::max<int64_t>(c, tile_keys(layout)), max_split_keys(layout));
     *chunk = (int32_t)c;
     *splits = (int32_t)std::max<int64_t>(1, (nmax + c - 1) / c);
 }
@@ -405,18 +414,18 @@ const char* dsv4_last_error(void) { return g_err.c_str(); }
 int32_t dsv4_abi_version(void) { return DSV4_ABI_VERSION; }
 
 dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
-    if (keys_per_split < 0 || keys_per_split % kTileKeys != 0 || keys_per_split > kMaxSplitKeys)
-        return fail(DSV4_ERR_INVALID, "keys_per_split must be 0 or a multiple of %d up to %d", kTileKeys,
-                    kMaxSplitKeys);
+    if (keys_per_split < 0 || keys_per_split % kNarrowTileKeys != 0 || keys_per_split > kNarrowMaxSplitKeys)
+        return fail(DSV4_ERR_INVALID, "keys_per_split must be 0 or a multiple of %d up to %d", kNarrowTileKeys,
+                    kNarrowMaxSplitKeys);
     std::lock_guard<std::mutex> lk(g_mu);
     g_force_split_keys = keys_per_split;
     return DSV4_OK;
 }
 
 dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads) {
-    if (heads != 0 && heads != kTeamHeadsPerBlock && heads != kWideHeadsPerBlock)
-        return fail(DSV4_ERR_INVALID, "heads per workgroup must be 0, %d or %d", kTeamHeadsPerBlock,
-                    kWideHeadsPerBlock);
+    if (heads != 0 && heads != kNarrowHeadsPerBlock && heads != kTeamHeadsPerBlock && heads != kWideHeadsPerBlock)
+        return fail(DSV4_ERR_INVALID, "heads per workgroup must be 0, %d, %d or %d", kNarrowHeadsPerBlock,
+                    kTeamHeadsPerBlock, kWideHeadsPerBlock);
     std::lock_guard<std::mutex> lk(g_mu);
     g_force_heads_per_workgroup = heads;
     return DSV4_OK;

@@ -140,6 +140,25 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_row) {
         : "memory");
 }
 
+// dma16 with a byte offset folded into the instruction (a 13-bit signed
+// immediate).  The instruction adds that offset to the LDS address as well
+// as to the global one, so M0 is set to the destination minus the offset.
+template <int OFF>
+__device__ __forceinline__ void dma16_off(const void* src, uint32_t lds_row) {
+    static_assert(OFF >= 0 && OFF < 4096, "global offset is 13-bit signed");
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_row - OFF);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off offset:%3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base), "n"(OFF)
+        : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
@@ -163,15 +182,13 @@ __device__ __forceinline__ bool decode_item(const AttnArgs& a, Item& it) {
 }
 
 // Q^T as the B operand of S^T: lane holds head (l & 31) of the wave's half,
-// dims 256*dh + 16*j + 8*(l >> 5) .. +8 for k-step j (zeros past H).
-__device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, bool head_ok, int dh, int l,
-                                       bf16x8 (&qf)[16]) {
-    const uint16_t* qrow = a.q + (int64_t)t * a.q_s0 + (int64_t)(head_ok ? head : 0) * a.q_s1 + dh * 256 + 8 * (l >> 5);
+// dims 256*dh + 16*j + 8*(l >> 5) .. +8 for k-step j.  Heads past H read head
+// H-1 (unconditional loads, no branch around them); their scores and outputs
+// are never written.
+__device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, int dh, int l, bf16x8 (&qf)[16]) {
+    const uint16_t* qrow = a.q + (int64_t)t * a.q_s0 + (int64_t)min(head, a.H - 1) * a.q_s1 + dh * 256 + 8 * (l >> 5);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        u32x4 v = head_ok ? *(const u32x4*)(qrow + 16 * j) : u32x4{0u, 0u, 0u, 0u};
-        qf[j] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int j = 0; j < 16; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
 }
 
 // Slot list of keys [k0, k0 + n_here) of row t into s_slot.  One round of
@@ -180,9 +197,10 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, bool 
 // range so that no load sits under a per-lane branch and all of them are in
 // flight together.  Compressed slots then resolve through the LDS table (or,
 // for a table longer than kTableCap pages, through one more round of loads).
+template <int kMaxKeys = kMaxSplitKeys>
 __device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk, int t, int k0, int n_here,
                                             int32_t* s_slot, int32_t* s_table, int tid) {
-    constexpr int kU = kMaxSplitKeys / 256;
+    constexpr int kU = kMaxKeys / 256;
     constexpr int kTU = kTableCap / 256;
     const bool cached_table = a.m.R != 0 && a.ext_pages <= kTableCap;
     const int32_t* ext_row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
@@ -284,6 +302,28 @@ __device__ __forceinline__ void scale_accumulators(f32x16 (&oacc)[NB], float alp
     for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
+            float x = oacc[mb][e];
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "s_nop 1\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(x), "=&v"(tmp)
+                : "v"(alpha));
+            oacc[mb][e] = x;
+        }
+    asm volatile("s_nop 4");
+}
+
+// The same for 16x16 accumulator tiles (four registers each).
+template <int NB>
+__device__ __forceinline__ void scale_accumulators(f32x4 (&oacc)[NB], float alpha) {
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3");
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
             float x = oacc[mb][e];
             float tmp;
             asm volatile(
@@ -475,148 +515,263 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
 // bf16 KV, wide layout: one workgroup per (row, block of 64 heads, key
 // split); wave w = 2*hh + dh owns heads [32*hh, 32*hh + 32) and head dims
 // [256*dh, 256*dh + 256) of every tile.  Key rows stream from HBM into a
-// 4-stage LDS ring with direct global->LDS loads (no VGPR staging), three
-// tiles in flight.
+// 4-stage LDS ring with direct global->LDS loads (no VGPR staging).
+//
+// Tile layout in LDS (32 KiB per stage).  Rows 8g .. 8g+7 form group g; the
+// 512 bytes of dim half dh of those rows form four 1 KiB blocks m (128-byte
+// line m of each row), at byte g*8192 + dh*4096 + m*1024.  Inside block
+// (g, dh, m), 16-byte position p holds the chunk (k-step j = 4m + (p >> 4),
+// half hi = (p & 1) ^ (g & 1)) of row 8g + ((p >> 1) & 7), i.e. dims
+// 16j + 8hi .. +8 of the dim half.  With this placement
+//   * wave w copies rows 8w .. 8w+7, each copy instruction moving 8 whole
+//     128-byte lines;
+//   * the score operand of k-step j (lane: key l & 31, half l >> 5) sits at
+//     a per-lane base + 256*j, conflict-free over every 16 lanes;
+//   * the transposing PV reads sit at a per-lane base + 16384*pp + 512*mb,
+//     conflict-free over every 16 lanes;
+// so no LDS address arithmetic is left in the loop.
+//
+// The loop is software-pipelined with one barrier per tile: iteration i
+// publishes the S partial of tile i, and after the barrier runs the PV
+// product of tile i-1 and the score MFMAs of tile i+1 while tile i's softmax
+// proceeds on the vector ALUs.  The S partials go through two exchange
+// buffers used alternately (a buffer is rewritten only two barriers after
+// it was read).  Tile i+3 is requested right after the barrier of iteration
+// i, into the stage tile i-1 held, so two tiles are always in flight.  Q is
+// loaded straight into registers, after the first metadata loads are issued
+// so that its latency overlaps the metadata round trips.
+//
+// LDS: ring 4 x 32 KiB + exchange 2 x 16 KiB = 160 KiB; the prologue's slot
+// list, per-tile key masks and page-table cache live in the exchange
+// buffers until the loop starts.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
-    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
-    __shared__ int32_t s_slot[kMaxSplitKeys];
-    __shared__ int32_t s_table[kTableCap];
-    __shared__ __attribute__((aligned(16))) uint64_t s_addr[kMaxSplitKeys];
+    __shared__ __attribute__((aligned(16))) float s_x[2][4 * 64 * 16];
+    int32_t* s_slot = (int32_t*)&s_x[0][0];                // kMaxSplitKeys entries, prologue only
+    uint32_t* s_mask = (uint32_t*)&s_x[0][kMaxSplitKeys];  // one 32-key mask per tile, prologue only
+    int32_t* s_table = (int32_t*)&s_x[1][0];               // kTableCap entries, prologue only
+    static_assert(kMaxSplitKeys + kMaxSplitKeys / kTileKeys <= 4 * 64 * 16, "prologue scratch fits buffer 0");
+    static_assert(kTableCap <= 4 * 64 * 16, "page-table cache fits buffer 1");
 
     Item it;
     if (!decode_item(a, it)) return;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int hh = w >> 1, dh = w & 1;
 
-    const RowKeys rk = row_keys(a.m, it.t, l);
+    // Metadata round 1 (request bounds), then Q (independent of it), then
+    // the rest of the row resolution.
+    const RequestChunk rc = load_requests(a.m, 0, l);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 qf[16];
+    {
+        const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
+        load_q(a, it.t, my_head, dh, l, qf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
     const int k0 = it.s * a.chunk;
-    const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
+    const int n_here = __builtin_amdgcn_readfirstlane(max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0));
+    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
     build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
-    build_row_addresses(a, rk, k0, n_here, s_slot, s_addr, tid);
-    const uint64_t zero_row = (uint64_t)(uintptr_t)a.zero_row;
 
-    // Wave w fetches tile keys 8w .. 8w+7; lane l moves 16 bytes of a row.
-    // Lane l reads logical chunk l ^ row_swz(k) so that the row lands in the
-    // swizzled layout of krow_offset.  Unused keys read the zero row.
-    // Wave w copies tile keys 8w .. 8w+7: their row addresses come from LDS
-    // (four 16-byte broadcast reads) and lane l moves logical chunk
-    // l ^ row_swz(k) so that each row lands in the swizzled layout.
-    auto fetch_tile = [&](int tile) {
-        uint8_t* dst = &s_tile[tile % kStages][0];
-        const u64x2* ap = (const u64x2*)&s_addr[tile * kTileKeys + 8 * w];
-        const u64x2 a01 = ap[0], a23 = ap[1], a45 = ap[2], a67 = ap[3];
-        const uint64_t rows[8] = {a01[0], a01[1], a23[0], a23[1], a45[0], a45[1], a67[0], a67[1]};
+    // Row addresses of the keys this wave copies: tile j, row 8w + e sits in
+    // lane (8j + e) & 63 of ad[(8j + e) >> 6]; unused keys read the zero row.
+    uint64_t ad[kMaxSplitKeys / 256];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            dma16((const uint8_t*)(uintptr_t)rows[e] + 16 * (l ^ row_swz(8 * w + e)), lds_addr(dst + (8 * w + e) * 1024));
+    for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
+        const int idx = 64 * u + l;
+        const int key = kTileKeys * (idx >> 3) + 8 * w + (idx & 7);
+        const int32_t slot = key < n_here ? s_slot[key] : -1;
+        const bool swa = k0 + key < rk.n_swa;
+        ad[u] = slot >= 0 ? (uint64_t)(uintptr_t)((swa ? a.swa_pool : a.ext_pool) +
+                                                  (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes))
+                          : (uint64_t)(uintptr_t)a.zero_row;
+    }
+
+    // Copy of one tile: lane p moves 16-byte chunks of row 8w + ((p >> 1) & 7),
+    // at chunk 2*(p >> 4) + ((p & 1) ^ (w & 1)) of each 128-byte line.
+    const int dma_row = (l >> 1) & 7;
+    const uint32_t dma_lane_off = 16u * (2u * (l >> 4) + ((l & 1) ^ (w & 1)));
+    auto fetch_tile = [&](int tile) {
+        const int u = tile >> 3;
+        const uint64_t au = u == 0 ? ad[0] : (u == 1 ? ad[1] : (u == 2 ? ad[2] : ad[3]));
+        const int src = 4 * (8 * (tile & 7) + dma_row);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
+        const uint8_t* row = (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo) + dma_lane_off;
+        const uint32_t dst = lds_addr(&s_tile[tile % kStages][0]) + w * 8192;
+        dma16_off<0>(row, dst);
+        dma16_off<128>(row, dst + 1024);
+        dma16_off<256>(row, dst + 2048);
+        dma16_off<384>(row, dst + 3072);
+        dma16_off<512>(row, dst + 4096);
+        dma16_off<640>(row, dst + 5120);
+        dma16_off<768>(row, dst + 6144);
+        dma16_off<896>(row, dst + 7168);
+    };
+
+    // Per-lane LDS bases of the score operand and of the two transposing PV
+    // reads (rows r0 = 16pp + 4hq + kq and r0 + 8); see the layout above.
+    const int kk = l & 31, khi = l >> 5, kg = kk >> 3;
+    const uint32_t s_base = kg * 8192 + dh * 4096 + 32 * (kk & 7) + 16 * (khi ^ (kg & 1));
+    const int a4 = l & 3, kq = (l >> 2) & 3, half = (l >> 4) & 1, hq = l >> 5;
+    const uint32_t t_base0 = dh * 4096 + 256 * half + 128 * hq + 32 * kq + 8 * a4;
+    const uint32_t t_base1 = t_base0 + 8192 + 16 - 32 * (a4 >> 1);
+    const uint32_t ring = lds_addr(&s_tile[0][0]);
+
+    auto read_k = [&](int tile, bf16x8 (&av)[16]) {
+        const lds_void* base = (const lds_void*)(uintptr_t)(ring + (tile % kStages) * (kTileKeys * 1024) + s_base);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) av[j] = *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)base + 256 * j);
+    };
+    // K^T operand of PV: lane L takes dim 32*mb + (L & 31) of its dim half and
+    // keys G(pp, L >> 5) from two transposing reads (rows r0 and r0 + 8).
+    auto read_kt = [&](int tile, bf16x8 (&kt)[16]) {
+        const uint32_t st = ring + (tile % kStages) * (kTileKeys * 1024);
+        const __attribute__((address_space(3))) uint8_t* b0 = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_base0);
+        const __attribute__((address_space(3))) uint8_t* b1 = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_base1);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b0 + 16384 * pp + 512 * mb));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b1 + 16384 * pp + 512 * mb));
+                kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
     };
 
     f32x16 oacc[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
-    const float no_scale[16] = {};
+    // PV operands of the previous tile, consumed one iteration later (zero
+    // before the first tile, so the first PV step adds nothing).
+    bf16x8 kt[16], pb[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kt[j] = bf16x8{};
+    pb[0] = bf16x8{};
+    pb[1] = bf16x8{};
 
-    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
-    // Retire every compiler-visible load (slot metadata) first, so the only
+    // Every compiler-visible load (metadata, Q) is retired here, so the only
     // vector-memory operations in flight below are this wave's copies into
-    // LDS (16 for Q, then 8 per tile) and the explicit vmcnt waits count
-    // exactly those.
+    // LDS (8 per tile) and the explicit vmcnt waits count exactly those.
     wait_vmcnt<0>();
-    // Q travels the same way as the keys: the block's 64 head rows (zero rows
-    // past H) are copied into ring stages 2-3, in the swizzled row layout,
-    // ahead of tiles 0 and 1, so Q and the first keys arrive together.  Once
-    // every wave holds its Q operands, stages 2-3 return to the ring.
-    bf16x8 qf[16];
+    if (n_tiles > 0) fetch_tile(0);
+    if (n_tiles > 1) fetch_tile(1);
+    if (n_tiles > 2) fetch_tile(2);
+    // Valid-key mask of every tile (built while the first tiles are in flight).
+    for (int j = w; j < n_tiles; j += 4) {
+        const int key = kTileKeys * j + (l & 31);
+        const uint64_t b = __ballot(l < 32 && key < n_here && s_slot[key] >= 0);
+        if (l == 0) s_mask[j] = (uint32_t)b;
+    }
+    __syncthreads();
+    const uint32_t tile_mask = s_mask[l & 31];  // lane j: valid keys of tile j
+    f32x16 sacc = f32x16{};
     if (n_tiles > 0) {
-        uint8_t* qs = &s_tile[2][0];
+        if (n_tiles > 2) wait_vmcnt<16>();
+        else if (n_tiles > 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // tile 0 is in LDS for every wave; the prologue scratch is dead
+        bf16x8 av[16];
+        read_k(0, av);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int k = 16 * w + e;
-            const int head = it.hb * kWideHeadsPerBlock + k;
-            const uint8_t* src = head < a.H ? (const uint8_t*)(a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1)
-                                            : a.zero_row;
-            dma16(src + 16 * (l ^ row_swz(k)), lds_addr(qs + k * 1024));
-        }
-        fetch_tile(0);
-        if (n_tiles > 1) {
-            fetch_tile(1);
-            wait_vmcnt<8>();  // Q and tile 0
-        } else {
-            wait_vmcnt<0>();
-        }
-        __syncthreads();
-        const int qrow = hh * 32 + (l & 31);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) qf[j] = *(const bf16x8*)(qs + krow_offset(qrow, dh * 32 + 2 * j + (l >> 5)));
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __syncthreads();  // every wave has its Q: stages 2-3 are free
-        if (n_tiles > 2) fetch_tile(2);
+        for (int j = 0; j < 16; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
     }
 
+    const float sl2 = a.scale_log2;
+    const int key_shift = 4 * khi;  // register r of a score tile: key 8*(r >> 2) + 4*(l >> 5) + (r & 3)
     for (int i = 0; i < n_tiles; ++i) {
-        // Tiles i+1 and i+2 may still be in flight; wait for this wave's rows of tile i.
-        const int newer = min(kStages - 2, n_tiles - 1 - i);
-        if (newer >= 2) wait_vmcnt<16>();
-        else if (newer == 1) wait_vmcnt<8>();
+        // This wave's rows of tile i+1 (tile i+2 may still be in flight).
+        if (i + 2 < n_tiles) wait_vmcnt<8>();
         else wait_vmcnt<0>();
-        const uint64_t vmask = __ballot(l < 32 && s_addr[i * kTileKeys + (l & 31)] != zero_row);
-        __syncthreads();  // tile i is in LDS for every wave; stage (i-1) % kStages is free
-
-        const uint8_t* tile = &s_tile[i % kStages][0];
-        // S^T partial over this wave's 256 dims (operands read ahead of the MFMAs).
-        f32x16 sacc = f32x16{};
+        float* xb = &s_x[i & 1][0];
         {
-            const int k = l & 31;
-            bf16x8 av[16];
+            f32x4* mine = (f32x4*)xb + w * 256 + l;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) av[j] = *(const bf16x8*)(tile + krow_offset(k, dh * 32 + 2 * j + (l >> 5)));
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
+            for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
         }
-        if (i + kStages - 1 < n_tiles) fetch_tile(i + kStages - 1);
-        exchange_partial(s_sx, w, l, sacc);
+        __syncthreads();  // S partials of tile i published; tile i+1 landed; tile i-1's stage is free
+        if (i + 3 < n_tiles) fetch_tile(i + 3);
 
-        // O^T[d, heads] += K^T[d, keys] P^T[keys, heads].  The K^T operand of
-        // lane L (dim 32*mb + (L & 31), keys G(pp, L >> 5)) comes from two
-        // transposing reads: source lane S of each 16-lane block points at key
-        // row r_k (k = (S >> 2) & 3) and dims d0 .. d0+3, d0 = 16*((S >> 4) & 1)
-        // + 4*(S & 3); the block returns dim d0 + j of rows r_0..r_3 to lane
-        // 4*(S & 3) + j.  These reads do not depend on P: they are issued
-        // before the softmax and land while it runs (the schedule barriers
-        // keep the compiler from sinking them past it).
-        bf16x8 kt[16];
+        // The partner's S partial of tile i and the score operand of tile
+        // i+1 (when tile i is the last, that stage holds stale rows whose
+        // scores are discarded).
+        f32x4 other[4];
         {
-            const int a4 = l & 3, kq = (l >> 2) & 3, hq = l >> 5, half = (l >> 4) & 1;
-            __builtin_amdgcn_sched_barrier(0);
+            const f32x4* op = (const f32x4*)xb + (w ^ 1) * 256 + l;
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                const int d0 = dh * 256 + 32 * mb + 16 * half + 4 * a4;
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const int r0 = 16 * pp + 4 * hq + kq;
-                    const int r1 = r0 + 8;
-                    const uint8_t* p0 = tile + krow_offset(r0, d0 >> 3) + 2 * (d0 & 7);
-                    const uint8_t* p1 = tile + krow_offset(r1, d0 >> 3) + 2 * (d0 & 7);
-                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
-                    kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int q = 0; q < 4; ++q) other[q] = op[64 * q];
         }
-
-        bf16x8 pb[2], pbs[2];
-        softmax_tile<false>(sacc, vmask, a.scale_log2, l, no_scale, m_run, l_run, oacc, pb, pbs);
+        bf16x8 av[16];
+        read_k(i + 1, av);
+        // PV of tile i-1 while those reads land; then the PV operand of tile i.
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
                 oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
+        read_kt(i, kt);
+
+        // Softmax of tile i (base 2, raw scores; the scale is applied in the
+        // exponent), interleaved with the score MFMAs of tile i+1.  Register r
+        // holds head (l & 31), key 8*(r >> 2) + 4*(l >> 5) + (r & 3); lanes l and
+        // l ^ 32 hold the two halves of a head's keys.  The running reference
+        // m_run (scaled units) moves only when a score exceeds it by more than
+        // 2^8 (probabilities stay <= 256), so the accumulators are rescaled on
+        // few tiles; l_run is this lane's share of the denominator, the two
+        // shares are added in write_result.
+        f32x16 snext = f32x16{};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
+        float sv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = sacc[r] + other[r >> 2][r & 3];
+        const uint32_t tmask = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i);
+        if (tmask != 0xFFFFFFFFu) {
+            const uint32_t mine = tmask >> key_shift;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = ((mine >> (8 * (r >> 2) + (r & 3))) & 1u) ? sv[r] : -INFINITY;
+        }
+        float smax = sv[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) smax = fmaxf(smax, sv[r]);
+        const float tmax = smax * sl2;  // scale > 0: the maximum commutes with it
+        if (__any(tmax > m_run + kRescaleLog2)) {
+            const float hmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the head's tile maximum
+            const bool grow = hmax > m_run + kRescaleLog2;
+            const float m_target = grow ? hmax : m_run;
+            const float alpha = fast_exp2(m_run - m_target);  // 0 while nothing was accumulated
+            if (__any(grow && m_run != -INFINITY)) scale_accumulators(oacc, alpha);
+            l_run *= alpha;
+            m_run = m_target;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(fmaf(sv[r], sl2, neg_m));
+            psum += pr;
+            pb[r >> 3][r & 7] = (__bf16)pr;
+        }
+        l_run += psum;
+#pragma unroll
+        for (int j = 8; j < 16; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then VALU
+        }
+        sacc = snext;
     }
+    // PV of the last tile.
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+            oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
     write_result(a, it, hh, dh, l, oacc, m_run, l_run, &s_tile[0][0], &s_tile[1][0]);
 }
 
@@ -840,6 +995,272 @@ __global__ __launch_bounds__(256, 1) void attn_team_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 KV, narrow layout: one workgroup per (row, block of 16 heads, key
+// split).  The four waves are independent: wave w takes the split's 16-key
+// tiles w, w+4, w+8, ... through a private two-stage LDS ring, keeps its own
+// online softmax and its own O^T for the 16 heads x 512 dims, and the four
+// states are merged once, in the epilogue.  The loop has no exchange and no
+// barrier: a wave waits only for its own copies.  Products on the 16x16 MFMAs:
+//     S^T[16 keys, 16 heads]  = K[keys, d] . Q^T[d, heads]      (16x16x32, 16 k-steps)
+//     O^T[16 dims, 16 heads] += K^T[dims, keys] . P^T[keys, heads]   (16x16x16, 32 dim blocks)
+// The score output (lane: head l & 15, keys 4*(l >> 4) + i) is already the
+// P^T operand layout, so P goes from the softmax straight into the PV MFMA.
+// The head blocks of one row are consecutive work items (same XCD) and read
+// the same key rows, which L2 then fetches from HBM once.
+//
+// Tile layout (16 KiB): 1 KiB block kk (the k-step of dims 32kk .. 32kk+31)
+// holds at 16-byte position p the chunk 4kk + (p >> 4) (dims 8*chunk .. +8)
+// of key row (p & 15) ^ (4*((p >> 4) & 1)).  The score operand of k-step kk
+// is then lane l's position (l & 48) | ((l & 15) ^ ((l & 16) >> 2)) of block
+// kk, and the transposing PV read of dim block db sits at a per-lane base +
+// 512*db; both are conflict-free over every 16 lanes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
+    constexpr int kTile = kNarrowTileKeys * 1024;  // 16 KiB
+    constexpr int kH = kNarrowHeadsPerBlock;
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ring[4][2][kTile];
+    __shared__ int32_t s_slot[kNarrowMaxSplitKeys];
+    __shared__ int32_t s_table[kTableCap];
+    __shared__ float s_ml[4][2][kH];
+
+    Item it;
+    if (!decode_item(a, it)) return;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int head0 = it.hb * kH;
+
+    // Metadata round 1 (request bounds), then Q (independent of it), then
+    // the rest of the row resolution.
+    const RequestChunk rc = load_requests(a.m, 0, l);
+    __builtin_amdgcn_sched_barrier(0);
+    // Q^T as the B operand of the score MFMA: lane holds head (l & 15), dims
+    // 32*kk + 8*(l >> 4) .. +8 of k-step kk.  Heads past H read head H-1;
+    // their results are never written.
+    bf16x8 qf[16];
+    {
+        const uint16_t* qrow =
+            a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(head0 + (l & 15), a.H - 1) * a.q_s1 + 8 * (l >> 4);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * kk));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
+    const int k0 = it.s * a.chunk;
+    const int n_here = __builtin_amdgcn_readfirstlane(max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0));
+    build_slots<kNarrowMaxSplitKeys>(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+    // Q and the metadata are retired here, so the only vector-memory
+    // operations in flight below are this wave's copies into LDS (16 per
+    // tile) and the explicit vmcnt waits count exactly those.
+    wait_vmcnt<0>();
+
+    const int n_tiles = (n_here + kNarrowTileKeys - 1) / kNarrowTileKeys;
+    const int n_mine = n_tiles > w ? (n_tiles - w + 3) / 4 : 0;  // tiles w, w+4, ...
+    const uint32_t ring_w = lds_addr(&s_ring[w][0][0]);
+
+    // Copy of this wave's n-th tile (tile w + 4n) into stage n & 1: lane p
+    // moves 16 bytes of row (p & 15) ^ (4*((p >> 4) & 1)) into position p of
+    // every block.  Returns the tile's valid-key mask (bit k: key k).
+    const int dma_row = (l & 15) ^ (4 * ((l >> 4) & 1));
+    auto fetch = [&](int n) -> uint32_t {
+        const int key = kNarrowTileKeys * (w + 4 * n) + dma_row;
+        const int32_t slot = key < n_here ? s_slot[key] : -1;
+        const bool swa = k0 + key < rk.n_swa;
+        const uint8_t* row = slot >= 0 ? (swa ? a.swa_pool : a.ext_pool) + (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes)
+                                       : a.zero_row;
+        const uint8_t* src = row + 16 * (l >> 4);
+        const uint32_t dst = ring_w + (n & 1) * kTile;
+        dma16_off<0>(src, dst);
+        dma16_off<64>(src, dst + 1024);
+        dma16_off<128>(src, dst + 2048);
+        dma16_off<192>(src, dst + 3072);
+        dma16_off<256>(src, dst + 4096);
+        dma16_off<320>(src, dst + 5120);
+        dma16_off<384>(src, dst + 6144);
+        dma16_off<448>(src, dst + 7168);
+        dma16_off<512>(src, dst + 8192);
+        dma16_off<576>(src, dst + 9216);
+        dma16_off<640>(src, dst + 10240);
+        dma16_off<704>(src, dst + 11264);
+        dma16_off<768>(src, dst + 12288);
+        dma16_off<832>(src, dst + 13312);
+        dma16_off<896>(src, dst + 14336);
+        dma16_off<960>(src, dst + 15360);
+        return (uint32_t)__ballot(slot >= 0) & 0xFFFFu;  // lanes 0..15 copy rows 0..15
+    };
+
+    // Per-lane LDS offsets of the score operand and of the transposing PV
+    // read.  PV source lane S = 4k + q of 16-lane block b points at row
+    // 4b + k, dims 16*db + 4q .. +3 (chunk 2db + (q >> 1), half q & 1), so
+    // result lane 4q + j of the block gets dim 4q + j of rows 4b .. 4b+3.
+    const uint32_t s_lane = 16u * ((l & 48) | ((l & 15) ^ ((l & 16) >> 2)));
+    const int tq = l & 3, trow = 4 * (l >> 4) + ((l >> 2) & 3), th1 = tq >> 1;
+    const uint32_t t_lane = 256u * th1 + 16u * (trow ^ (4 * th1)) + 8u * (tq & 1);
+
+    f32x4 oacc[32];
+#pragma unroll
+    for (int db = 0; db < 32; ++db) oacc[db] = f32x4{};
+    float m_run = -INFINITY, l_part = 0.f;
+    const float sl2 = a.scale_log2;
+    const int key_shift = 4 * (l >> 4);  // score register i: key 4*(l >> 4) + i
+
+    // Online softmax (base 2).  The running reference m_run (scaled units,
+    // per head) is set by the first tile and moves only when a score exceeds
+    // it by more than 2^20: probabilities up to 2^20 keep bf16's relative
+    // precision and stay far from overflow.  When a head that has already
+    // accumulated needs a larger reference, the wave restarts its tiles from
+    // the first with that reference (its accumulators are never rescaled, so
+    // they stay in place in the accumulation registers); the reference only
+    // grows, so restarts are bounded and, for attention scores, rare.
+    constexpr float kRefSlackLog2 = 20.0f;
+    uint32_t msk0 = 0, msk1 = 0;
+    if (n_mine > 0) msk0 = fetch(0);
+    if (n_mine > 1) msk1 = fetch(1);
+    for (int n = 0; n < n_mine; ++n) {
+        if (n + 1 < n_mine) wait_vmcnt<16>();  // tile n landed (tile n+1 may be in flight)
+        else wait_vmcnt<0>();
+        const uint32_t st = ring_w + (n & 1) * kTile;
+        const __attribute__((address_space(3))) uint8_t* sp = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + s_lane);
+        const __attribute__((address_space(3))) uint8_t* tp = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_lane);
+        // Operand reads in two waves so that at most 48 operand registers are
+        // live: the score operand and the first half of the PV operand, then
+        // (once the score MFMAs hold their operands) the second half.
+        bf16x8 av[16];
+        bf16x4 kt[32];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) av[kk] = *(const __attribute__((address_space(3))) bf16x8*)(sp + 1024 * kk);
+#pragma unroll
+        for (int db = 0; db < 16; ++db) kt[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 512 * db));
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 sacc = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], qf[kk], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 16; db < 32; ++db) kt[db] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tp + 512 * db));
+        const uint32_t msk = (n & 1) ? msk1 : msk0;
+        // Every read of this stage has returned: refill it with tile n+2.
+        if (n + 2 < n_mine) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const uint32_t nm = fetch(n + 2);
+            if (n & 1) msk1 = nm;
+            else msk0 = nm;
+        }
+
+        // This lane holds keys 4*(l >> 4) .. +3 of head l & 15; the other
+        // three quarters of the head's keys sit in lanes l ^ 16, l ^ 32, l ^ 48.
+        float sv[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+        if (msk != 0xFFFFu) {
+            const uint32_t mine = msk >> key_shift;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = ((mine >> i) & 1u) ? sv[i] : -INFINITY;
+        }
+        const float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) * sl2;
+        if (__any(tmax > m_run + kRefSlackLog2)) {
+            float hmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            hmax = fmaxf(hmax, __shfl_xor(hmax, 32));  // the head's tile maximum
+            const bool grow = hmax > m_run + kRefSlackLog2;
+            const bool restart = __any(grow && m_run != -INFINITY);
+            m_run = grow ? hmax : m_run;
+            if (restart) {
+                wait_vmcnt<0>();  // this wave's copies have landed; its stages are free
+#pragma unroll
+                for (int db = 0; db < 32; ++db) oacc[db] = f32x4{};
+                l_part = 0.f;
+                msk0 = fetch(0);
+                if (n_mine > 1) msk1 = fetch(1);
+                n = -1;
+                continue;
+            }
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        bf16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pr = fast_exp2(fmaf(sv[i], sl2, neg_m));
+            l_part += pr;
+            pb[i] = (__bf16)pr;
+        }
+#pragma unroll
+        for (int db = 0; db < 32; ++db) oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kt[db], pb, oacc[db], 0, 0, 0);
+    }
+
+    // Epilogue: merge the four waves' states per head.  M = max of the wave
+    // references (and the sink when the row is not split), Z = sum of
+    // l_w * 2^(m_w - M) (+ 2^(sink - M)); wave w stages O_w * 2^(m_w - M) / Z
+    // as fp32 rows [head][512] in ring quarter w (16-byte chunk c of row h at
+    // chunk c ^ h), and wave w then sums the four quarters for heads
+    // 4w .. 4w+3 and writes the output (or the normalised partial and its
+    // base-2 log-sum-exp for the merge kernel).
+    float lh = l_part + __shfl_xor(l_part, 16);
+    lh += __shfl_xor(lh, 32);
+    __syncthreads();  // every wave is done with the ring
+    if (l < kH) {
+        s_ml[w][0][l] = lh > 0.f ? m_run : -INFINITY;
+        s_ml[w][1][l] = lh;
+    }
+    __syncthreads();
+    const int hd = l & 15;
+    const int my_head = head0 + hd;
+    float M = (a.splits == 1 && a.sink != nullptr && my_head < a.H) ? a.sink[my_head] * kLog2e : -INFINITY;
+    const float sig = M;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, s_ml[v][0][hd]);
+    float Z = 0.f, f_own = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float mv = s_ml[v][0][hd];
+            Z += mv == -INFINITY ? 0.f : s_ml[v][1][hd] * fast_exp2(mv - M);
+        }
+        if (sig != -INFINITY) Z += fast_exp2(sig - M);
+        const float mw = s_ml[w][0][hd];
+        f_own = (mw == -INFINITY || Z <= 0.f) ? 0.f : fast_exp2(mw - M) / Z;
+    }
+    const float lse2 = Z > 0.f ? M + fast_log2(Z) : -INFINITY;
+    {
+        uint8_t* q = &s_ring[0][0][0] + w * 32768 + hd * 2048;
+#pragma unroll
+        for (int db = 0; db < 32; ++db) {
+            const int c = 4 * db + (l >> 4);
+            const f32x4& o = oacc[db];
+            *(f32x4*)(q + 16 * (c ^ hd)) = f32x4{o[0] * f_own, o[1] * f_own, o[2] * f_own, o[3] * f_own};
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h2 = 4 * w + e;
+        const int head = head0 + h2;
+        if (head >= a.H) break;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint8_t* q = &s_ring[0][0][0] + v * 32768 + h2 * 2048;
+            const f32x4 x0 = *(const f32x4*)(q + 16 * ((2 * l) ^ h2));
+            const f32x4 x1 = *(const f32x4*)(q + 16 * ((2 * l + 1) ^ h2));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] += x0[i];
+                acc[4 + i] += x1[i];
+            }
+        }
+        const u32x4 ov = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                          pack_bf16x2(acc[6], acc[7])};
+        const float lse_h = __shfl(lse2, h2);
+        if (a.splits == 1) {
+            uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
+            *(u32x2*)orow = u32x2{ov[0], ov[1]};  // out rows need only 8-byte alignment
+            *(u32x2*)(orow + 4) = u32x2{ov[2], ov[3]};
+            if (a.lse != nullptr && l == 0) a.lse[(int64_t)it.t * a.lse_s0 + head] = lse_h * kLn2;
+        } else {
+            const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + head;
+            *(u32x4*)(a.ws_o + part * kHeadDim + 8 * l) = ov;
+            if (l == 0) a.ws_lse[part] = lse_h;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Packed FP8 KV: rows staged through registers (one tile ahead), decoded, and
 // written to LDS row-major and as 8-key columns.  E4M3 codes are exact in
 // bf16; the per-token scale multiplies the fp32 non-rotary score partial and
@@ -862,7 +1283,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     const bool head_ok = my_head < a.H;
 
     bf16x8 qf[16];
-    load_q(a, it.t, my_head, head_ok, dh, l, qf);
+    load_q(a, it.t, my_head, dh, l, qf);
 
     const RowKeys rk = row_keys(a.m, it.t, l);
     const int k0 = it.s * a.chunk;
@@ -1083,6 +1504,9 @@ hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream
             break;
         case Layout::kWide:
             hipLaunchKernelGGL(attn_wide_kernel, grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kNarrow:
+            hipLaunchKernelGGL(attn_narrow_kernel, grid, dim3(256), 0, stream, a);
             break;
     }
     return hipGetLastError();

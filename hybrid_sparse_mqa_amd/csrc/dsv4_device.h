@@ -53,28 +53,47 @@ struct RowKeys {
     int n_ext;   // extra list length (C4: K entries including unused ones)
 };
 
+// Bounds and length of 64 consecutive requests, one per lane.
+struct RequestChunk {
+    int lo, hi, len;
+};
+
+// Lanes past B load request B-1 (every load is unconditional, so no branch
+// splits them and a later wait counts them exactly); callers mask those
+// lanes out.
+__device__ __forceinline__ RequestChunk load_requests(const Meta& m, int base, int lane) {
+    const int i = min(base + lane, m.B - 1);
+    RequestChunk c;
+    c.lo = m.qo_indptr[i];
+    c.hi = m.qo_indptr[i + 1];
+    c.len = m.seq_lens[i];
+    return c;
+}
+
 // Row resolution by one wave.  Lane i of each 64-request chunk loads
 // qo_indptr[i], qo_indptr[i+1] and seq_lens[i] together; the owning request
 // is the last i with qo_indptr[i] <= t (a ballot), and its values are read
-// from that lane, so the whole lookup costs one round of loads.  `lane` is
-// the caller's lane id; the result is clamped to the batch.
-__device__ __forceinline__ RowKeys row_keys(const Meta& m, int t, int lane) {
+// from that lane, so the whole lookup costs one round of loads per chunk.
+// `first` is the chunk of requests 0..63, loaded by the caller (which may
+// issue other loads before using it); `lane` is the caller's lane id; the
+// result is clamped to the batch.
+__device__ __forceinline__ RowKeys row_keys_from(const Meta& m, int t, int lane, RequestChunk c) {
     int r = 0, q_lo = 0, q_hi = 0, len = 0;
-    for (int base = 0; base < m.B; base += 64) {
-        const int i = base + lane;
-        const bool in = i < m.B;
-        const int lo = in ? m.qo_indptr[i] : 0;
-        const int hi = in ? m.qo_indptr[i + 1] : 0;
-        const int sl = in ? m.seq_lens[i] : 0;
-        const uint64_t le = __ballot(in && lo <= t);
+    auto scan = [&](int base, const RequestChunk& cc) {
+        const bool in = base + lane < m.B;
+        const uint64_t le = __ballot(in && cc.lo <= t);
         if (le != 0ull) {
             const int src = 63 - __clzll(le);
             r = base + src;
-            q_lo = __shfl(lo, src);
-            q_hi = __shfl(hi, src);
-            len = __shfl(sl, src);
+            q_lo = __shfl(cc.lo, src);
+            q_hi = __shfl(cc.hi, src);
+            len = __shfl(cc.len, src);
         }
-    }
+    };
+    // The first chunk outside any loop, so that waiting for it does not
+    // wait for loads the caller issued after it.
+    scan(0, c);
+    for (int base = 64; base < m.B; base += 64) scan(base, load_requests(m, base, lane));
     RowKeys k;
     k.r = r;
     const int n_q = q_hi - q_lo;
@@ -83,6 +102,10 @@ __device__ __forceinline__ RowKeys row_keys(const Meta& m, int t, int lane) {
     k.swa_lo = k.p + 1 - k.n_swa;
     k.n_ext = m.R == 4 ? m.K : (m.R == 128 ? (k.p + 1) / 128 : 0);
     return k;
+}
+
+__device__ __forceinline__ RowKeys row_keys(const Meta& m, int t, int lane) {
+    return row_keys_from(m, t, lane, load_requests(m, 0, lane));
 }
 
 // Physical slot of entry i of row t's key list; -1 for an unused C4 entry.

@@ -163,22 +163,25 @@ void dsv4_attn_workspace_release(void);
 
 /*
  * Tuning / test hook: force the number of keys handled by one split
- * (a positive multiple of 32), or 0 for the automatic plan.  Process-wide.
+ * (a positive multiple of 16 up to 2048), or 0 for the automatic plan.  The
+ * kernel that runs rounds it up to its own tile (32 keys for the 32- and
+ * 64-head variants and FP8, 16 for the 16-head variant) and caps it at its
+ * own limit (1024 keys; 2048 for the 16-head variant).  Process-wide.
  */
 dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
 
 /*
  * Tuning / test hook: force the bf16 kernel variant by its query heads per
- * workgroup (32: two teams of waves on alternate tiles; 64: one tile per
- * step), or 0 for the automatic choice.  Packed FP8 pools always use 64.
- * Process-wide.
+ * workgroup (16: four independent waves on alternate 16-key tiles; 32: two
+ * teams of waves on alternate tiles; 64: one tile per step), or 0 for the
+ * automatic choice.  Packed FP8 pools always use 64.  Process-wide.
  */
 dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads);
 
 /*
  * Plan that dsv4_attn_forward would use for these sizes: number of key
  * splits per (row, head block), keys per split, and query heads per
- * workgroup (32 or 64; the kernel variant).  kv_fp8 is nonzero for packed
+ * workgroup (16, 32 or 64; the kernel variant).  kv_fp8 is nonzero for packed
  * FP8 pools (the two formats run different kernels and are planned
  * differently).  heads_per_workgroup may be NULL.  Host-only, no device
  * access.

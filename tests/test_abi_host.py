@@ -161,6 +161,7 @@ def test_plan_is_host_only_and_sane():
         assert c.value >= (32 if fp8 else 128)
     assert L.dsv4_attn_plan(32, 64, 7, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), None) == UNSUPPORTED
     assert L.dsv4_attn_set_split_keys(33) == INVALID
+    assert L.dsv4_attn_set_split_keys(2064) == INVALID
     assert L.dsv4_attn_set_split_keys(64) == 0
     assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), None) == 0
     assert c.value == 64 and s.value == 10
@@ -171,7 +172,7 @@ def test_plan_is_host_only_and_sane():
     assert h.value in (32, 64)
     assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
     assert h.value == 64  # packed FP8 always runs 64-head blocks
-    for forced in (32, 64):
+    for forced in (16, 32, 64):
         assert L.dsv4_attn_set_heads_per_workgroup(forced) == 0
         assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
         assert h.value == forced

@@ -133,7 +133,7 @@ def heads_per_workgroup(request):
     dsv4_attn_set_heads_per_workgroup(0)
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [32, 64], indirect=True)
+@pytest.mark.parametrize("heads_per_workgroup", [16, 32, 64], indirect=True)
 @pytest.mark.parametrize("i", [0, 3, 5, 8, 11, 12, 14, 15, 16], ids=[SMALL_IDS[i] for i in [0, 3, 5, 8, 11, 12, 14, 15, 16]])
 def test_forward_small_each_bf16_kernel(orc, i, heads_per_workgroup):
     case = small_case(i)
@@ -143,8 +143,8 @@ def test_forward_small_each_bf16_kernel(orc, i, heads_per_workgroup):
     G.compare(out, lse, ro, rl, what=f"{SMALL_IDS[i]}-hpw{heads_per_workgroup}")
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [32, 64], indirect=True)
-@pytest.mark.parametrize("keys", [32, 96, 160])
+@pytest.mark.parametrize("heads_per_workgroup", [16, 32, 64], indirect=True)
+@pytest.mark.parametrize("keys", [16, 32, 48, 96, 160, 2048])
 def test_forced_split_sizes_each_bf16_kernel(orc, keys, heads_per_workgroup):
     from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
 
@@ -288,8 +288,9 @@ SPIKES = [
 ]
 
 
+@pytest.mark.parametrize("heads_per_workgroup", [0, 16], indirect=True)
 @pytest.mark.parametrize("name,R,sl,nq,where,visible", SPIKES, ids=[s[0] for s in SPIKES])
-def test_spikes(orc, name, R, sl, nq, where, visible):
+def test_spikes(orc, name, R, sl, nq, where, visible, heads_per_workgroup):
     case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=77, n_sel=300)
     t = 0  # first row of the request
     p = int(case.seq_lens[0]) - nq + 0
@@ -315,6 +316,30 @@ def test_spikes(orc, name, R, sl, nq, where, visible):
     G.compare(out, lse, ro, rl, what=name)
     dominated = rl[t, 0] > 50.0
     assert dominated == visible, (name, rl[t, 0])
+
+
+@pytest.mark.parametrize("heads_per_workgroup", [16, 64], indirect=True)
+@pytest.mark.parametrize("R", [0, 128])
+def test_growing_scores(orc, R, heads_per_workgroup):
+    """Key rows of row 0 blend, along its key list, from random towards
+    2 * q[0, head 0], so head 0's scores climb by about 65 (base 2) over the
+    pass: its running softmax reference falls far behind later keys several
+    times (for the 16-head kernel, a restart of the wave's tiles each time),
+    while the values stay near unit scale."""
+    case = make_case(seq_lens=[40000, 300], n_q=[1, 2], H=64, R=R, seed=53)
+    q0 = torch.from_numpy(case.q[0, 0].view(np.int16)).view(torch.bfloat16).float()
+    swa, ext = orc.gather(case, 0)
+    n = len(swa) + len(ext)
+    for pool_name, slots, base in (("swa_pool", swa, 0), ("extra_pool", ext, len(swa))):
+        pool = getattr(case, pool_name)
+        for i, slot in enumerate(slots):
+            beta = (base + i) / max(n - 1, 1)
+            row = torch.from_numpy(pool[slot].view(np.int16)).view(torch.bfloat16).float()
+            grown = ((1.0 - beta) * row + beta * 2.0 * q0).to(torch.bfloat16)
+            pool[slot] = grown.view(torch.int16).numpy().view(np.uint16)
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"growing-R{R}-hpw{heads_per_workgroup}")
 
 
 # --------------------------------------------------------------------------
