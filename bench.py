@@ -38,6 +38,13 @@ KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_mqa_amd", "csrc", f)
                   for f in ("dsv4_attn_kernels.hip", "dsv4_device.h", "dsv4_launch.h")]
 
 
+
+def split_kernel_name(kv: str, heads_per_workgroup: int) -> str:
+    """Name (as rocprofv3 prints it) of the split kernel that runs."""
+    if kv == "fp8":
+        return "attn_fp8_kernel"
+    return {16: "attn_narrow_kernel", 32: "attn_wide_kernel<1>", 64: "attn_wide_kernel<2>"}[heads_per_workgroup]
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -165,7 +172,7 @@ def record_traffic(config: int, split_keys: int, fetch_dir: str, write_dir: str,
     _, _, hpw = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
                                0 if case.extra_page_table is None else case.extra_page_table.shape[1],
                                kv_fp8=case.kv == "fp8")
-    name = "attn_fp8_kernel" if case.kv == "fp8" else "attn_team_kernel" if hpw == 32 else "attn_wide_kernel"
+    name = split_kernel_name(case.kv, hpw)
 
     def pick(d, key):
         hits = {k: v for k, v in d.items() if key in k}
@@ -343,8 +350,7 @@ def main() -> int:
     merge_avg_ms = merge_ms / calls
     kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
     achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
-    kernel_name = ("attn_fp8_kernel" if case.kv == "fp8" else
-                   "attn_team_kernel" if heads_per_wg == 32 else "attn_wide_kernel")
+    kernel_name = split_kernel_name(case.kv, heads_per_wg)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

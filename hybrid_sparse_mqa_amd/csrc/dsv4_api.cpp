@@ -222,38 +222,31 @@ dsv4_status ensure_zero_row(DeviceState* d) {
     return DSV4_OK;
 }
 
-// Keys per split: enough splits per row to fill the chip once, with at
-// least 64 keys per split for bf16 pools (32 for packed FP8, whose kernel
-// stages one tile through registers and is latency-bound on few rows); for
-// bf16 at least 128 keys (4 tiles) when that still occupies half the compute
-// units, which spreads the fixed per-workgroup cost (metadata, Q, partial
-// write) over more tiles.  (Measured on MI355X: C4 decode with 32 rows x 640
-// keys runs 26.1 us with 7 splits and 25.0 us with 5; FP8 C4 decode with 8
-// rows runs 28.0 us with 10 splits and 24.7 us with 20.)
-// Kernel layout.  bf16 pools take the team kernel (32-head blocks, two teams
-// of waves on alternate tiles) when doubling the head blocks buys out most of
-// the key splitting: when the rows alone, in 64-head blocks, fill less than a
-// quarter of the chip (short key splits whose partials and merge dominate),
-// or when 32-head blocks fill the whole chip without any split.  Otherwise
-// the wide kernel (64-head blocks, one tile per step, three tiles in flight)
-// moves keys faster.  Measured on MI355X, graph replay, cold inputs: C4
-// decode 32 rows x 640 keys 23.9 -> 22.7 us (team), C4 verify 128 rows
-// 37.5 -> 36.6 us (team), C128 decode 64 rows x 1152 keys 36.2 (wide) vs
-// 38.0 us (team).
+// Kernel layout.  Heads <= 16: the 16-head kernel (no padding of heads).
+// Otherwise the 64-head kernel, whose waves read each key tile for twice as
+// many heads per LDS read as the 32-head kernel; but when the rows in 64-head
+// blocks fill less than a quarter of the chip, the 32-head kernel, which
+// needs half as many key splits for the same parallelism (fewer partials
+// to write and merge).  Measured on MI355X (rocprofv3, split + merge kernel):
+// C4 decode 32 rows x 640 keys 16.1 + 3.9 us (32-head, 4 splits) vs
+// 17.2 + 4.8 us (64-head, 5 splits); C128 decode 64 rows x 1152 keys
+// 25.4 + 5.5 us (64-head, 4 splits) vs 31.2 + 4.0 us (32-head, 2 splits);
+// C4 verify 128 rows 27.3 + 5.8 us (64-head, 2 splits) vs 34.5 us (32-head,
+// no split).
 Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
     if (fp8) return Layout::kFp8;
-    if (g_force_heads_per_workgroup == kTeamHeadsPerBlock) return Layout::kTeam;
+    if (g_force_heads_per_workgroup == kWide32HeadsPerBlock) return Layout::kWide32;
     if (g_force_heads_per_workgroup == kWideHeadsPerBlock) return Layout::kWide;
     if (g_force_heads_per_workgroup == kNarrowHeadsPerBlock) return Layout::kNarrow;
+    if (H <= kNarrowHeadsPerBlock) return Layout::kNarrow;
     const int64_t wide_rows = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
-    const int64_t team_rows = (int64_t)T * ((H + kTeamHeadsPerBlock - 1) / kTeamHeadsPerBlock);
-    if (wide_rows * 4 < cus || team_rows >= cus) return Layout::kTeam;
-    return Layout::kWide;
+    return wide_rows * 4 < cus ? Layout::kWide32 : Layout::kWide;
 }
 
 int32_t heads_per_block(Layout layout) {
-    return layout == Layout::kTeam ? kTeamHeadsPerBlock
-                                   : (layout == Layout::kNarrow ? kNarrowHeadsPerBlock : kWideHeadsPerBlock);
+    return layout == Layout::kWide32
+               ? kWide32HeadsPerBlock
+               : (layout == Layout::kNarrow ? kNarrowHeadsPerBlock : kWideHeadsPerBlock);
 }
 
 // Keys per LDS tile and most keys per split of each split kernel.
@@ -265,7 +258,7 @@ int32_t max_split_keys(Layout layout) { return layout == Layout::kNarrow ? kNarr
 // stages one tile through registers and is latency-bound on few rows); for
 // bf16 at least 128 keys (4 tiles) when that still occupies half the compute
 // units, which spreads the fixed per-workgroup cost (metadata, Q, partial
-// write) over more tiles.  The team kernel takes whole tile pairs.
+// write) over more tiles.
 // (Measured on MI355X: FP8 C4 decode with 8 rows runs 28.0 us with 10
 // splits and 24.7 us with 20.)
 void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int32_t* splits, int32_t* chunk) {
@@ -286,7 +279,7 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
             if (rows * w128 * 2 >= cus) want = w128;
         }
         c = (nmax + want - 1) / want;
-        const int64_t unit = layout == Layout::kTeam ? 2 * kTileKeys : tile_keys(layout);
+        const int64_t unit = tile_keys(layout);
         c = (c + unit - 1) / unit * unit;
     }
     c = (c + tile_keys(layout) - 1) / tile_keys(layout) * tile_keys(layout);
@@ -423,9 +416,9 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
 }
 
 dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads) {
-    if (heads != 0 && heads != kNarrowHeadsPerBlock && heads != kTeamHeadsPerBlock && heads != kWideHeadsPerBlock)
+    if (heads != 0 && heads != kNarrowHeadsPerBlock && heads != kWide32HeadsPerBlock && heads != kWideHeadsPerBlock)
         return fail(DSV4_ERR_INVALID, "heads per workgroup must be 0, %d, %d or %d", kNarrowHeadsPerBlock,
-                    kTeamHeadsPerBlock, kWideHeadsPerBlock);
+                    kWide32HeadsPerBlock, kWideHeadsPerBlock);
     std::lock_guard<std::mutex> lk(g_mu);
     g_force_heads_per_workgroup = heads;
     return DSV4_OK;

@@ -5,29 +5,25 @@
 //  * split kernels -- gather + KV tile load (+ FP8 decode) + scores + online
 //    softmax + PV for one (query row, head block, key split); with a single
 //    split they also apply the sink and write out / lse:
-//      attn_wide_kernel  bf16 KV, 64-head blocks, one 32-key tile per step;
-//      attn_team_kernel  bf16 KV, 32-head blocks, two teams of two waves
-//                        taking alternate tiles (fewer splits for the same
-//                        parallelism);
-//      attn_fp8_kernel   packed FP8 KV, 64-head blocks.
+//      attn_wide_kernel<2>  bf16 KV, 64-head blocks (two head groups x two
+//                           dim halves), one 32-key tile per step;
+//      attn_wide_kernel<1>  bf16 KV, 32-head blocks (four dim quarters),
+//                           fewer splits for the same parallelism;
+//      attn_narrow_kernel   bf16 KV, 16-head blocks, four independent waves;
+//      attn_fp8_kernel      packed FP8 KV, 64-head blocks.
 //  * merge_kernel: log-sum-exp merge of the split partials with the per-head
 //    sink folded in once (test-matrix page, attention-sink correction).
 //    All query heads share each KV row (MQA with one KV head, walk-through
 //    page section 1), so a key tile is fetched from HBM once per workgroup into
-//    LDS and feeds both products on bf16 MFMA (v_mfma_f32_32x32x16_bf16):
+//    LDS and feeds both products on bf16 MFMA:
 //        S^T[keys, heads]  = K[keys, d] . Q^T[d, heads]
 //        O^T[d, heads]    += K^T[d, keys] . P^T[keys, heads]      (V = K)
 //    The second product reduces over keys.  The bf16 kernels stream key rows
-//    straight from HBM into a 4-stage LDS ring (global_load_lds) and read PV
-//    operands with the gfx950 transposing LDS read (ds_read_b64_tr_b16).  The
-//    FP8 kernel stages rows through registers, decodes them, and writes the
-//    tile twice (row-major for S, 8-key columns for PV, via an in-register
-//    8x8 transpose).
-//
-// Every wave owns 32 heads x 256 head dims of a tile: the two waves that share
-// a head set each reduce S over their half of the dims and sum the halves
-// through LDS; both then run the same online softmax and accumulate O^T for
-// their own 256 dims (8 MFMA tiles of 32x32 = 128 fp32 accumulators).
+//    straight from HBM into LDS (global_load_lds) and read PV operands with
+//    the gfx950 transposing LDS read (ds_read_b64_tr_b16).  The FP8 kernel
+//    stages rows through registers, decodes them, and writes the tile twice
+//    (row-major for S, 8-key columns for PV, via an in-register 8x8
+//    transpose).
 //
 // Work items (row, head block, split) are laid out so that consecutive
 // items -- the head blocks and splits of one row -- go to the same XCD
@@ -254,6 +250,119 @@ __device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk
     __syncthreads();  // slot list ready
 }
 
+// ---- Compressed-first key lists (the wide kernels) -------------------------
+// The wide kernels walk a row's keys compressed entries first: list index
+// i < n_ext is compressed entry i (C4: c4_indices[t][i], negative = unused;
+// C128: entry i), and i >= n_ext is window position swa_lo + (i - n_ext).
+// (The softmax does not depend on the order; the canonical order of the
+// gather entry point is unchanged.)  The C4 indices of a split depend only on
+// the query row, and the extra page-table row only on the request, so both
+// are requested in the first round of loads, together with the request
+// bounds, for the request a row has when every request has equally many
+// query rows (t * B / T); a wrong guess costs one reload.  Window slots need
+// the row's position, so they come from a second round: one or a few
+// page-table entries at uniform addresses, read with scalar loads, which a
+// wave can wait for without waiting for tile copies already in flight.
+template <int kMaxKeys>
+struct ExtPrefetch {
+    int32_t c4[kMaxKeys / 256];    // C4 index of list entry k0 + tid + 256*u (clamped into the row)
+    int32_t tab[kTableCap / 256];  // extra page-table entries tid + 256*j of request r_guess
+    int r_guess;
+};
+
+template <int kMaxKeys>
+__device__ __forceinline__ void prefetch_ext(const AttnArgs& a, int t, int k0, int tid, ExtPrefetch<kMaxKeys>& pf) {
+    pf.r_guess = min(a.m.B - 1, (int)((int64_t)t * a.m.B / max(a.T, 1)));
+    if (a.m.R == 4) {
+        const int32_t* c4_row = a.m.c4 + (int64_t)t * a.m.c4_ld;
+#pragma unroll
+        for (int u = 0; u < kMaxKeys / 256; ++u) pf.c4[u] = c4_row[min(k0 + tid + 256 * u, a.m.K - 1)];  // K >= 1
+    }
+    if (a.m.R != 0 && a.ext_pages <= kTableCap) {
+        const int32_t* ext_row = a.m.ext_table + (int64_t)pf.r_guess * a.m.ext_ld;
+#pragma unroll
+        for (int j = 0; j < kTableCap / 256; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+    }
+}
+
+// Slots of the split's compressed entries into s_slot[i] (i = list index -
+// k0); window entries are left to the caller.
+template <int kMaxKeys>
+__device__ __forceinline__ void build_ext_slots(const AttnArgs& a, const RowKeys& rk, int k0, int n_here,
+                                                ExtPrefetch<kMaxKeys>& pf, int32_t* s_slot, int32_t* s_table,
+                                                int tid) {
+    constexpr int kU = kMaxKeys / 256;
+    constexpr int kTU = kTableCap / 256;
+    if (a.m.R == 0) return;
+    const bool cached = a.ext_pages <= kTableCap;
+    const int32_t* ext_row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
+    if (cached) {
+        if (rk.r != pf.r_guess) {  // uniform: the guessed request was wrong
+#pragma unroll
+            for (int j = 0; j < kTU; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < kTU; ++j)
+            if (tid + 256 * j < a.ext_pages) s_table[tid + 256 * j] = pf.tab[j];
+    }
+    int32_t c[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) c[u] = a.m.R == 4 ? pf.c4[u] : k0 + tid + 256 * u;
+    __syncthreads();  // s_table ready
+    // A table too long for LDS: one more round of (clamped) loads.
+    int32_t pg[kU] = {};
+    if (!cached) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) pg[u] = ext_row[c[u] >= 0 ? min(c[u] >> 8, a.ext_pages - 1) : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int i = tid + 256 * u;
+        if (i < n_here && k0 + i < rk.n_ext)
+            s_slot[i] = c[u] < 0 ? -1 : (cached ? s_table[c[u] >> 8] : pg[u]) * kPage + (c[u] & (kPage - 1));
+    }
+    __syncthreads();  // compressed slots ready
+}
+
+// Page-table entries of the window pages a split touches: pages pg_lo ..
+// pg_lo + 4 (clamped to the last page touched), which covers any split of at
+// most 1024 window keys.  They are issued as uniform scalar loads whose
+// results the compiler is not told about: wait_swa_pages() must run before
+// any use, and no LDS access may come in between (scalar and LDS loads share
+// a counter, and a partial LDS wait could pass while a scalar load is still
+// pending).
+struct SwaPages {
+    int32_t e[5];
+    int pg_lo;
+    bool any;  // the split holds window keys
+};
+
+__device__ __forceinline__ SwaPages issue_swa_pages(const AttnArgs& a, const RowKeys& rk, int k0, int n_here) {
+    SwaPages sp;
+    const int i_lo = max(k0, rk.n_ext), i_hi = min(k0 + n_here, rk.n_ext + rk.n_swa);
+    sp.any = __builtin_amdgcn_readfirstlane(i_lo < i_hi ? 1 : 0) != 0;  // uniform: rk is
+    sp.pg_lo = __builtin_amdgcn_readfirstlane((rk.swa_lo + max(i_lo - rk.n_ext, 0)) >> 8);
+    const int pg_hi = __builtin_amdgcn_readfirstlane(sp.any ? (rk.swa_lo + (i_hi - 1 - rk.n_ext)) >> 8 : sp.pg_lo);
+    const int32_t* row = a.m.swa_table + (int64_t)__builtin_amdgcn_readfirstlane(rk.r) * a.m.swa_ld;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) sp.e[k] = 0;
+    if (sp.any) {  // only then are pg_lo .. pg_hi pages of the row
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const int32_t* p = row + min(sp.pg_lo + k, pg_hi);
+            asm volatile("s_load_dword %0, %1, 0x0" : "=s"(sp.e[k]) : "s"(p) : "memory");
+        }
+    }
+    return sp;
+}
+
+__device__ __forceinline__ void wait_swa_pages(SwaPages& sp) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+s"(sp.e[0]), "+s"(sp.e[1]), "+s"(sp.e[2]), "+s"(sp.e[3]), "+s"(sp.e[4])
+                 :
+                 : "memory");
+}
+
 // bf16 kernel: the row address of every key [k0, k0 + n_here) of the split
 // (zero_row for unused C4 entries and for the padding up to the last tile),
 // built once so that copying a tile needs no address arithmetic.
@@ -394,23 +503,27 @@ __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask
     l_run += psum;
 }
 
-// Epilogue.  Accumulator r of tile mb holds head (l & 31) of the wave's half,
-// dim 256*dh + 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3).  One split: apply
-// the sink and write out / lse.  Several: publish the normalised partial (in
-// bf16: it is a convex combination of key rows, so 8 significant bits keep it
-// within the output's own rounding; an empty split publishes zeros) and its
-// base-2 log-sum-exp (-inf for an empty split) for merge_kernel.
-// The bf16 rows are first assembled in LDS (stage_lo / stage_hi for the two
-// head halves: 32 head rows of
-// 1 KiB, 16-byte chunk c of row r at chunk c ^ r), so that every global
-// store instruction writes one whole 1 KiB row.  The caller's LDS must be
-// free: the first barrier below waits until every wave is done with it.
-__device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int hh, int dh, int l,
-                                             const f32x16 (&oacc)[8], float m_run, float l_half,
+// Epilogue of the wide layouts.  kHH head groups of 32 heads; wave (hh, dq)
+// holds O^T for heads 32*hh + (l & 31) and its slice of kDims = 128*kHH dims:
+// accumulator r of tile mb is dim kDims*dq + 32*mb + 8*(r >> 2) + 4*(l >> 5) +
+// (r & 3).  One split: apply the sink and write out / lse.  Several: publish
+// the normalised partial (in bf16: it is a convex combination of key rows,
+// so 8 significant bits keep it within the output's own rounding; an empty
+// split publishes zeros) and its base-2 log-sum-exp (-inf for an empty
+// split) for merge_kernel.  The bf16 rows are first assembled in LDS
+// (stage_lo / stage_hi for the head groups: 32 head rows of 1 KiB, 16-byte
+// chunk c of row r at chunk c ^ r), so that every global store instruction
+// writes one whole 1 KiB row.  The caller's LDS must be free: the first
+// barrier below waits until every wave is done with it.
+template <int kHH>
+__device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, int hh, int dq, int l,
+                                             const f32x16 (&oacc)[4 * kHH], float m_run, float l_half,
                                              uint8_t* stage_lo, uint8_t* stage_hi) {
+    constexpr int kGroup = 4 / kHH;
+    constexpr int kRows = 32 / kGroup;  // head rows stored by each wave
     uint8_t* stage = hh ? stage_hi : stage_lo;
     const float l_run = l_half + __shfl_xor(l_half, 32);  // both halves of the head's keys
-    const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
+    const int my_head = it.hb * 32 * kHH + hh * 32 + (l & 31);
     const bool head_ok = my_head < a.H;
     float f = 0.f, lse2 = -INFINITY;
     if (a.splits == 1) {
@@ -431,10 +544,10 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, 
         const int r = l & 31;
         uint8_t* base = stage + r * 1024 + 8 * (l >> 5);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
+        for (int mb = 0; mb < 4 * kHH; ++mb) {
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const int c = dh * 32 + 4 * mb + qd;
+                const int c = dq * 16 * kHH + 4 * mb + qd;
                 const f32x16& o = oacc[mb];
                 *(u32x2*)(base + 16 * (c ^ r)) = u32x2{pack_bf16x2(o[4 * qd] * f, o[4 * qd + 1] * f),
                                                        pack_bf16x2(o[4 * qd + 2] * f, o[4 * qd + 3] * f)};
@@ -442,24 +555,25 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, 
         }
     }
     __syncthreads();
-    // Wave (hh, dh) stores rows 16*dh .. 16*dh+15 of its half; lane l moves
-    // the row's 16-byte chunk l.
+    // Wave (hh, dq) stores rows kRows*dq .. +kRows of its head group; lane l
+    // moves the row's 16-byte chunk l.
 #pragma unroll 4
-    for (int e = 0; e < 16; ++e) {
-        const int r = 16 * dh + e;
-        const int head = it.hb * kWideHeadsPerBlock + hh * 32 + r;
+    for (int e = 0; e < kRows; ++e) {
+        const int r = kRows * dq + e;
+        const int head = it.hb * 32 * kHH + hh * 32 + r;
         if (head >= a.H) break;
         const u32x4 v = *(const u32x4*)(stage + r * 1024 + 16 * (l ^ r));
+        // Streaming stores: nothing in this kernel reads these rows again.
         if (a.splits == 1) {
             uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
-            *(u32x2*)orow = u32x2{v[0], v[1]};  // out rows need only 8-byte alignment
-            *(u32x2*)(orow + 4) = u32x2{v[2], v[3]};
+            __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)orow);  // out rows need only 8-byte alignment
+            __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(orow + 4));
         } else {
             const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + head;
-            *(u32x4*)(a.ws_o + part * kHeadDim + 8 * l) = v;
+            __builtin_nontemporal_store(v, (u32x4*)(a.ws_o + part * kHeadDim + 8 * l));
         }
     }
-    if (head_ok && dh == 0 && l < 32) {
+    if (head_ok && dq == 0 && l < 32) {
         if (a.splits == 1) {
             if (a.lse != nullptr) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
         } else {
@@ -512,10 +626,14 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 KV, wide layout: one workgroup per (row, block of 64 heads, key
-// split); wave w = 2*hh + dh owns heads [32*hh, 32*hh + 32) and head dims
-// [256*dh, 256*dh + 256) of every tile.  Key rows stream from HBM into a
-// 4-stage LDS ring with direct global->LDS loads (no VGPR staging).
+// bf16 KV, wide layouts: one workgroup per (row, block of 32*kHH heads, key
+// split).  kHH = 2: wave w = 2*hh + dq owns heads [32*hh, 32*hh + 32) and
+// head dims [256*dq, 256*dq + 256) of every tile; kHH = 1: wave w = dq owns
+// head dims [128*dq, 128*dq + 128) of all 32 heads.  The waves of one head
+// group (2 or 4) each reduce the scores over their dims and sum the partials
+// through LDS, in wave order, so that all of them hold the same scores and
+// run the same softmax.  Key rows stream from HBM into a 4-stage LDS ring
+// with direct global->LDS loads (no VGPR staging).
 //
 // Tile layout in LDS (32 KiB per stage).  Rows 8g .. 8g+7 form group g; the
 // 512 bytes of dim half dh of those rows form four 1 KiB blocks m (128-byte
@@ -545,7 +663,13 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
 // list, per-tile key masks and page-table cache live in the exchange
 // buffers until the loop starts.
 // ---------------------------------------------------------------------------
+template <int kHH>
 __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
+    constexpr int kGroup = 4 / kHH;          // waves per head group (dim slices)
+    constexpr int kDims = kHeadDim / kGroup;  // head dims per wave
+    constexpr int kSteps = kDims / 16;        // score k-steps per tile
+    constexpr int kMb = kDims / 32;           // PV dim blocks per wave
+    constexpr int kHeads = 32 * kHH;          // heads per workgroup
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) float s_x[2][4 * 64 * 16];
     int32_t* s_slot = (int32_t*)&s_x[0][0];                // kMaxSplitKeys entries, prologue only
@@ -558,49 +682,76 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     if (!decode_item(a, it)) return;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int hh = w >> 1, dh = w & 1;
+    const int hh = w / kGroup, dq = w % kGroup;
 
-    // Metadata round 1 (request bounds), then Q (independent of it), then
-    // the rest of the row resolution.
+    // Round 1: the request bounds, the split's C4 indices and the guessed
+    // request's extra page-table row, then Q (independent of all of them,
+    // issued last so that waiting for the metadata does not wait for it).
     const RequestChunk rc = load_requests(a.m, 0, l);
+    const int k0 = it.s * a.chunk;
+    ExtPrefetch<kMaxSplitKeys> pf;
+    prefetch_ext(a, it.t, k0, tid, pf);
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 qf[16];
+    // Q^T as the B operand of the scores: lane holds head (l & 31) of the
+    // wave's head group, dims kDims*dq + 16*j + 8*(l >> 5) .. +8 of k-step j.
+    // Heads past H read head H-1; their results are never written.
+    bf16x8 qf[kSteps];
     {
-        const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
-        load_q(a, it.t, my_head, dh, l, qf);
+        const int my_head = it.hb * kHeads + hh * 32 + (l & 31);
+        const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(my_head, a.H - 1) * a.q_s1 + dq * kDims + 8 * (l >> 5);
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
     }
     __builtin_amdgcn_sched_barrier(0);
     const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
-    const int k0 = it.s * a.chunk;
     const int n_here = __builtin_amdgcn_readfirstlane(max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0));
     const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
-    build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+    build_ext_slots(a, rk, k0, n_here, pf, s_slot, s_table, tid);
 
     // Row addresses of the keys this wave copies: tile j, row 8w + e sits in
-    // lane (8j + e) & 63 of ad[(8j + e) >> 6]; unused keys read the zero row.
-    uint64_t ad[kMaxSplitKeys / 256];
+    // lane (8j + e) & 63 of ad[(8j + e) >> 6]; and, for the first three
+    // tiles, the row lane l copies (8w + ((l >> 1) & 7)) in pro[j], so those
+    // copies need no cross-lane step.  Unused keys read the zero row; window
+    // keys are filled in once their page entries have arrived.
+    const int dma_row = (l >> 1) & 7;
+    auto ext_addr = [&](int key) -> uint64_t {
+        const int32_t slot = key < n_here && k0 + key < rk.n_ext ? s_slot[key] : -1;
+        return slot >= 0 ? (uint64_t)(uintptr_t)(a.ext_pool + (int64_t)slot * a.ext_row_bytes)
+                         : (uint64_t)(uintptr_t)a.zero_row;
+    };
+    uint64_t ad[kMaxSplitKeys / 256], pro[3];
 #pragma unroll
     for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
         const int idx = 64 * u + l;
-        const int key = kTileKeys * (idx >> 3) + 8 * w + (idx & 7);
-        const int32_t slot = key < n_here ? s_slot[key] : -1;
-        const bool swa = k0 + key < rk.n_swa;
-        ad[u] = slot >= 0 ? (uint64_t)(uintptr_t)((swa ? a.swa_pool : a.ext_pool) +
-                                                  (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes))
-                          : (uint64_t)(uintptr_t)a.zero_row;
+        ad[u] = ext_addr(kTileKeys * (idx >> 3) + 8 * w + (idx & 7));
     }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) pro[j] = ext_addr(kTileKeys * j + 8 * w + dma_row);
+    // Round 2 (window pages, scalar loads), issued after the last LDS access
+    // above and waited for after the first copies below (nothing in between
+    // touches LDS).
+    __builtin_amdgcn_sched_barrier(0);
+    SwaPages swp = issue_swa_pages(a, rk, k0, n_here);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Copy of one tile: lane p moves 16-byte chunks of row 8w + ((p >> 1) & 7),
-    // at chunk 2*(p >> 4) + ((p & 1) ^ (w & 1)) of each 128-byte line.
-    const int dma_row = (l >> 1) & 7;
+    // at chunk 2*(p >> 4) + ((p & 1) ^ (w & 1)) of each 128-byte line; the
+    // row address comes from pro[] for the first three tiles and from ad[]
+    // (one cross-lane permute) after them.
     const uint32_t dma_lane_off = 16u * (2u * (l >> 4) + ((l & 1) ^ (w & 1)));
     auto fetch_tile = [&](int tile) {
-        const int u = tile >> 3;
-        const uint64_t au = u == 0 ? ad[0] : (u == 1 ? ad[1] : (u == 2 ? ad[2] : ad[3]));
-        const int src = 4 * (8 * (tile & 7) + dma_row);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
-        const uint8_t* row = (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo) + dma_lane_off;
+        uint64_t ra;
+        if (tile < 3) {
+            ra = tile == 0 ? pro[0] : (tile == 1 ? pro[1] : pro[2]);
+        } else {
+            const int u = tile >> 3;
+            const uint64_t au = u == 0 ? ad[0] : (u == 1 ? ad[1] : (u == 2 ? ad[2] : ad[3]));
+            const int src = 4 * (8 * (tile & 7) + dma_row);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
+            ra = ((uint64_t)hi << 32) | lo;
+        }
+        const uint8_t* row = (const uint8_t*)(uintptr_t)ra + dma_lane_off;
         const uint32_t dst = lds_addr(&s_tile[tile % kStages][0]) + w * 8192;
         dma16_off<0>(row, dst);
         dma16_off<128>(row, dst + 1024);
@@ -615,25 +766,25 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     // Per-lane LDS bases of the score operand and of the two transposing PV
     // reads (rows r0 = 16pp + 4hq + kq and r0 + 8); see the layout above.
     const int kk = l & 31, khi = l >> 5, kg = kk >> 3;
-    const uint32_t s_base = kg * 8192 + dh * 4096 + 32 * (kk & 7) + 16 * (khi ^ (kg & 1));
+    const uint32_t s_base = kg * 8192 + dq * (16 * kDims) + 32 * (kk & 7) + 16 * (khi ^ (kg & 1));
     const int a4 = l & 3, kq = (l >> 2) & 3, half = (l >> 4) & 1, hq = l >> 5;
-    const uint32_t t_base0 = dh * 4096 + 256 * half + 128 * hq + 32 * kq + 8 * a4;
+    const uint32_t t_base0 = dq * (16 * kDims) + 256 * half + 128 * hq + 32 * kq + 8 * a4;
     const uint32_t t_base1 = t_base0 + 8192 + 16 - 32 * (a4 >> 1);
     const uint32_t ring = lds_addr(&s_tile[0][0]);
 
-    auto read_k = [&](int tile, bf16x8 (&av)[16]) {
+    auto read_k = [&](int tile, bf16x8 (&av)[kSteps]) {
         const lds_void* base = (const lds_void*)(uintptr_t)(ring + (tile % kStages) * (kTileKeys * 1024) + s_base);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) av[j] = *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)base + 256 * j);
+        for (int j = 0; j < kSteps; ++j) av[j] = *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)base + 256 * j);
     };
-    // K^T operand of PV: lane L takes dim 32*mb + (L & 31) of its dim half and
-    // keys G(pp, L >> 5) from two transposing reads (rows r0 and r0 + 8).
-    auto read_kt = [&](int tile, bf16x8 (&kt)[16]) {
+    // K^T operand of PV: lane L takes dim 32*mb + (L & 31) of its dim slice
+    // and keys G(pp, L >> 5) from two transposing reads (rows r0 and r0 + 8).
+    auto read_kt = [&](int tile, bf16x8 (&kt)[2 * kMb]) {
         const uint32_t st = ring + (tile % kStages) * (kTileKeys * 1024);
         const __attribute__((address_space(3))) uint8_t* b0 = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_base0);
         const __attribute__((address_space(3))) uint8_t* b1 = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_base1);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+        for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b0 + 16384 * pp + 512 * mb));
@@ -642,29 +793,53 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
             }
     };
 
-    f32x16 oacc[8];
+    f32x16 oacc[kMb];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
+    for (int mb = 0; mb < kMb; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
     // PV operands of the previous tile, consumed one iteration later (zero
     // before the first tile, so the first PV step adds nothing).
-    bf16x8 kt[16], pb[2];
+    bf16x8 kt[2 * kMb], pb[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) kt[j] = bf16x8{};
+    for (int j = 0; j < 2 * kMb; ++j) kt[j] = bf16x8{};
     pb[0] = bf16x8{};
     pb[1] = bf16x8{};
 
-    // Every compiler-visible load (metadata, Q) is retired here, so the only
-    // vector-memory operations in flight below are this wave's copies into
-    // LDS (8 per tile) and the explicit vmcnt waits count exactly those.
-    wait_vmcnt<0>();
-    if (n_tiles > 0) fetch_tile(0);
-    if (n_tiles > 1) fetch_tile(1);
-    if (n_tiles > 2) fetch_tile(2);
-    // Valid-key mask of every tile (built while the first tiles are in flight).
+    // The tile copies below go out while Q (the last compiler-visible vector
+    // loads) may still be in flight: every explicit vmcnt wait below counts
+    // the copies issued after its target, and loads completing in order make
+    // any earlier ones only strengthen it.
+    // Tiles made of compressed entries only are requested right away.
+    const int n_first = min(n_tiles, 3);
+    const int n_early = min(n_first, max(0, rk.n_ext - k0) / kTileKeys);
+    for (int j = 0; j < n_early; ++j) fetch_tile(j);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_swa_pages(swp);
+    __builtin_amdgcn_sched_barrier(0);
+    // Window keys, now that their page entries have arrived.
+    if (swp.any) {
+        auto swa_addr = [&](int key, uint64_t cur) -> uint64_t {
+            const int i = k0 + key;
+            if (key >= n_here || i < rk.n_ext) return cur;
+            const int x = rk.swa_lo + (i - rk.n_ext);
+            const int pk = (x >> 8) - swp.pg_lo;
+            const int32_t e = pk == 0 ? swp.e[0] : (pk == 1 ? swp.e[1] : (pk == 2 ? swp.e[2] : (pk == 3 ? swp.e[3] : swp.e[4])));
+            return (uint64_t)(uintptr_t)(a.swa_pool + ((int64_t)e * kPage + (x & (kPage - 1))) * a.swa_row_bytes);
+        };
+#pragma unroll
+        for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
+            const int idx = 64 * u + l;
+            ad[u] = swa_addr(kTileKeys * (idx >> 3) + 8 * w + (idx & 7), ad[u]);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) pro[j] = swa_addr(kTileKeys * j + 8 * w + dma_row, pro[j]);
+    }
+    for (int j = n_early; j < n_first; ++j) fetch_tile(j);
+    // Valid-key mask of every tile: window keys are always valid.
     for (int j = w; j < n_tiles; j += 4) {
         const int key = kTileKeys * j + (l & 31);
-        const uint64_t b = __ballot(l < 32 && key < n_here && s_slot[key] >= 0);
+        const bool valid = key < n_here && (k0 + key >= rk.n_ext || s_slot[key] >= 0);
+        const uint64_t b = __ballot(l < 32 && valid);
         if (l == 0) s_mask[j] = (uint32_t)b;
     }
     __syncthreads();
@@ -675,10 +850,10 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         else if (n_tiles > 1) wait_vmcnt<8>();
         else wait_vmcnt<0>();
         __syncthreads();  // tile 0 is in LDS for every wave; the prologue scratch is dead
-        bf16x8 av[16];
+        bf16x8 av[kSteps];
         read_k(0, av);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
+        for (int j = 0; j < kSteps; ++j) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
     }
 
     const float sl2 = a.scale_log2;
@@ -696,20 +871,22 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         __syncthreads();  // S partials of tile i published; tile i+1 landed; tile i-1's stage is free
         if (i + 3 < n_tiles) fetch_tile(i + 3);
 
-        // The partner's S partial of tile i and the score operand of tile
-        // i+1 (when tile i is the last, that stage holds stale rows whose
-        // scores are discarded).
-        f32x4 other[4];
-        {
-            const f32x4* op = (const f32x4*)xb + (w ^ 1) * 256 + l;
+        // The other S partials of the head group for tile i and the score
+        // operand of tile i+1 (when tile i is the last, that stage holds stale
+        // rows whose scores are discarded).
+        f32x4 part[kGroup][4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) other[q] = op[64 * q];
+        for (int v = 0; v < kGroup; ++v) {
+            if (v == dq) continue;
+            const f32x4* op = (const f32x4*)xb + (hh * kGroup + v) * 256 + l;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) part[v][q] = op[64 * q];
         }
-        bf16x8 av[16];
+        bf16x8 av[kSteps];
         read_k(i + 1, av);
         // PV of tile i-1 while those reads land; then the PV operand of tile i.
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+        for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
                 oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
@@ -725,10 +902,20 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         // shares are added in write_result.
         f32x16 snext = f32x16{};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
+        for (int j = 0; j < kSteps / 2; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
+        // Sum of the group's partials in wave order (this wave's own from
+        // its registers), identical in every wave of the group.
         float sv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = sacc[r] + other[r >> 2][r & 3];
+        for (int r = 0; r < 16; ++r) {
+            float x = 0.f;
+#pragma unroll
+            for (int v = 0; v < kGroup; ++v) {
+                const float pv = v == dq ? sacc[r] : part[v][r >> 2][r & 3];
+                x = v == 0 ? pv : x + pv;
+            }
+            sv[r] = x;
+        }
         const uint32_t tmask = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i);
         if (tmask != 0xFFFFFFFFu) {
             const uint32_t mine = tmask >> key_shift;
@@ -758,9 +945,9 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         }
         l_run += psum;
 #pragma unroll
-        for (int j = 8; j < 16; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
+        for (int j = kSteps / 2; j < kSteps; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kSteps / 2; ++j) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then VALU
         }
@@ -768,230 +955,11 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     }
     // PV of the last tile.
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
             oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
-    write_result(a, it, hh, dh, l, oacc, m_run, l_run, &s_tile[0][0], &s_tile[1][0]);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 KV, team layout: one workgroup per (row, block of 32 heads, key split).  Key rows
-// stream from HBM into a 4-stage LDS ring with direct global->LDS loads (no
-// VGPR staging).  The four waves form two teams of two: team p takes the
-// split's tiles 2j + p, so a pair of tiles is processed per step, and within
-// a team wave dh owns head dims [256*dh, 256*dh + 256) of all 32 heads (its
-// partner holds the other half of each score).  Each team keeps its own
-// online softmax; the two are merged in the epilogue.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void attn_team_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
-    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
-    __shared__ int32_t s_slot[kMaxSplitKeys];
-    __shared__ int32_t s_table[kTableCap];
-    __shared__ __attribute__((aligned(16))) uint64_t s_addr[kMaxSplitKeys];
-
-    Item it;
-    if (!decode_item(a, it)) return;
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;  // wave-uniform
-    const int team = w >> 1, dh = w & 1;
-    const int head0 = it.hb * kTeamHeadsPerBlock;
-
-    const RowKeys rk = row_keys(a.m, it.t, l);
-    const int k0 = it.s * a.chunk;
-    const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
-    build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
-    build_row_addresses(a, rk, k0, n_here, s_slot, s_addr, tid);
-    const uint64_t zero_row = (uint64_t)(uintptr_t)a.zero_row;
-
-    // Wave w copies tile keys 8w .. 8w+7: their row addresses come from LDS
-    // (four 16-byte broadcast reads) and lane l moves logical chunk
-    // l ^ row_swz(k) so that each row lands in the swizzled layout.
-    auto fetch_tile = [&](int tile) {
-        uint8_t* dst = &s_tile[tile % kStages][0];
-        const u64x2* ap = (const u64x2*)&s_addr[tile * kTileKeys + 8 * w];
-        const u64x2 a01 = ap[0], a23 = ap[1], a45 = ap[2], a67 = ap[3];
-        const uint64_t rows[8] = {a01[0], a01[1], a23[0], a23[1], a45[0], a45[1], a67[0], a67[1]};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            dma16((const uint8_t*)(uintptr_t)rows[e] + 16 * (l ^ row_swz(8 * w + e)), lds_addr(dst + (8 * w + e) * 1024));
-    };
-
-    f32x16 oacc[8];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float no_scale[16] = {};
-
-    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
-    const int n_pairs = (n_tiles + 1) / 2;
-    // Retire every compiler-visible load (slot metadata) first, so the only
-    // vector-memory operations in flight below are this wave's copies into
-    // LDS (8 for Q, then 8 per tile) and the explicit vmcnt waits count
-    // exactly those.
-    wait_vmcnt<0>();
-    // Q travels the same way as the keys: the block's 32 head rows (zero rows
-    // past H) go to ring stage 3, in the swizzled row layout, together with
-    // tiles 0 and 1.  Once every wave holds its Q operands, stage 3 returns
-    // to the ring and tiles 2 and 3 are requested.
-    bf16x8 qf[16];
-    if (n_tiles > 0) {
-        uint8_t* qs = &s_tile[3][0];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int k = 8 * w + e;
-            const int head = head0 + k;
-            const uint8_t* src = head < a.H ? (const uint8_t*)(a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1)
-                                            : a.zero_row;
-            dma16(src + 16 * (l ^ row_swz(k)), lds_addr(qs + k * 1024));
-        }
-        fetch_tile(0);
-        if (n_tiles > 1) fetch_tile(1);
-        wait_vmcnt<0>();
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 16; ++j) qf[j] = *(const bf16x8*)(qs + krow_offset(l & 31, dh * 32 + 2 * j + (l >> 5)));
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __syncthreads();  // every wave has its Q: stage 3 is free
-        if (n_tiles > 2) fetch_tile(2);
-        if (n_tiles > 3) fetch_tile(3);
-    }
-
-    for (int j = 0; j < n_pairs; ++j) {
-        if (j > 0) {
-            // The pair fetched at the previous step is the only one in flight.
-            wait_vmcnt<0>();
-            __syncthreads();  // tiles 2j, 2j+1 are in LDS for every wave; pair j-1's stages are free
-            if (2 * j + 2 < n_tiles) fetch_tile(2 * j + 2);
-            if (2 * j + 3 < n_tiles) fetch_tile(2 * j + 3);
-        }
-        // Team 1 has no tile when the split's tile count is odd and this is
-        // the last pair: it then runs on team 0's tile under an empty key
-        // mask, so every probability is zero, its reference does not move and
-        // the PV products add zero times finite keys.
-        const int ti = 2 * j + team;
-        const bool busy = ti < n_tiles;
-        const uint8_t* tile = &s_tile[(busy ? ti : 2 * j) % kStages][0];
-        const uint64_t vmask = __ballot(busy && l < 32 && s_addr[ti * kTileKeys + (l & 31)] != zero_row);
-
-        // S^T partial over this wave's 256 dims (operands read ahead of the MFMAs).
-        f32x16 sacc = f32x16{};
-        {
-            const int k = l & 31;
-            bf16x8 av[16];
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) av[jj] = *(const bf16x8*)(tile + krow_offset(k, dh * 32 + 2 * jj + (l >> 5)));
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[jj], qf[jj], sacc, 0, 0, 0);
-        }
-        exchange_partial(s_sx, w, l, sacc);
-
-        {
-            // O^T[d, heads] += K^T[d, keys] P^T[keys, heads].  The K^T operand
-            // of lane L (dim 32*mb + (L & 31), keys G(pp, L >> 5)) comes from
-            // two transposing reads: source lane S of each 16-lane block points
-            // at key row r_k (k = (S >> 2) & 3) and dims d0 .. d0+3, d0 =
-            // 16*((S >> 4) & 1) + 4*(S & 3); the block returns dim d0 + j of
-            // rows r_0..r_3 to lane 4*(S & 3) + j.  These reads do not depend
-            // on P: they are issued before the softmax and land while it runs
-            // (the schedule barriers keep the compiler from sinking them).
-            bf16x8 kt[16];
-            {
-                const int a4 = l & 3, kq = (l >> 2) & 3, hq = l >> 5, half = (l >> 4) & 1;
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb) {
-                    const int d0 = dh * 256 + 32 * mb + 16 * half + 4 * a4;
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const int r0 = 16 * pp + 4 * hq + kq;
-                        const int r1 = r0 + 8;
-                        const uint8_t* p0 = tile + krow_offset(r0, d0 >> 3) + 2 * (d0 & 7);
-                        const uint8_t* p1 = tile + krow_offset(r1, d0 >> 3) + 2 * (d0 & 7);
-                        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-                        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
-                        kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            bf16x8 pb[2], pbs[2];
-            softmax_tile<false>(sacc, vmask, a.scale_log2, l, no_scale, m_run, l_run, oacc, pb, pbs);
-#pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp)
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
-        }
-    }
-
-    // Epilogue.  Accumulator r of tile mb holds head (l & 31), dim 256*dh +
-    // 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3), unnormalised, with the
-    // team's running reference m_run and (per lane) half of its denominator.
-    // Each team's fp32 rows go to LDS (team p: 32 rows of 2 KiB at byte
-    // 65536*p, 16-byte chunk c of row r at chunk c ^ r), then wave w merges
-    // rows 8w .. 8w+7 of the two teams, lane l owning dims 8l .. 8l+7, and
-    // writes either the output with the sink folded in (one split) or the
-    // normalised bf16 partial and its base-2 log-sum-exp (several).
-    {
-        const float l_sum = l_run + __shfl_xor(l_run, 32);  // both halves of the head's keys
-        float (*s_ml)[2][kTeamHeadsPerBlock] = (float (*)[2][kTeamHeadsPerBlock])s_sx;  // [team][m, l][head]
-        __syncthreads();  // every wave is done with the ring and the exchange buffer
-        uint8_t* stage = &s_tile[0][0] + 65536 * team;
-        const int r = l & 31;
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int c = dh * 64 + 8 * mb + 2 * qd + (l >> 5);
-                const f32x16& o = oacc[mb];
-                *(f32x4*)(stage + r * 2048 + 16 * (c ^ r)) = f32x4{o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]};
-            }
-        if (dh == 0 && l < 32) {
-            s_ml[team][0][r] = l_sum > 0.f ? m_run : -INFINITY;
-            s_ml[team][1][r] = l_sum;
-        }
-        __syncthreads();
-        for (int e = 0; e < 8; ++e) {
-            const int rr = 8 * w + e;
-            const int head = head0 + rr;
-            if (head >= a.H) break;
-            const float m0 = s_ml[0][0][rr], l0 = s_ml[0][1][rr];
-            const float m1 = s_ml[1][0][rr], l1 = s_ml[1][1][rr];
-            const float sig = (a.splits == 1 && a.sink != nullptr) ? a.sink[head] * kLog2e : -INFINITY;
-            const float M = fmaxf(fmaxf(m0, m1), sig);
-            float e0 = 0.f, e1 = 0.f, Z = 0.f;
-            if (M != -INFINITY) {
-                e0 = m0 == -INFINITY ? 0.f : fast_exp2(m0 - M);
-                e1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
-                Z = l0 * e0 + l1 * e1 + (sig == -INFINITY ? 0.f : fast_exp2(sig - M));
-            }
-            const float f = Z > 0.f ? 1.f / Z : 0.f;
-            const float w0 = e0 * f, w1 = e1 * f;
-            const uint8_t* row0 = &s_tile[0][0] + rr * 2048;
-            const uint8_t* row1 = row0 + 65536;
-            const f32x4 a0 = *(const f32x4*)(row0 + 16 * ((2 * l) ^ rr));
-            const f32x4 a1 = *(const f32x4*)(row0 + 16 * ((2 * l + 1) ^ rr));
-            const f32x4 b0 = *(const f32x4*)(row1 + 16 * ((2 * l) ^ rr));
-            const f32x4 b1 = *(const f32x4*)(row1 + 16 * ((2 * l + 1) ^ rr));
-            const u32x4 v = {pack_bf16x2(a0[0] * w0 + b0[0] * w1, a0[1] * w0 + b0[1] * w1),
-                             pack_bf16x2(a0[2] * w0 + b0[2] * w1, a0[3] * w0 + b0[3] * w1),
-                             pack_bf16x2(a1[0] * w0 + b1[0] * w1, a1[1] * w0 + b1[1] * w1),
-                             pack_bf16x2(a1[2] * w0 + b1[2] * w1, a1[3] * w0 + b1[3] * w1)};
-            const float lse2 = Z > 0.f ? M + fast_log2(Z) : -INFINITY;
-            if (a.splits == 1) {
-                uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
-                *(u32x2*)orow = u32x2{v[0], v[1]};  // out rows need only 8-byte alignment
-                *(u32x2*)(orow + 4) = u32x2{v[2], v[3]};
-                if (a.lse != nullptr && l == 0) a.lse[(int64_t)it.t * a.lse_s0 + head] = lse2 * kLn2;
-            } else {
-                const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + head;
-                *(u32x4*)(a.ws_o + part * kHeadDim + 8 * l) = v;
-                if (l == 0) a.ws_lse[part] = lse2;
-            }
-        }
-    }
+    write_result<kHH>(a, it, hh, dq, l, oacc, m_run, l_run, &s_tile[0][0], &s_tile[1][0]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1401,7 +1369,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
         }
         __syncthreads();
     }
-    write_result(a, it, hh, dh, l, oacc, m_run, l_run, s_krow, s_kt);
+    write_result<2>(a, it, hh, dh, l, oacc, m_run, l_run, s_krow, s_kt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1499,11 +1467,11 @@ hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream
         case Layout::kFp8:
             hipLaunchKernelGGL(attn_fp8_kernel, grid, dim3(256), 0, stream, a);
             break;
-        case Layout::kTeam:
-            hipLaunchKernelGGL(attn_team_kernel, grid, dim3(256), 0, stream, a);
-            break;
         case Layout::kWide:
-            hipLaunchKernelGGL(attn_wide_kernel, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(attn_wide_kernel<2>, grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kWide32:
+            hipLaunchKernelGGL(attn_wide_kernel<1>, grid, dim3(256), 0, stream, a);
             break;
         case Layout::kNarrow:
             hipLaunchKernelGGL(attn_narrow_kernel, grid, dim3(256), 0, stream, a);

@@ -172,9 +172,10 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
 
 /*
  * Tuning / test hook: force the bf16 kernel variant by its query heads per
- * workgroup (16: four independent waves on alternate 16-key tiles; 32: two
- * teams of waves on alternate tiles; 64: one tile per step), or 0 for the
- * automatic choice.  Packed FP8 pools always use 64.  Process-wide.
+ * workgroup (16: four independent waves on alternate 16-key tiles; 32: four
+ * waves on the four quarters of the head dims; 64: two head groups x two dim
+ * halves), or 0 for the automatic choice.  Packed FP8 pools always use 64.
+ * Process-wide.
  */
 dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads);
 

@@ -167,7 +167,7 @@ def test_plan_is_host_only_and_sane():
     assert c.value == 64 and s.value == 10
     assert L.dsv4_attn_set_split_keys(0) == 0
     h = ctypes.c_int32()
-    # 32 rows of 64 heads fill a quarter of the chip at most: team kernel (32 heads per workgroup)
+    # 32 rows of 64 heads fill a quarter of the chip at most: the 32-head kernel
     assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
     assert h.value in (32, 64)
     assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
