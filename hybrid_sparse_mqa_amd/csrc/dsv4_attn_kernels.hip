@@ -165,16 +165,31 @@ struct Item {
 
 // Work item of this workgroup (XCD-aware: consecutive items -- the splits of
 // one row -- share an XCD, since workgroups go to the 8 XCDs round robin).
+// Returns false for a spare workgroup of the rounded-up grid, whose item is
+// clamped into range so that it can issue its first loads like the others
+// before leaving (no branch splits the kernel-argument loads).
 __device__ __forceinline__ bool decode_item(const AttnArgs& a, Item& it) {
     const int per_xcd = (a.n_items + 7) >> 3;
     const int slot_in_xcd = blockIdx.x >> 3;
-    const int item = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
-    if (slot_in_xcd >= per_xcd || item >= a.n_items) return false;
+    const int raw = (blockIdx.x & 7) * per_xcd + slot_in_xcd;
+    const bool live = slot_in_xcd < per_xcd && raw < a.n_items;
+    const int item = min(raw, a.n_items - 1);
     it.s = item % a.splits;
     const int th = item / a.splits;
     it.hb = th % a.head_blocks;
     it.t = th / a.head_blocks;
-    return true;
+    return live;
+}
+
+// The kernel arguments that the first round of loads depends on, made
+// available at one point so that they arrive in one round of scalar loads
+// (left to itself the compiler fetches them in several dependent rounds, each
+// a memory round trip before the loads that need it can go out).
+__device__ __forceinline__ void fetch_args(const AttnArgs& a) {
+    asm volatile("" ::"s"(a.m.seq_lens), "s"(a.m.qo_indptr), "s"(a.m.c4), "s"(a.m.c4_ld), "s"(a.m.ext_table),
+                 "s"(a.m.ext_ld), "s"(a.m.swa_table), "s"(a.m.swa_ld), "s"(a.m.K), "s"(a.m.B), "s"(a.m.R),
+                 "s"(a.m.W), "s"(a.q), "s"(a.q_s0), "s"(a.q_s1), "s"(a.T), "s"(a.H), "s"(a.chunk), "s"(a.splits),
+                 "s"(a.head_blocks), "s"(a.n_items), "s"(a.ext_pages));
 }
 
 // Q^T as the B operand of S^T: lane holds head (l & 31) of the wave's half,
@@ -300,6 +315,9 @@ __device__ __forceinline__ void build_ext_slots(const AttnArgs& a, const RowKeys
         if (rk.r != pf.r_guess) {  // uniform: the guessed request was wrong
 #pragma unroll
             for (int j = 0; j < kTU; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+            // Wait here, on this path only: otherwise the compiler waits for
+            // every later load (Q) below, on the common path too.
+            wait_vmcnt<0>();
         }
 #pragma unroll
         for (int j = 0; j < kTU; ++j)
@@ -314,6 +332,7 @@ __device__ __forceinline__ void build_ext_slots(const AttnArgs& a, const RowKeys
     if (!cached) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) pg[u] = ext_row[c[u] >= 0 ? min(c[u] >> 8, a.ext_pages - 1) : 0];
+        wait_vmcnt<0>();  // on this path only (see above)
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -678,8 +697,9 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     static_assert(kMaxSplitKeys + kMaxSplitKeys / kTileKeys <= 4 * 64 * 16, "prologue scratch fits buffer 0");
     static_assert(kTableCap <= 4 * 64 * 16, "page-table cache fits buffer 1");
 
+    fetch_args(a);
     Item it;
-    if (!decode_item(a, it)) return;
+    const bool live = decode_item(a, it);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int hh = w / kGroup, dq = w % kGroup;
@@ -703,6 +723,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         for (int j = 0; j < kSteps; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (!live) return;
     const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
     const int n_here = __builtin_amdgcn_readfirstlane(max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0));
     const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
@@ -991,6 +1012,7 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
     __shared__ int32_t s_table[kTableCap];
     __shared__ float s_ml[4][2][kH];
 
+    fetch_args(a);
     Item it;
     if (!decode_item(a, it)) return;
     const int tid = threadIdx.x;
@@ -1242,6 +1264,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     __shared__ int32_t s_table[kTableCap];
     __shared__ __attribute__((aligned(16))) float s_scale[kTileKeys];
 
+    fetch_args(a);
     Item it;
     if (!decode_item(a, it)) return;
     const int tid = threadIdx.x;
@@ -1378,10 +1401,13 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
 // row's merge costs one round of loads.
 // ---------------------------------------------------------------------------
 // kPass: splits per pass (the smallest of 2, 4, 8, 16 that covers the
-// splits, so no load is wasted on a clamped duplicate; more than 16 splits
-// take several passes).
+// splits, so no load is wasted on a clamped duplicate; only kPass = 16 loops,
+// over more than 16 splits).
 template <int kPass>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+    // Every kernel argument used below, in one round of scalar loads.
+    asm volatile("" ::"s"(a.H), "s"(a.splits), "s"(a.ws_lse), "s"(a.ws_o), "s"(a.sink), "s"(a.zero_row), "s"(a.out),
+                 "s"(a.out_s0), "s"(a.out_s1), "s"(a.lse), "s"(a.lse_s0));
     const int t = blockIdx.x;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
@@ -1434,8 +1460,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
             }
         }
     };
-    if (S <= kPass) {
-        pass(0);  // the usual case: one round trip, no loop
+    if constexpr (kPass < 16) {
+        pass(0);  // the launcher picks kPass >= splits: one round trip, no loop
     } else {
         for (int k0 = 0; k0 < S; k0 += kPass) pass(k0);
     }
