@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dsv4_launch.h"
 
 namespace dsv4 {
@@ -756,32 +758,35 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // Copy of one tile: lane p moves 16-byte chunks of row 8w + ((p >> 1) & 7),
-    // at chunk 2*(p >> 4) + ((p & 1) ^ (w & 1)) of each 128-byte line; the
-    // row address comes from pro[] for the first three tiles and from ad[]
-    // (one cross-lane permute) after them.
+    // at chunk 2*(p >> 4) + ((p & 1) ^ (w & 1)) of each 128-byte line, in four
+    // parts of two lines each.  The row address comes from pro[] for the first
+    // three tiles and from ad[] (one cross-lane permute) after them.
     const uint32_t dma_lane_off = 16u * (2u * (l >> 4) + ((l & 1) ^ (w & 1)));
+    auto tile_row = [&](int tile) -> const uint8_t* {  // tile >= 3; past the split: zero rows
+        const int u = min(tile >> 3, kMaxSplitKeys / 256 - 1);
+        const uint64_t au = u == 0 ? ad[0] : (u == 1 ? ad[1] : (u == 2 ? ad[2] : ad[3]));
+        const int src = 4 * (8 * (tile & 7) + dma_row);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
+        return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo) + dma_lane_off;
+    };
+    auto copy_part = [&](const uint8_t* row, int tile, auto part) {
+        constexpr int kP = decltype(part)::value;
+        const uint32_t dst = lds_addr(&s_tile[tile % kStages][0]) + w * 8192 + kP * 2048;
+        dma16_off<256 * kP>(row, dst);
+        dma16_off<256 * kP + 128>(row, dst + 1024);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
     auto fetch_tile = [&](int tile) {
-        uint64_t ra;
-        if (tile < 3) {
-            ra = tile == 0 ? pro[0] : (tile == 1 ? pro[1] : pro[2]);
-        } else {
-            const int u = tile >> 3;
-            const uint64_t au = u == 0 ? ad[0] : (u == 1 ? ad[1] : (u == 2 ? ad[2] : ad[3]));
-            const int src = 4 * (8 * (tile & 7) + dma_row);
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
-            ra = ((uint64_t)hi << 32) | lo;
-        }
-        const uint8_t* row = (const uint8_t*)(uintptr_t)ra + dma_lane_off;
-        const uint32_t dst = lds_addr(&s_tile[tile % kStages][0]) + w * 8192;
-        dma16_off<0>(row, dst);
-        dma16_off<128>(row, dst + 1024);
-        dma16_off<256>(row, dst + 2048);
-        dma16_off<384>(row, dst + 3072);
-        dma16_off<512>(row, dst + 4096);
-        dma16_off<640>(row, dst + 5120);
-        dma16_off<768>(row, dst + 6144);
-        dma16_off<896>(row, dst + 7168);
+        const uint8_t* row = tile < 3 ? (const uint8_t*)(uintptr_t)(tile == 0 ? pro[0] : (tile == 1 ? pro[1] : pro[2])) + dma_lane_off
+                                      : tile_row(tile);
+        copy_part(row, tile, P0{});
+        copy_part(row, tile, P1{});
+        copy_part(row, tile, P2{});
+        copy_part(row, tile, P3{});
     };
 
     // Per-lane LDS bases of the score operand and of the two transposing PV
@@ -879,9 +884,15 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
 
     const float sl2 = a.scale_log2;
     const int key_shift = 4 * khi;  // register r of a score tile: key 8*(r >> 2) + 4*(l >> 5) + (r & 3)
-    for (int i = 0; i < n_tiles; ++i) {
+    // One iteration; kFetch: tile i+3 exists and is requested, its copy split
+    // into four parts spread over the iteration (a burst of copies would hold
+    // the wave at the memory queue), from a row address computed one
+    // iteration ahead.
+    const uint8_t* next_row = tile_row(3);
+    auto iteration = [&](int i, auto fetch_tag) {
+        constexpr bool kFetch = decltype(fetch_tag)::value;
         // This wave's rows of tile i+1 (tile i+2 may still be in flight).
-        if (i + 2 < n_tiles) wait_vmcnt<8>();
+        if (kFetch || i + 2 < n_tiles) wait_vmcnt<8>();
         else wait_vmcnt<0>();
         float* xb = &s_x[i & 1][0];
         {
@@ -890,7 +901,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
             for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
         }
         __syncthreads();  // S partials of tile i published; tile i+1 landed; tile i-1's stage is free
-        if (i + 3 < n_tiles) fetch_tile(i + 3);
+        const uint8_t* row = next_row;
+        if constexpr (kFetch) copy_part(row, i + 3, P0{});
 
         // The other S partials of the head group for tile i and the score
         // operand of tile i+1 (when tile i is the last, that stage holds stale
@@ -905,13 +917,19 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         }
         bf16x8 av[kSteps];
         read_k(i + 1, av);
+        if constexpr (kFetch) copy_part(row, i + 3, P1{});
         // PV of tile i-1 while those reads land; then the PV operand of tile i.
 #pragma unroll
         for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
                 oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
+        if constexpr (kFetch) copy_part(row, i + 3, P2{});
         read_kt(i, kt);
+        if constexpr (kFetch) {
+            copy_part(row, i + 3, P3{});
+            next_row = tile_row(i + 4);
+        }
 
         // Softmax of tile i (base 2, raw scores; the scale is applied in the
         // exponent), interleaved with the score MFMAs of tile i+1.  Register r
@@ -973,7 +991,10 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then VALU
         }
         sacc = snext;
-    }
+    };
+    int i = 0;
+    for (; i + 3 < n_tiles; ++i) iteration(i, std::true_type{});
+    for (; i < n_tiles; ++i) iteration(i, std::false_type{});
     // PV of the last tile.
 #pragma unroll
     for (int mb = 0; mb < kMb; ++mb)
