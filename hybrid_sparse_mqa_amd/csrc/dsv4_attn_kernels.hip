@@ -191,7 +191,7 @@ __device__ __forceinline__ void fetch_args(const AttnArgs& a) {
     asm volatile("" ::"s"(a.m.seq_lens), "s"(a.m.qo_indptr), "s"(a.m.c4), "s"(a.m.c4_ld), "s"(a.m.ext_table),
                  "s"(a.m.ext_ld), "s"(a.m.swa_table), "s"(a.m.swa_ld), "s"(a.m.K), "s"(a.m.B), "s"(a.m.R),
                  "s"(a.m.W), "s"(a.q), "s"(a.q_s0), "s"(a.q_s1), "s"(a.T), "s"(a.H), "s"(a.chunk), "s"(a.splits),
-                 "s"(a.head_blocks), "s"(a.n_items), "s"(a.ext_pages));
+                 "s"(a.head_blocks), "s"(a.n_items), "s"(a.ext_pages), "s"(a.zero_row));
 }
 
 // Q^T as the B operand of S^T: lane holds head (l & 31) of the wave's half,
@@ -272,77 +272,114 @@ __device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk
 // i < n_ext is compressed entry i (C4: c4_indices[t][i], negative = unused;
 // C128: entry i), and i >= n_ext is window position swa_lo + (i - n_ext).
 // (The softmax does not depend on the order; the canonical order of the
-// gather entry point is unchanged.)  The C4 indices of a split depend only on
-// the query row, and the extra page-table row only on the request, so both
-// are requested in the first round of loads, together with the request
-// bounds, for the request a row has when every request has equally many
-// query rows (t * B / T); a wrong guess costs one reload.  Window slots need
-// the row's position, so they come from a second round: one or a few
+// gather entry point is unchanged.)
+//
+// Each lane resolves only the keys whose row addresses it holds: the rows
+// it copies itself for tiles 0..2, and one row of every later tile, which
+// it hands to the copying lane through a cross-lane permute (see
+// lane_key).  The C4 indices of a split depend only on the query row, and
+// the extra page-table row only on the request, so both are requested in the
+// first round of loads, together with the request bounds, for the request a
+// row has when every request has equally many query rows (t * B / T); a
+// wrong guess costs one reload.  C128 entries need no index: the lane loads
+// the page-table entry of each of its keys' pages directly.  Window slots
+// need the row's position, so they come from a second round: one or a few
 // page-table entries at uniform addresses, read with scalar loads, which a
 // wave can wait for without waiting for tile copies already in flight.
-template <int kMaxKeys>
+constexpr int kAdRegs = kMaxSplitKeys / 256;  // permuted row addresses per lane
+constexpr int kLaneKeys = kAdRegs + 3;
+
+// Split-relative key of lane key q of lane l in wave w: q < kAdRegs is row
+// 8w + (l & 7) of tile 8q + (l >> 3); q = kAdRegs + j is the row lane l
+// copies in tile j (row 8w + ((l >> 1) & 7)).
+__device__ __forceinline__ int lane_key(int q, int w, int l) {
+    return q < kAdRegs ? 256 * q + 32 * (l >> 3) + 8 * w + (l & 7) : 32 * (q - kAdRegs) + 8 * w + ((l >> 1) & 7);
+}
+
 struct ExtPrefetch {
-    int32_t c4[kMaxKeys / 256];    // C4 index of list entry k0 + tid + 256*u (clamped into the row)
-    int32_t tab[kTableCap / 256];  // extra page-table entries tid + 256*j of request r_guess
-    int r_guess;
+    int32_t e[kLaneKeys];          // C4: index of each lane key's entry; C128: page-table entry of its page
+    int32_t tab[kTableCap / 256];  // C4: extra page-table entries tid + 256*j
+    int r_guess;                   // the request the page-table loads assume
 };
 
-template <int kMaxKeys>
-__device__ __forceinline__ void prefetch_ext(const AttnArgs& a, int t, int k0, int tid, ExtPrefetch<kMaxKeys>& pf) {
+// Every load is unconditional (from the zero row where the ratio does not
+// need it), so that no branch splits them.
+__device__ __forceinline__ void prefetch_ext(const AttnArgs& a, int t, int k0, int w, int l, int tid, ExtPrefetch& pf) {
     pf.r_guess = min(a.m.B - 1, (int)((int64_t)t * a.m.B / max(a.T, 1)));
-    if (a.m.R == 4) {
-        const int32_t* c4_row = a.m.c4 + (int64_t)t * a.m.c4_ld;
+    const bool c4 = a.m.R == 4, c128 = a.m.R == 128;
+    const bool table = c4 && a.ext_pages <= kTableCap;
+    const int32_t* zero = (const int32_t*)a.zero_row;
+    const int32_t* ext_row = c4 || c128 ? a.m.ext_table + (int64_t)pf.r_guess * a.m.ext_ld : zero;
+    const int32_t* c4_row = c4 ? a.m.c4 + (int64_t)t * a.m.c4_ld : zero;
 #pragma unroll
-        for (int u = 0; u < kMaxKeys / 256; ++u) pf.c4[u] = c4_row[min(k0 + tid + 256 * u, a.m.K - 1)];  // K >= 1
+    for (int q = 0; q < kLaneKeys; ++q) {
+        const int key = k0 + lane_key(q, w, l);
+        const int32_t* src = c4 ? c4_row + min(key, a.m.K - 1) : ext_row + (c128 ? min(key >> 8, a.ext_pages - 1) : 0);
+        pf.e[q] = *src;
     }
-    if (a.m.R != 0 && a.ext_pages <= kTableCap) {
-        const int32_t* ext_row = a.m.ext_table + (int64_t)pf.r_guess * a.m.ext_ld;
+    const int32_t* tab_row = table ? ext_row : zero;
 #pragma unroll
-        for (int j = 0; j < kTableCap / 256; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+    for (int j = 0; j < kTableCap / 256; ++j) {
+        const int32_t* src = tab_row + (table ? min(tid + 256 * j, a.ext_pages - 1) : 0);
+        pf.tab[j] = *src;
     }
 }
 
-// Slots of the split's compressed entries into s_slot[i] (i = list index -
-// k0); window entries are left to the caller.
-template <int kMaxKeys>
-__device__ __forceinline__ void build_ext_slots(const AttnArgs& a, const RowKeys& rk, int k0, int n_here,
-                                                ExtPrefetch<kMaxKeys>& pf, int32_t* s_slot, int32_t* s_table,
-                                                int tid) {
-    constexpr int kU = kMaxKeys / 256;
-    constexpr int kTU = kTableCap / 256;
-    if (a.m.R == 0) return;
-    const bool cached = a.ext_pages <= kTableCap;
+// Row address of every lane key that is a compressed entry of the split; the
+// zero row for unused C4 entries, keys past the split and window keys (which
+// the caller fills in later).  Bit q of valid (q < kAdRegs): the key is used.
+__device__ __forceinline__ void ext_addresses(const AttnArgs& a, const RowKeys& rk, int k0, int n_here, int w,
+                                              int l, int tid, ExtPrefetch& pf, int32_t* s_table,
+                                              uint64_t (&addr)[kLaneKeys], uint32_t& valid) {
     const int32_t* ext_row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
-    if (cached) {
+    int32_t slot[kLaneKeys];
+    valid = 0;
+    if (a.m.R == 128) {
         if (rk.r != pf.r_guess) {  // uniform: the guessed request was wrong
 #pragma unroll
-            for (int j = 0; j < kTU; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+            for (int q = 0; q < kLaneKeys; ++q) pf.e[q] = ext_row[min((k0 + lane_key(q, w, l)) >> 8, a.ext_pages - 1)];
             // Wait here, on this path only: otherwise the compiler waits for
             // every later load (Q) below, on the common path too.
             wait_vmcnt<0>();
         }
 #pragma unroll
-        for (int j = 0; j < kTU; ++j)
-            if (tid + 256 * j < a.ext_pages) s_table[tid + 256 * j] = pf.tab[j];
-    }
-    int32_t c[kU];
+        for (int q = 0; q < kLaneKeys; ++q) slot[q] = pf.e[q] * kPage + ((k0 + lane_key(q, w, l)) & (kPage - 1));
+    } else if (a.m.R == 4) {
+        if (a.ext_pages <= kTableCap) {  // uniform: the request's table goes through LDS
+            if (rk.r != pf.r_guess) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) c[u] = a.m.R == 4 ? pf.c4[u] : k0 + tid + 256 * u;
-    __syncthreads();  // s_table ready
-    // A table too long for LDS: one more round of (clamped) loads.
-    int32_t pg[kU] = {};
-    if (!cached) {
+                for (int j = 0; j < kTableCap / 256; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+                wait_vmcnt<0>();  // on this path only (see above)
+            }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) pg[u] = ext_row[c[u] >= 0 ? min(c[u] >> 8, a.ext_pages - 1) : 0];
-        wait_vmcnt<0>();  // on this path only (see above)
+            for (int j = 0; j < kTableCap / 256; ++j)
+                if (tid + 256 * j < a.ext_pages) s_table[tid + 256 * j] = pf.tab[j];
+            __syncthreads();  // s_table ready
+            int32_t pg[kLaneKeys];  // read unconditionally (clamped), so that the reads go out together
+#pragma unroll
+            for (int q = 0; q < kLaneKeys; ++q) pg[q] = s_table[pf.e[q] >= 0 ? min(pf.e[q] >> 8, a.ext_pages - 1) : 0];
+#pragma unroll
+            for (int q = 0; q < kLaneKeys; ++q) slot[q] = pf.e[q] < 0 ? -1 : pg[q] * kPage + (pf.e[q] & (kPage - 1));
+        } else {  // a table too long for LDS: one more round of (clamped) loads
+            int32_t pg[kLaneKeys];
+#pragma unroll
+            for (int q = 0; q < kLaneKeys; ++q) pg[q] = ext_row[pf.e[q] >= 0 ? min(pf.e[q] >> 8, a.ext_pages - 1) : 0];
+            wait_vmcnt<0>();  // on this path only (see above)
+#pragma unroll
+            for (int q = 0; q < kLaneKeys; ++q) slot[q] = pf.e[q] < 0 ? -1 : pg[q] * kPage + (pf.e[q] & (kPage - 1));
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kLaneKeys; ++q) slot[q] = -1;
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        const int i = tid + 256 * u;
-        if (i < n_here && k0 + i < rk.n_ext)
-            s_slot[i] = c[u] < 0 ? -1 : (cached ? s_table[c[u] >> 8] : pg[u]) * kPage + (c[u] & (kPage - 1));
+    for (int q = 0; q < kLaneKeys; ++q) {
+        const int key = lane_key(q, w, l);
+        const bool ext = key < n_here && k0 + key < rk.n_ext;
+        addr[q] = ext && slot[q] >= 0 ? (uint64_t)(uintptr_t)(a.ext_pool + (int64_t)slot[q] * a.ext_row_bytes)
+                                      : (uint64_t)(uintptr_t)a.zero_row;
+        if (q < kAdRegs && key < n_here && (!ext || slot[q] >= 0)) valid |= 1u << q;  // window keys are always used
     }
-    __syncthreads();  // compressed slots ready
 }
 
 // Page-table entries of the window pages a split touches: pages pg_lo ..
@@ -382,22 +419,6 @@ __device__ __forceinline__ void wait_swa_pages(SwaPages& sp) {
                  : "+s"(sp.e[0]), "+s"(sp.e[1]), "+s"(sp.e[2]), "+s"(sp.e[3]), "+s"(sp.e[4])
                  :
                  : "memory");
-}
-
-// bf16 kernel: the row address of every key [k0, k0 + n_here) of the split
-// (zero_row for unused C4 entries and for the padding up to the last tile),
-// built once so that copying a tile needs no address arithmetic.
-__device__ __forceinline__ void build_row_addresses(const AttnArgs& a, const RowKeys& rk, int k0, int n_here,
-                                                    const int32_t* s_slot, uint64_t* s_addr, int tid) {
-    const int n_pad = (n_here + kTileKeys - 1) / kTileKeys * kTileKeys;
-    for (int i = tid; i < n_pad; i += 256) {
-        const int32_t slot = i < n_here ? s_slot[i] : -1;
-        const bool swa = k0 + i < rk.n_swa;
-        const uint8_t* row = slot >= 0 ? (swa ? a.swa_pool : a.ext_pool) + (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes)
-                                       : a.zero_row;
-        s_addr[i] = (uint64_t)(uintptr_t)row;
-    }
-    __syncthreads();
 }
 
 // Sum the S^T partials of the two waves that share a head half (they cover
@@ -693,10 +714,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     constexpr int kHeads = 32 * kHH;          // heads per workgroup
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) float s_x[2][4 * 64 * 16];
-    int32_t* s_slot = (int32_t*)&s_x[0][0];                // kMaxSplitKeys entries, prologue only
-    uint32_t* s_mask = (uint32_t*)&s_x[0][kMaxSplitKeys];  // one 32-key mask per tile, prologue only
-    int32_t* s_table = (int32_t*)&s_x[1][0];               // kTableCap entries, prologue only
-    static_assert(kMaxSplitKeys + kMaxSplitKeys / kTileKeys <= 4 * 64 * 16, "prologue scratch fits buffer 0");
+    uint32_t* s_mask = (uint32_t*)&s_x[0][0];  // one 32-key mask per tile, prologue only
+    int32_t* s_table = (int32_t*)&s_x[1][0];   // kTableCap entries, prologue only
     static_assert(kTableCap <= 4 * 64 * 16, "page-table cache fits buffer 1");
 
     fetch_args(a);
@@ -711,8 +730,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     // issued last so that waiting for the metadata does not wait for it).
     const RequestChunk rc = load_requests(a.m, 0, l);
     const int k0 = it.s * a.chunk;
-    ExtPrefetch<kMaxSplitKeys> pf;
-    prefetch_ext(a, it.t, k0, tid, pf);
+    ExtPrefetch pf;
+    prefetch_ext(a, it.t, k0, w, l, tid, pf);
     __builtin_amdgcn_sched_barrier(0);
     // Q^T as the B operand of the scores: lane holds head (l & 31) of the
     // wave's head group, dims kDims*dq + 16*j + 8*(l >> 5) .. +8 of k-step j.
@@ -729,7 +748,6 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
     const int n_here = __builtin_amdgcn_readfirstlane(max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0));
     const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
-    build_ext_slots(a, rk, k0, n_here, pf, s_slot, s_table, tid);
 
     // Row addresses of the keys this wave copies: tile j, row 8w + e sits in
     // lane (8j + e) & 63 of ad[(8j + e) >> 6]; and, for the first three
@@ -737,19 +755,24 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     // copies need no cross-lane step.  Unused keys read the zero row; window
     // keys are filled in once their page entries have arrived.
     const int dma_row = (l >> 1) & 7;
-    auto ext_addr = [&](int key) -> uint64_t {
-        const int32_t slot = key < n_here && k0 + key < rk.n_ext ? s_slot[key] : -1;
-        return slot >= 0 ? (uint64_t)(uintptr_t)(a.ext_pool + (int64_t)slot * a.ext_row_bytes)
-                         : (uint64_t)(uintptr_t)a.zero_row;
-    };
-    uint64_t ad[kMaxSplitKeys / 256], pro[3];
+    uint64_t ad[kAdRegs], pro[3];
+    {
+        uint64_t addr[kLaneKeys];
+        uint32_t valid;
+        ext_addresses(a, rk, k0, n_here, w, l, tid, pf, s_table, addr, valid);
 #pragma unroll
-    for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
-        const int idx = 64 * u + l;
-        ad[u] = ext_addr(kTileKeys * (idx >> 3) + 8 * w + (idx & 7));
+        for (int u = 0; u < kAdRegs; ++u) ad[u] = addr[u];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) pro[j] = addr[kAdRegs + j];
+        // Valid-key mask of every tile (byte w of word j: rows 8w .. 8w+7 of
+        // tile j), published by the barrier before the first tile.
+        uint8_t* s_mask8 = (uint8_t*)s_mask;
+#pragma unroll
+        for (int u = 0; u < kAdRegs; ++u) {
+            const uint64_t b = __ballot((valid >> u) & 1u);
+            if (l < 8) s_mask8[4 * (8 * u + l) + w] = (uint8_t)(b >> (8 * l));
+        }
     }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) pro[j] = ext_addr(kTileKeys * j + 8 * w + dma_row);
     // Round 2 (window pages, scalar loads), issued after the last LDS access
     // above and waited for after the first copies below (nothing in between
     // touches LDS).
@@ -838,6 +861,13 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     // Tiles made of compressed entries only are requested right away.
     const int n_first = min(n_tiles, 3);
     const int n_early = min(n_first, max(0, rk.n_ext - k0) / kTileKeys);
+    // Q has arrived by now (it was requested with the first metadata, a few
+    // round trips ago).  Waiting for it here, before any tile copy (which the
+    // compiler does not see), lets the compiler know it is in registers;
+    // otherwise it would wait for it again before every score product of the
+    // loop, and such a wait, counting the copies issued after Q as well,
+    // would stall on the tiles still in flight.
+    wait_vmcnt<0>();
     for (int j = 0; j < n_early; ++j) fetch_tile(j);
     __builtin_amdgcn_sched_barrier(0);
     wait_swa_pages(swp);
@@ -853,7 +883,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
             return (uint64_t)(uintptr_t)(a.swa_pool + ((int64_t)e * kPage + (x & (kPage - 1))) * a.swa_row_bytes);
         };
 #pragma unroll
-        for (int u = 0; u < kMaxSplitKeys / 256; ++u) {
+        for (int u = 0; u < kAdRegs; ++u) {
             const int idx = 64 * u + l;
             ad[u] = swa_addr(kTileKeys * (idx >> 3) + 8 * w + (idx & 7), ad[u]);
         }
@@ -861,14 +891,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         for (int j = 0; j < 3; ++j) pro[j] = swa_addr(kTileKeys * j + 8 * w + dma_row, pro[j]);
     }
     for (int j = n_early; j < n_first; ++j) fetch_tile(j);
-    // Valid-key mask of every tile: window keys are always valid.
-    for (int j = w; j < n_tiles; j += 4) {
-        const int key = kTileKeys * j + (l & 31);
-        const bool valid = key < n_here && (k0 + key >= rk.n_ext || s_slot[key] >= 0);
-        const uint64_t b = __ballot(l < 32 && valid);
-        if (l == 0) s_mask[j] = (uint32_t)b;
-    }
-    __syncthreads();
+    __syncthreads();  // tile masks published
     const uint32_t tile_mask = s_mask[l & 31];  // lane j: valid keys of tile j
     f32x16 sacc = f32x16{};
     if (n_tiles > 0) {
@@ -902,62 +925,47 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         }
         __syncthreads();  // S partials of tile i published; tile i+1 landed; tile i-1's stage is free
         const uint8_t* row = next_row;
-        if constexpr (kFetch) copy_part(row, i + 3, P0{});
+        if constexpr (kFetch) next_row = tile_row(i + 4);
 
-        // The other S partials of the head group for tile i and the score
-        // operand of tile i+1 (when tile i is the last, that stage holds stale
-        // rows whose scores are discarded).
-        f32x4 part[kGroup][4];
+        // The other S partials of the head group for tile i (the waves that
+        // hold the other dim slices: dq ^ 1, and for four slices dq ^ 2 and
+        // dq ^ 3) and the score operand of tile i+1 (when tile i is the last,
+        // that stage holds stale rows whose scores are discarded).
+        f32x4 part[kGroup - 1][4];
 #pragma unroll
-        for (int v = 0; v < kGroup; ++v) {
-            if (v == dq) continue;
-            const f32x4* op = (const f32x4*)xb + (hh * kGroup + v) * 256 + l;
+        for (int v = 1; v < kGroup; ++v) {
+            const f32x4* op = (const f32x4*)xb + (hh * kGroup + (dq ^ v)) * 256 + l;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) part[v][q] = op[64 * q];
+            for (int q = 0; q < 4; ++q) part[v - 1][q] = op[64 * q];
         }
         bf16x8 av[kSteps];
         read_k(i + 1, av);
-        if constexpr (kFetch) copy_part(row, i + 3, P1{});
-        // PV of tile i-1 while those reads land; then the PV operand of tile i.
+        if constexpr (kFetch) copy_part(row, i + 3, P0{});
+
+        // PV of tile i-1 (operands from the previous iteration), interleaved
+        // with the first half of tile i's softmax.  Register r of a score tile
+        // holds head (l & 31), key 8*(r >> 2) + 4*(l >> 5) + (r & 3); lanes l and
+        // l ^ 32 hold the two halves of a head's keys.  The scores of the head
+        // group are the sum of its dim slices' partials, added pairwise
+        // ((slices 0+1) + (slices 2+3)) so that every wave of the group gets
+        // the same value (each addition is commutative).
 #pragma unroll
         for (int mb = 0; mb < kMb; ++mb)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
                 oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], pb[pp], oacc[mb], 0, 0, 0);
-        if constexpr (kFetch) copy_part(row, i + 3, P2{});
-        read_kt(i, kt);
-        if constexpr (kFetch) {
-            copy_part(row, i + 3, P3{});
-            next_row = tile_row(i + 4);
-        }
-
-        // Softmax of tile i (base 2, raw scores; the scale is applied in the
-        // exponent), interleaved with the score MFMAs of tile i+1.  Register r
-        // holds head (l & 31), key 8*(r >> 2) + 4*(l >> 5) + (r & 3); lanes l and
-        // l ^ 32 hold the two halves of a head's keys.  The running reference
-        // m_run (scaled units) moves only when a score exceeds it by more than
-        // 2^8 (probabilities stay <= 256), so the accumulators are rescaled on
-        // few tiles; l_run is this lane's share of the denominator, the two
-        // shares are added in write_result.
-        f32x16 snext = f32x16{};
-#pragma unroll
-        for (int j = 0; j < kSteps / 2; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
-        // Sum of the group's partials in wave order (this wave's own from
-        // its registers), identical in every wave of the group.
         float sv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float x = 0.f;
-#pragma unroll
-            for (int v = 0; v < kGroup; ++v) {
-                const float pv = v == dq ? sacc[r] : part[v][r >> 2][r & 3];
-                x = v == 0 ? pv : x + pv;
+            const float own = sacc[r] + part[0][r >> 2][r & 3];
+            if constexpr (kGroup == 2) {
+                sv[r] = own;
+            } else {
+                sv[r] = own + (part[1][r >> 2][r & 3] + part[2][r >> 2][r & 3]);
             }
-            sv[r] = x;
         }
-        const uint32_t tmask = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i);
-        if (tmask != 0xFFFFFFFFu) {
-            const uint32_t mine = tmask >> key_shift;
+        {
+            const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i) >> key_shift;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sv[r] = ((mine >> (8 * (r >> 2) + (r & 3))) & 1u) ? sv[r] : -INFINITY;
         }
@@ -965,6 +973,18 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 1; r < 16; ++r) smax = fmaxf(smax, sv[r]);
         const float tmax = smax * sl2;  // scale > 0: the maximum commutes with it
+#pragma unroll
+        for (int j = 0; j < 2 * kMb; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // then VALU / transcendental
+        }
+        if constexpr (kFetch) copy_part(row, i + 3, P1{});
+
+        // The running reference m_run (scaled units) moves only when a score
+        // exceeds it by more than 2^8 (probabilities stay <= 256), so the
+        // accumulators are rescaled on few tiles (after the PV product above,
+        // which used the old reference); l_run is this lane's share of the
+        // denominator, the two shares are added in write_result.
         if (__any(tmax > m_run + kRescaleLog2)) {
             const float hmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the head's tile maximum
             const bool grow = hmax > m_run + kRescaleLog2;
@@ -974,6 +994,18 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
             l_run *= alpha;
             m_run = m_target;
         }
+        // The PV operand of tile i (its stage is read for the last time).
+        read_kt(i, kt);
+        if constexpr (kFetch) {
+            copy_part(row, i + 3, P2{});
+            copy_part(row, i + 3, P3{});
+        }
+
+        // Second half of the softmax (base 2, raw scores; the scale is applied
+        // in the exponent), interleaved with the score MFMAs of tile i+1.
+        f32x16 snext = f32x16{};
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
         const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
         float psum = 0.f;
 #pragma unroll
@@ -984,11 +1016,9 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         }
         l_run += psum;
 #pragma unroll
-        for (int j = kSteps / 2; j < kSteps; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < kSteps / 2; ++j) {
+        for (int j = 0; j < kSteps; ++j) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then VALU
+            __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // then VALU / transcendental
         }
         sacc = snext;
     };

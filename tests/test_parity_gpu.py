@@ -91,6 +91,16 @@ def test_gather_workloads_bit_exact(orc, n):
     check_gather(orc, make_config(n))
 
 
+@pytest.fixture
+def heads_per_workgroup(request):
+    """Force one bf16 kernel variant for the test, then restore the automatic choice."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_heads_per_workgroup
+
+    dsv4_attn_set_heads_per_workgroup(request.param)
+    yield request.param
+    dsv4_attn_set_heads_per_workgroup(0)
+
+
 def widen_extra_table(case, pages):
     """Pad each request's extra page-table row to `pages` columns with the
     poison page: the keys do not change, but the row no longer fits the
@@ -101,14 +111,15 @@ def widen_extra_table(case, pages):
     return dataclasses.replace(case, extra_page_table=wide)
 
 
+@pytest.mark.parametrize("heads_per_workgroup", [0, 16, 32, 64], indirect=True)
 @pytest.mark.parametrize("i", [9, 12, 14, 17])
-def test_extra_table_wider_than_lds_copy(orc, i):
+def test_extra_table_wider_than_lds_copy(orc, i, heads_per_workgroup):
     case = widen_extra_table(small_case(i), 1100)
-    log(f"wide extra table {SMALL_IDS[i]}")
+    log(f"wide extra table {SMALL_IDS[i]} heads/workgroup={heads_per_workgroup}")
     check_gather(orc, case)
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
-    G.compare(out, lse, ro, rl, what=f"wide-{SMALL_IDS[i]}")
+    G.compare(out, lse, ro, rl, what=f"wide-{SMALL_IDS[i]}-hpw{heads_per_workgroup}")
 
 
 # --------------------------------------------------------------------------
@@ -121,16 +132,6 @@ def test_forward_small(orc, i):
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
     G.compare(out, lse, ro, rl, what=SMALL_IDS[i])
-
-
-@pytest.fixture
-def heads_per_workgroup(request):
-    """Force one bf16 kernel variant for the test, then restore the automatic choice."""
-    from hybrid_sparse_mqa_amd import dsv4_attn_set_heads_per_workgroup
-
-    dsv4_attn_set_heads_per_workgroup(request.param)
-    yield request.param
-    dsv4_attn_set_heads_per_workgroup(0)
 
 
 @pytest.mark.parametrize("heads_per_workgroup", [16, 32, 64], indirect=True)
