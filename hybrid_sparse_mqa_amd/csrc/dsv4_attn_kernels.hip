@@ -1332,27 +1332,25 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
     build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
 
+    // Loads of one tile: lane l < 56 takes codes 8l .. 8l+7 of each record
+    // (in the low 8 bytes of a 16-byte load that stays inside the record),
+    // lanes 56..63 the rotary dims 8(l-56) .. +8; every lane also loads the
+    // key's scale.  Unused keys read the zero row (codes, rotary dims and
+    // scale all zero), so no load sits under a branch and all of them are in
+    // flight together.
     TileRegs pre;
     auto issue_loads = [&](int tb) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int i = tb + group_key(w, e);
             const int32_t slot = i < n_here ? s_slot[i] : -1;
-            pre.v[e] = u32x4{0u, 0u, 0u, 0u};
-            pre.sc[e] = 0.f;
-            if (slot >= 0) {
-                const bool swa = k0 + i < rk.n_swa;
-                const uint8_t* page = (swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
-                const int rec = slot & 255;
-                const uint8_t* row = page + rec * kFp8RecBytes;
-                if (l < 56) {
-                    const u32x2 c = *(const u32x2*)(row + 8 * l);
-                    pre.v[e] = u32x4{c[0], c[1], 0u, 0u};
-                } else {
-                    pre.v[e] = *(const u32x4*)(row + kNope + 16 * (l - 56));
-                }
-                pre.sc[e] = *(const float*)(page + kFp8ScaleOffset + 4 * rec);
-            }
+            const bool swa = k0 + i < rk.n_swa;
+            const uint8_t* page = (swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
+            const int rec = slot & 255;
+            const uint8_t* row = slot >= 0 ? page + rec * kFp8RecBytes : a.zero_row;
+            const uint8_t* scp = slot >= 0 ? page + kFp8ScaleOffset + 4 * rec : a.zero_row;
+            pre.v[e] = *(const u32x4*)(row + (l < 56 ? 8 * l : kNope + 16 * (l - 56)));
+            pre.sc[e] = *(const float*)scp;
         }
     };
 
