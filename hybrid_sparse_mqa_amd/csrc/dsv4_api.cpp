@@ -324,8 +324,11 @@ hipEvent_t take_event() {
         g_event_pool.pop_back();
         return e;
     }
+    // Timing only: no system-scope fence when the event is recorded (such a
+    // fence writes back and invalidates the caches, which would both stretch
+    // the interval and slow the kernel that follows).
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 

@@ -195,8 +195,10 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
  * Kernel timing on the caller's stream with HIP events.  While enabled, every
  * dsv4_attn_forward records an event before the split kernel, one between it
  * and the merge kernel, and one after the merge kernel (which only runs when
- * a row is split).  Calls made while the stream is being captured into a HIP
- * graph record external event nodes instead, re-recorded on every replay.
+ * a row is split).  The events are timing-only (created without the
+ * system-scope fence on record), so they neither flush caches nor stall the
+ * work that follows.  Calls made while the stream is being captured into a
+ * HIP graph record external event nodes instead, re-recorded on every replay.
  * dsv4_attn_timing_read waits for the recorded events and returns the summed
  * milliseconds of the split kernels and of the merge kernels (either pointer
  * may be NULL) and the number of calls recorded, then clears the record; for
