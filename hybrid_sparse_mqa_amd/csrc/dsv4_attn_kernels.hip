@@ -598,22 +598,32 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Item& it, 
     }
     __syncthreads();
     // Wave (hh, dq) stores rows kRows*dq .. +kRows of its head group; lane l
-    // moves the row's 16-byte chunk l.
-#pragma unroll 4
+    // moves the row's 16-byte chunk l.  All LDS reads go out first, then the
+    // stores (rows of heads past H are skipped), so that no store waits for
+    // the next read.
+    u32x4 v[kRows];
+#pragma unroll
     for (int e = 0; e < kRows; ++e) {
         const int r = kRows * dq + e;
-        const int head = it.hb * 32 * kHH + hh * 32 + r;
-        if (head >= a.H) break;
-        const u32x4 v = *(const u32x4*)(stage + r * 1024 + 16 * (l ^ r));
-        // Streaming stores: nothing in this kernel reads these rows again.
-        if (a.splits == 1) {
-            uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head * a.out_s1 + 8 * l;
-            __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)orow);  // out rows need only 8-byte alignment
-            __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(orow + 4));
-        } else {
-            const int64_t part = ((int64_t)it.t * a.splits + it.s) * a.H + head;
-            __builtin_nontemporal_store(v, (u32x4*)(a.ws_o + part * kHeadDim + 8 * l));
+        v[e] = *(const u32x4*)(stage + r * 1024 + 16 * (l ^ r));
+    }
+    const int head0 = it.hb * 32 * kHH + hh * 32 + kRows * dq;
+    const int n_rows = min(kRows, a.H - head0);  // uniform
+    // Streaming stores: nothing in this kernel reads these rows again.
+    if (a.splits == 1) {
+        uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head0 * a.out_s1 + 8 * l;
+#pragma unroll
+        for (int e = 0; e < kRows; ++e) {
+            if (e < n_rows) {
+                __builtin_nontemporal_store(u32x2{v[e][0], v[e][1]}, (u32x2*)(orow + e * a.out_s1));  // 8-byte aligned rows
+                __builtin_nontemporal_store(u32x2{v[e][2], v[e][3]}, (u32x2*)(orow + e * a.out_s1 + 4));
+            }
         }
+    } else {
+        uint16_t* prow = a.ws_o + (((int64_t)it.t * a.splits + it.s) * a.H + head0) * kHeadDim + 8 * l;
+#pragma unroll
+        for (int e = 0; e < kRows; ++e)
+            if (e < n_rows) __builtin_nontemporal_store(v[e], (u32x4*)(prow + e * kHeadDim));
     }
     if (head_ok && dq == 0 && l < 32) {
         if (a.splits == 1) {
@@ -1324,9 +1334,9 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
     const bool head_ok = my_head < a.H;
 
-    bf16x8 qf[16];
-    load_q(a, it.t, my_head, dh, l, qf);
-
+    // Q is requested with the first tile's rows (below), not before the
+    // metadata: loads complete in order, so every wait on the chain request
+    // bounds -> slot list -> first tile would otherwise wait for Q as well.
     const RowKeys rk = row_keys(a.m, it.t, l);
     const int k0 = it.s * a.chunk;
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
@@ -1384,6 +1394,12 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     if (n_here > 0) issue_loads(0);
+    bf16x8 qf[16];
+    load_q(a, it.t, my_head, dh, l, qf);
+    // Tile 0 and Q are both needed before the first product; waiting for
+    // them here tells the compiler Q is in, so that it does not wait for Q
+    // (and for the next tile's loads issued after it) inside the loop.
+    wait_vmcnt<0>();
     for (int tb = 0; tb < n_here; tb += kTileKeys) {
         commit_tile();
         if (tb + kTileKeys < n_here) issue_loads(tb + kTileKeys);
