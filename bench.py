@@ -39,11 +39,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_mqa_amd", "csrc", f)
 
 
 
-def split_kernel_name(kv: str, heads_per_workgroup: int) -> str:
+# Split-kernel variant (DSV4_KERNEL_* of dsv4_attn_plan) -> (name as rocprofv3 prints it, heads per workgroup).
+SPLIT_KERNELS = {1: ("attn_narrow_kernel", 16), 2: ("attn_wide_kernel<1>", 32), 3: ("attn_ws_kernel<1>", 32),
+                 4: ("attn_wide_kernel<2>", 64), 5: ("attn_fp8_kernel", 64)}
+
+
+def split_kernel_name(kernel: int) -> str:
     """Name (as rocprofv3 prints it) of the split kernel that runs."""
-    if kv == "fp8":
-        return "attn_fp8_kernel"
-    return {16: "attn_narrow_kernel", 32: "attn_wide_kernel<1>", 64: "attn_wide_kernel<2>"}[heads_per_workgroup]
+    return SPLIT_KERNELS[kernel][0]
+
 
 def kernel_sha() -> str:
     h = hashlib.sha256()
@@ -169,10 +173,10 @@ def record_traffic(config: int, split_keys: int, fetch_dir: str, write_dir: str,
     case = make_config(config)
     from hybrid_sparse_mqa_amd import dsv4_attn_plan
 
-    _, _, hpw = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
+    _, _, kernel = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
                                0 if case.extra_page_table is None else case.extra_page_table.shape[1],
                                kv_fp8=case.kv == "fp8")
-    name = split_kernel_name(case.kv, hpw)
+    name = split_kernel_name(kernel)
 
     def pick(d, key):
         hits = {k: v for k, v in d.items() if key in k}
@@ -277,7 +281,7 @@ def main() -> int:
 
     if args.split_keys:
         dsv4_attn_set_split_keys(args.split_keys)
-    splits, chunk, heads_per_wg = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
+    splits, chunk, kernel = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
                                    0 if case.extra_page_table is None else case.extra_page_table.shape[1],
                                    kv_fp8=case.kv == "fp8")
 
@@ -350,7 +354,7 @@ def main() -> int:
     merge_avg_ms = merge_ms / calls
     kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
     achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
-    kernel_name = split_kernel_name(case.kv, heads_per_wg)
+    kernel_name = split_kernel_name(kernel)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -372,7 +376,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": dict(describe_workload(args.config, case), splits=int(splits), keys_per_split=int(chunk),
-                       heads_per_workgroup=int(heads_per_wg),
+                       heads_per_workgroup=SPLIT_KERNELS[kernel][1], split_kernel=kernel_name,
                        input_sets=int(n_sets), cache="cold-rotated" if cold else "warm-rotated",
                        timed="HIP graph replay", parallelism="single GPU"),
         "path": {

@@ -10,7 +10,7 @@ from .api import (  # noqa: F401
     dsv4_attn_forward,
     dsv4_attn_gather_slots,
     dsv4_attn_plan,
-    dsv4_attn_set_heads_per_workgroup,
+    dsv4_attn_set_kernel,
     dsv4_attn_set_split_keys,
     dsv4_attn_timing_enable,
     dsv4_attn_timing_read,

@@ -67,8 +67,8 @@ def load() -> ctypes.CDLL:
         L.dsv4_attn_workspace_release.restype = None
         L.dsv4_attn_set_split_keys.restype = ctypes.c_int
         L.dsv4_attn_set_split_keys.argtypes = [ctypes.c_int32]
-        L.dsv4_attn_set_heads_per_workgroup.restype = ctypes.c_int
-        L.dsv4_attn_set_heads_per_workgroup.argtypes = [ctypes.c_int32]
+        L.dsv4_attn_set_kernel.restype = ctypes.c_int
+        L.dsv4_attn_set_kernel.argtypes = [ctypes.c_int32]
         L.dsv4_attn_plan.restype = ctypes.c_int
         L.dsv4_attn_plan.argtypes = [ctypes.c_int32] * 7 + [ctypes.POINTER(ctypes.c_int32)] * 3
         L.dsv4_attn_timing_enable.restype = ctypes.c_int

@@ -92,21 +92,26 @@ def dsv4_attn_set_split_keys(keys_per_split: int) -> None:
     N.check(N.load().dsv4_attn_set_split_keys(int(keys_per_split)))
 
 
-def dsv4_attn_set_heads_per_workgroup(heads: int) -> None:
-    N.check(N.load().dsv4_attn_set_heads_per_workgroup(int(heads)))
+# Split-kernel variants (DSV4_KERNEL_* in dsv4_attn.h) and their heads per workgroup.
+KERNEL_AUTO, KERNEL_H16, KERNEL_H32, KERNEL_H32_ROLES, KERNEL_H64, KERNEL_FP8 = range(6)
+KERNEL_HEADS = {KERNEL_H16: 16, KERNEL_H32: 32, KERNEL_H32_ROLES: 32, KERNEL_H64: 64, KERNEL_FP8: 64}
+
+
+def dsv4_attn_set_kernel(kernel: int) -> None:
+    N.check(N.load().dsv4_attn_set_kernel(int(kernel)))
 
 
 def dsv4_attn_plan(num_rows, num_heads, compress_ratio, window, c4_width=0, extra_pages=0,
                    kv_fp8=False) -> Tuple[int, int, int]:
-    """(splits per row and head block, keys per split, heads per workgroup)
+    """(splits per row and head block, keys per split, split-kernel variant)
     that dsv4_attn_forward would use."""
     s = ctypes.c_int32()
     c = ctypes.c_int32()
-    h = ctypes.c_int32()
+    k = ctypes.c_int32()
     N.check(N.load().dsv4_attn_plan(int(num_rows), int(num_heads), int(compress_ratio), int(window), int(c4_width),
                                     int(extra_pages), int(bool(kv_fp8)), ctypes.byref(s), ctypes.byref(c),
-                                    ctypes.byref(h)))
-    return s.value, c.value, h.value
+                                    ctypes.byref(k)))
+    return s.value, c.value, k.value
 
 
 def dsv4_attn_workspace_reserve(nbytes: int) -> None:

@@ -181,7 +181,7 @@ struct DeviceState {
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
 int32_t g_force_split_keys = 0;
-int32_t g_force_heads_per_workgroup = 0;  // 0: automatic; 32 or 64 for bf16 pools
+int32_t g_force_kernel = DSV4_KERNEL_AUTO;  // bf16 pools only
 
 DeviceState* device_state(int dev) {
     if (dev < 0) return nullptr;
@@ -235,18 +235,42 @@ dsv4_status ensure_zero_row(DeviceState* d) {
 // no split).
 Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
     if (fp8) return Layout::kFp8;
-    if (g_force_heads_per_workgroup == kWide32HeadsPerBlock) return Layout::kWide32;
-    if (g_force_heads_per_workgroup == kWideHeadsPerBlock) return Layout::kWide;
-    if (g_force_heads_per_workgroup == kNarrowHeadsPerBlock) return Layout::kNarrow;
+    switch (g_force_kernel) {
+        case DSV4_KERNEL_H16: return Layout::kNarrow;
+        case DSV4_KERNEL_H32: return Layout::kWide32;
+        case DSV4_KERNEL_H32_ROLES: return Layout::kRoles32;
+        case DSV4_KERNEL_H64: return Layout::kWide;
+        default: break;
+    }
     if (H <= kNarrowHeadsPerBlock) return Layout::kNarrow;
+    // Enough rows for one 32-head workgroup per compute unit without
+    // splitting keys: the score/PV role kernel, whose tile loop is the
+    // fastest and which then needs no merge (measured on C4 verify, 128 rows
+    // x 64 heads).  Otherwise 64-head blocks when rows x splits fill the chip
+    // with splits of at least a few tiles, else 32-head blocks (measured: C128
+    // decode, 64 rows; C4 decode, 32 rows).
+    if ((int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) >= cus) return Layout::kRoles32;
     const int64_t wide_rows = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
     return wide_rows * 4 < cus ? Layout::kWide32 : Layout::kWide;
 }
 
 int32_t heads_per_block(Layout layout) {
-    return layout == Layout::kWide32
-               ? kWide32HeadsPerBlock
-               : (layout == Layout::kNarrow ? kNarrowHeadsPerBlock : kWideHeadsPerBlock);
+    switch (layout) {
+        case Layout::kWide32:
+        case Layout::kRoles32: return kWide32HeadsPerBlock;
+        case Layout::kNarrow: return kNarrowHeadsPerBlock;
+        default: return kWideHeadsPerBlock;
+    }
+}
+
+int32_t kernel_id(Layout layout) {
+    switch (layout) {
+        case Layout::kNarrow: return DSV4_KERNEL_H16;
+        case Layout::kWide32: return DSV4_KERNEL_H32;
+        case Layout::kRoles32: return DSV4_KERNEL_H32_ROLES;
+        case Layout::kWide: return DSV4_KERNEL_H64;
+        default: return DSV4_KERNEL_FP8;
+    }
 }
 
 // Keys per LDS tile and most keys per split of each split kernel.
@@ -290,7 +314,7 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
 
 // ---- timing -------------------------------------------------------------------
 // e0 before the split kernel, e1 between it and the merge kernel, e2 after
-// the merge kernel (e1 == e2 in time when no row is split).
+// the merge kernel (none when no row is split: there is no merge kernel).
 struct TimingRec {
     hipEvent_t e0, e1, e2;
 };
@@ -418,18 +442,19 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
     return DSV4_OK;
 }
 
-dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads) {
-    if (heads != 0 && heads != kNarrowHeadsPerBlock && heads != kWide32HeadsPerBlock && heads != kWideHeadsPerBlock)
-        return fail(DSV4_ERR_INVALID, "heads per workgroup must be 0, %d, %d or %d", kNarrowHeadsPerBlock,
-                    kWide32HeadsPerBlock, kWideHeadsPerBlock);
+dsv4_status dsv4_attn_set_kernel(int32_t kernel) {
+    if (kernel != DSV4_KERNEL_AUTO && kernel != DSV4_KERNEL_H16 && kernel != DSV4_KERNEL_H32 &&
+        kernel != DSV4_KERNEL_H32_ROLES && kernel != DSV4_KERNEL_H64)
+        return fail(DSV4_ERR_INVALID, "kernel must be DSV4_KERNEL_AUTO or one of the bf16 kernels (1..4), got %d",
+                    kernel);
     std::lock_guard<std::mutex> lk(g_mu);
-    g_force_heads_per_workgroup = heads;
+    g_force_kernel = kernel;
     return DSV4_OK;
 }
 
 dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
                            int32_t c4_width, int32_t extra_pages, int32_t kv_fp8, int32_t* splits,
-                           int32_t* keys_per_split, int32_t* heads_per_workgroup) {
+                           int32_t* keys_per_split, int32_t* kernel) {
     if (splits == nullptr || keys_per_split == nullptr) return fail(DSV4_ERR_INVALID, "NULL output");
     if (compress_ratio != 0 && compress_ratio != 4 && compress_ratio != 128)
         return fail(DSV4_ERR_UNSUPPORTED, "invalid compress_ratio %d (must be 0, 4 or 128)", compress_ratio);
@@ -445,7 +470,7 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
     const Layout layout = choose_layout(cus, num_rows, num_heads, kv_fp8 != 0);
     plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages),
                 layout, splits, keys_per_split);
-    if (heads_per_workgroup != nullptr) *heads_per_workgroup = heads_per_block(layout);
+    if (kernel != nullptr) *kernel = kernel_id(layout);
     return DSV4_OK;
 }
 
@@ -481,15 +506,15 @@ dsv4_status dsv4_attn_timing_read(double* split_ms, double* merge_ms, int64_t* c
     std::lock_guard<std::mutex> lk(g_mu);
     double a = 0.0, b = 0.0;
     for (TimingRec& r : g_timing_recs) {
-        DSV4_HIP(hipEventSynchronize(r.e2));
+        DSV4_HIP(hipEventSynchronize(r.e2 != nullptr ? r.e2 : r.e1));
         float x = 0.f, y = 0.f;
         DSV4_HIP(hipEventElapsedTime(&x, r.e0, r.e1));
-        DSV4_HIP(hipEventElapsedTime(&y, r.e1, r.e2));
+        if (r.e2 != nullptr) DSV4_HIP(hipEventElapsedTime(&y, r.e1, r.e2));
         a += x;
         b += y;
         g_event_pool.push_back(r.e0);
         g_event_pool.push_back(r.e1);
-        g_event_pool.push_back(r.e2);
+        if (r.e2 != nullptr) g_event_pool.push_back(r.e2);
     }
     if (calls) *calls = (int64_t)g_timing_recs.size();
     g_timing_recs.clear();
@@ -613,15 +638,15 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     if (g_timing) {
         rec.e0 = take_event();
         rec.e1 = take_event();
-        rec.e2 = take_event();
-        if (!rec.e0 || !rec.e1 || !rec.e2) return fail(DSV4_ERR_HIP, "hipEventCreate failed");
+        rec.e2 = a.splits > 1 ? take_event() : nullptr;  // no merge kernel: no interval to time
+        if (!rec.e0 || !rec.e1 || (a.splits > 1 && !rec.e2)) return fail(DSV4_ERR_HIP, "hipEventCreate failed");
         DSV4_HIP(record_event(rec.e0, st));
     }
     DSV4_HIP(launch_attention(a, layout, st));
     if (g_timing) DSV4_HIP(record_event(rec.e1, st));
     if (a.splits > 1) DSV4_HIP(launch_merge(a, st));
     if (g_timing) {
-        DSV4_HIP(record_event(rec.e2, st));
+        if (rec.e2 != nullptr) DSV4_HIP(record_event(rec.e2, st));
         g_timing_recs.push_back(rec);
     }
     return DSV4_OK;

@@ -1045,6 +1045,534 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 KV, one workgroup per (query row, block of 32*kHH heads, key split),
+// with the four waves in two roles.  Waves 0 and 1 (score waves) compute the
+// scores of every head of the block over dim half d = w and the softmax;
+// waves 2 and 3 (PV waves) accumulate O for every head of the block over dim
+// half d = w - 2.  Each key operand is therefore read from LDS by one wave
+// per dim half only (the score operand by a score wave, the transposing
+// PV operand by a PV wave), half of what a split by heads reads.  Key rows
+// stream from HBM into a 4-stage LDS ring with direct global->LDS copies,
+// issued by all four waves (8 rows each).
+//
+// Tile layout in LDS (32 KiB per stage): as for the score and transposing
+// reads of the dim-half kernels -- rows 8g .. 8g+7 form group g; the 512
+// bytes of dim half d of those rows form four 1 KiB blocks m (128-byte line
+// m of each row) at byte g*8192 + d*4096 + m*1024; inside a block, 16-byte
+// position p holds the chunk (k-step 4m + (p >> 4), half (p & 1) ^ (g & 1))
+// of row 8g + ((p >> 1) & 7).
+//
+// Pipeline, one barrier per tile.  Iteration i:
+//   score waves publish their score partial of tile i for the other score
+//   wave, and P and the rescale factors of tile i-1; after the barrier they
+//   add the other wave's partial, run tile i's softmax interleaved with the
+//   score products of tile i+1;
+//   PV waves, after the barrier, read P of tile i-1, rescale their
+//   accumulators if the reference moved, run the PV product of tile i-1 and
+//   read the PV operand of tile i (held in registers until the next
+//   iteration, so tile i's stage is free at barrier i+1).
+// With kHH = 2 each score wave runs the softmax of one head block (the sum of
+// its own partial and the other wave's); with kHH = 1 both run the block's
+// softmax on the same sum (own + other, in either order: the same value) and
+// wave 0 publishes it.
+//
+// LDS: ring 4 x 32 KiB + 2 exchange buffers of 8 KiB partials + kHH x (2 KiB
+// of P + 256 B of factors); the prologue's page-table cache and tile masks
+// live in the exchange buffers until the loop starts.
+// ---------------------------------------------------------------------------
+template <int kHH>
+__global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
+    constexpr int kDims = kHeadDim / 2;  // head dims per wave (a dim half)
+    constexpr int kSteps = kDims / 16;   // score k-steps per tile
+    constexpr int kMb = kDims / 32;      // PV dim blocks per wave
+    constexpr int kHeads = 32 * kHH;     // heads per workgroup
+    // Exchange buffer: [score wave][chunk q][lane] f32x4 partials, then per
+    // head block P (64 lanes x 32 bytes) and one float per lane (the rescale
+    // factor, and at the end the output scale).
+    constexpr int kXPart = 2 * 64 * 64;            // bytes
+    constexpr int kXP = kXPart;                    // P of block hb at kXP + hb * 2048
+    constexpr int kXF = kXP + kHH * 2048;          // factor of block hb at kXF + hb * 256
+    constexpr int kXBytes = kXF + kHH * 256 + kHH * 128;  // + the output scales at the end
+    __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXBytes];
+    uint32_t* s_mask = (uint32_t*)&s_x[0][0];  // one 32-key mask per tile, prologue only
+    int32_t* s_table = (int32_t*)&s_x[1][0];   // kTableCap entries, prologue only
+    static_assert(kTableCap * 4 <= kXBytes, "page-table cache fits buffer 1");
+
+    fetch_args(a);
+    Item it;
+    const bool live = decode_item(a, it);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int d = w & 1;          // dim half of the wave's products
+    const bool score = w < 2;     // score wave (else PV wave), wave-uniform
+
+    // Round 1: the request bounds, the split's C4 indices and the guessed
+    // request's extra page-table row, then Q (independent of all of them,
+    // issued last so that waiting for the metadata does not wait for it).
+    const RequestChunk rc = load_requests(a.m, 0, l);
+    const int k0 = it.s * a.chunk;
+    ExtPrefetch pf;
+    prefetch_ext(a, it.t, k0, w, l, tid, pf);
+    __builtin_amdgcn_sched_barrier(0);
+    // Score waves: Q^T as the B operand of the scores, for every head block
+    // of the workgroup: lane holds head 32*hb + (l & 31), dims
+    // 256*d + 16*j + 8*(l >> 5) .. +8 of k-step j.  Heads past H read head
+    // H-1; their results are never written.  PV waves load no Q.
+    // Local block 0 is the wave's own softmax block (d with two blocks), local
+    // block kHH-1 the one whose partial it publishes for the other wave.
+    bf16x8 qf[kHH][kSteps];
+    float sink_raw = 0.f;  // the sink logit of the head of this lane's softmax block (read early: it ends the chain)
+    if (score) {
+        const int sink_head = min(it.hb * kHeads + (kHH == 2 ? d : 0) * 32 + (l & 31), a.H - 1);
+        sink_raw = *(a.sink != nullptr ? a.sink + sink_head : (const float*)a.zero_row);
+#pragma unroll
+        for (int lb = 0; lb < kHH; ++lb) {
+            const int hb = kHH == 2 ? (lb == 0 ? d : 1 - d) : 0;
+            const int my_head = it.hb * kHeads + hb * 32 + (l & 31);
+            const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(my_head, a.H - 1) * a.q_s1 + d * kDims + 8 * (l >> 5);
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j) qf[lb][j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!live) return;
+    const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
+    const int n_here = __builtin_amdgcn_readfirstlane(max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0));
+    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
+
+    // Row addresses of the keys this wave copies: tile j, row 8w + e sits in
+    // lane (8j + e) & 63 of ad[(8j + e) >> 6]; and, for the first three
+    // tiles, the row lane l copies (8w + ((l >> 1) & 7)) in pro[j], so those
+    // copies need no cross-lane step.  Unused keys read the zero row; window
+    // keys are filled in once their page entries have arrived.
+    const int dma_row = (l >> 1) & 7;
+    uint64_t ad[kAdRegs], pro[3];
+    {
+        uint64_t addr[kLaneKeys];
+        uint32_t valid;
+        ext_addresses(a, rk, k0, n_here, w, l, tid, pf, s_table, addr, valid);
+#pragma unroll
+        for (int u = 0; u < kAdRegs; ++u) ad[u] = addr[u];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) pro[j] = addr[kAdRegs + j];
+        // Valid-key mask of every tile (byte w of word j: rows 8w .. 8w+7 of
+        // tile j), published by the barrier before the first tile.
+        uint8_t* s_mask8 = (uint8_t*)s_mask;
+#pragma unroll
+        for (int u = 0; u < kAdRegs; ++u) {
+            const uint64_t b = __ballot((valid >> u) & 1u);
+            if (l < 8) s_mask8[4 * (8 * u + l) + w] = (uint8_t)(b >> (8 * l));
+        }
+    }
+    // Round 2 (window pages, scalar loads), issued after the last LDS access
+    // above and waited for after the first copies below (nothing in between
+    // touches LDS).
+    __builtin_amdgcn_sched_barrier(0);
+    SwaPages swp = issue_swa_pages(a, rk, k0, n_here);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Copy of one tile: lane p moves 16-byte chunks of row 8w + ((p >> 1) & 7),
+    // at chunk 2*(p >> 4) + ((p & 1) ^ (w & 1)) of each 128-byte line, in four
+    // parts of two lines each.  The row address comes from pro[] for the first
+    // three tiles and from ad[] (one cross-lane permute) after them.
+    const uint32_t dma_lane_off = 16u * (2u * (l >> 4) + ((l & 1) ^ (w & 1)));
+    auto tile_row = [&](int tile) -> const uint8_t* {  // tile >= 3; past the split: zero rows
+        const int u = min(tile >> 3, kMaxSplitKeys / 256 - 1);
+        const uint64_t au = u == 0 ? ad[0] : (u == 1 ? ad[1] : (u == 2 ? ad[2] : ad[3]));
+        const int src = 4 * (8 * (tile & 7) + dma_row);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
+        return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo) + dma_lane_off;
+    };
+    auto copy_part = [&](const uint8_t* row, int tile, auto part) {
+        constexpr int kP = decltype(part)::value;
+        const uint32_t dst = lds_addr(&s_tile[tile % kStages][0]) + w * 8192 + kP * 2048;
+        dma16_off<256 * kP>(row, dst);
+        dma16_off<256 * kP + 128>(row, dst + 1024);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    auto fetch_tile = [&](int tile) {
+        const uint8_t* row = tile < 3 ? (const uint8_t*)(uintptr_t)(tile == 0 ? pro[0] : (tile == 1 ? pro[1] : pro[2])) + dma_lane_off
+                                      : tile_row(tile);
+        copy_part(row, tile, P0{});
+        copy_part(row, tile, P1{});
+        copy_part(row, tile, P2{});
+        copy_part(row, tile, P3{});
+    };
+
+    // Per-lane LDS bases of the score operand and of the two transposing PV
+    // reads (rows r0 = 16pp + 4hq + kq and r0 + 8); see the layout above.
+    const int kk = l & 31, khi = l >> 5, kg = kk >> 3;
+    const uint32_t s_base = kg * 8192 + d * (16 * kDims) + 32 * (kk & 7) + 16 * (khi ^ (kg & 1));
+    const int a4 = l & 3, kq = (l >> 2) & 3, half = (l >> 4) & 1, hq = l >> 5;
+    const uint32_t t_base0 = d * (16 * kDims) + 256 * half + 128 * hq + 32 * kq + 8 * a4;
+    const uint32_t t_base1 = t_base0 + 8192 + 16 - 32 * (a4 >> 1);
+    const uint32_t ring = lds_addr(&s_tile[0][0]);
+
+    auto read_k = [&](int tile, bf16x8 (&av)[kSteps]) {
+        const lds_void* base = (const lds_void*)(uintptr_t)(ring + (tile % kStages) * (kTileKeys * 1024) + s_base);
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) av[j] = *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)base + 256 * j);
+    };
+    // Half of the score operand (k-steps 8h .. 8h+7), for the two-block
+    // score waves, which cannot hold all sixteen k-steps besides Q.
+    auto read_k_half = [&](int tile, int h, bf16x8 (&av)[kSteps / 2]) {
+        const lds_void* base = (const lds_void*)(uintptr_t)(ring + (tile % kStages) * (kTileKeys * 1024) + s_base + 2048 * h);
+#pragma unroll
+        for (int j = 0; j < kSteps / 2; ++j) av[j] = *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)base + 256 * j);
+    };
+    // K^T operand of PV: lane L takes dim 32*mb + (L & 31) of its dim slice
+    // and keys G(pp, L >> 5) from two transposing reads (rows r0 and r0 + 8).
+    auto read_kt = [&](int tile, bf16x8 (&kt)[2 * kMb]) {
+        const uint32_t st = ring + (tile % kStages) * (kTileKeys * 1024);
+        const __attribute__((address_space(3))) uint8_t* b0 = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_base0);
+        const __attribute__((address_space(3))) uint8_t* b1 = (const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(st + t_base1);
+#pragma unroll
+        for (int mb = 0; mb < kMb; ++mb)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b0 + 16384 * pp + 512 * mb));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b1 + 16384 * pp + 512 * mb));
+                kt[2 * mb + pp] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+    };
+
+
+    auto xbuf = [&](int i) -> uint8_t* { return &s_x[i & 1][0]; };
+    constexpr int kOwn = 0, kOther = kHH - 1;  // local head blocks of a score wave
+    const int sb = kHH == 2 ? d : 0;           // head block of a score wave's softmax
+
+    // The tile copies below go out while Q (the last compiler-visible vector
+    // loads) may still be in flight: every explicit vmcnt wait below counts
+    // the copies issued after its target, and loads completing in order make
+    // any earlier ones only strengthen it.
+    // Tiles made of compressed entries only are requested right away.
+    const int n_first = min(n_tiles, 3);
+    const int n_early = min(n_first, max(0, rk.n_ext - k0) / kTileKeys);
+    // Q has arrived by now (it was requested with the first metadata, a few
+    // round trips ago).  Waiting for it here, before any tile copy (which the
+    // compiler does not see), lets the compiler know it is in registers;
+    // otherwise it would wait for it again before every score product of the
+    // loop, and such a wait, counting the copies issued after Q as well,
+    // would stall on the tiles still in flight.
+    wait_vmcnt<0>();
+    for (int j = 0; j < n_early; ++j) fetch_tile(j);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_swa_pages(swp);
+    __builtin_amdgcn_sched_barrier(0);
+    // Window keys, now that their page entries have arrived.
+    if (swp.any) {
+        auto swa_addr = [&](int key, uint64_t cur) -> uint64_t {
+            const int i = k0 + key;
+            if (key >= n_here || i < rk.n_ext) return cur;
+            const int x = rk.swa_lo + (i - rk.n_ext);
+            const int pk = (x >> 8) - swp.pg_lo;
+            const int32_t e = pk == 0 ? swp.e[0] : (pk == 1 ? swp.e[1] : (pk == 2 ? swp.e[2] : (pk == 3 ? swp.e[3] : swp.e[4])));
+            return (uint64_t)(uintptr_t)(a.swa_pool + ((int64_t)e * kPage + (x & (kPage - 1))) * a.swa_row_bytes);
+        };
+#pragma unroll
+        for (int u = 0; u < kAdRegs; ++u) {
+            const int idx = 64 * u + l;
+            ad[u] = swa_addr(kTileKeys * (idx >> 3) + 8 * w + (idx & 7), ad[u]);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) pro[j] = swa_addr(kTileKeys * j + 8 * w + dma_row, pro[j]);
+    }
+    for (int j = n_early; j < n_first; ++j) fetch_tile(j);
+    __syncthreads();  // tile masks published
+    const uint32_t tile_mask = s_mask[l & 31];  // lane j: valid keys of tile j
+    if (n_tiles > 0) {
+        if (n_tiles > 2) wait_vmcnt<16>();
+        else if (n_tiles > 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // tile 0 is in LDS for every wave; the prologue scratch is dead
+    }
+    const uint8_t* next_row = tile_row(3);
+    uint8_t* const xb_end = xbuf(n_tiles);
+    float* const s_f = (float*)(xb_end + kXF + kHH * 256);  // output scale of head 32*hb + j, at the end
+
+    // The two roles run separate loops (so that the compiler allocates each
+    // role's registers on its own); each loop has exactly one barrier per
+    // tile, and both issue their waves' share of every tile copy.
+    if (score) {
+        const float sl2 = a.scale_log2;
+        const int key_shift = 4 * (l >> 5);  // register r of a score tile: key 8*(r >> 2) + 4*(l >> 5) + (r & 3)
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x16 sacc[kHH];
+#pragma unroll
+        for (int lb = 0; lb < kHH; ++lb) sacc[lb] = f32x16{};
+        if (n_tiles > 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8 av[kSteps / 2];
+                read_k_half(0, h, av);
+#pragma unroll
+                for (int j = 0; j < kSteps / 2; ++j)
+#pragma unroll
+                    for (int lb = 0; lb < kHH; ++lb)
+                        sacc[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[lb][8 * h + j], sacc[lb], 0, 0, 0);
+            }
+        }
+        bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
+        float alpha_out = 1.f;
+        // Publish the partial of tile i for the other score wave and P /
+        // rescale factor of tile i-1 (with one head block, wave 0 only).
+        auto publish = [&](uint8_t* xb, bool with_partial, bool with_p) __attribute__((always_inline)) {
+            if (with_partial) {
+                f32x4* mine = (f32x4*)xb + d * 256 + l;
+                const f32x16& v = sacc[kOther];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+            }
+            if (with_p && (kHH == 2 || d == 0)) {
+                bf16x8* pp = (bf16x8*)(xb + kXP + sb * 2048) + 2 * l;
+                pp[0] = pb[0];
+                pp[1] = pb[1];
+                ((float*)(xb + kXF + sb * 256))[l] = alpha_out;
+            }
+        };
+        auto iteration = [&](int i, auto fetch_tag) __attribute__((always_inline)) {
+            constexpr bool kFetch = decltype(fetch_tag)::value;
+            // This wave's rows of tile i+1 (tile i+2 may still be in flight).
+            if (kFetch || i + 2 < n_tiles) wait_vmcnt<8>();
+            else wait_vmcnt<0>();
+            uint8_t* xb = xbuf(i);
+            publish(xb, true, i > 0);
+            __syncthreads();  // partials of tile i, P of tile i-1 published; tile i+1 landed; tile i-1's stage is free
+            const uint8_t* row = next_row;
+            if constexpr (kFetch) next_row = tile_row(i + 4);
+            // The other score wave's partial of tile i for this wave's block,
+            // and the score operand of tile i+1 (when tile i is the last, that
+            // stage holds stale rows whose scores are discarded).
+            f32x4 part[4];
+            {
+                const f32x4* op = (const f32x4*)xb + (1 - d) * 256 + l;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) part[q] = op[64 * q];
+            }
+            // (One block: all sixteen k-steps of the score operand now; two
+            // blocks: the first eight now, the rest after their products.)
+            bf16x8 av[kHH == 2 ? kSteps / 2 : kSteps];
+            if constexpr (kHH == 2) read_k_half(i + 1, 0, av);
+            else read_k(i + 1, av);
+            if constexpr (kFetch) {
+                copy_part(row, i + 3, P0{});
+                copy_part(row, i + 3, P1{});
+            }
+            // Score products of tile i+1 in two halves: the first interleaved
+            // with tile i's partial sums, mask and maximum, the second (after
+            // the rescale decision) with its exponentials.
+            f32x16 snext[kHH];
+#pragma unroll
+            for (int lb = 0; lb < kHH; ++lb) snext[lb] = f32x16{};
+            constexpr int kHalf = kSteps / 2;
+#pragma unroll
+            for (int j = 0; j < kHalf; ++j)
+#pragma unroll
+                for (int lb = 0; lb < kHH; ++lb)
+                    snext[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[lb][j], snext[lb], 0, 0, 0);
+            // Scores of tile i: own partial + the other wave's (commutative,
+            // so with one block both waves get the same sum).
+            float sv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = sacc[kOwn][r] + part[r >> 2][r & 3];
+            {
+                const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i) >> key_shift;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sv[r] = ((mine >> (8 * (r >> 2) + (r & 3))) & 1u) ? sv[r] : -INFINITY;
+            }
+            float smax = sv[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) smax = fmaxf(smax, sv[r]);
+            const float tmax = smax * sl2;  // scale > 0: the maximum commutes with it
+#pragma unroll
+            for (int j = 0; j < kHalf * kHH; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x402, kHH == 2 ? 2 : 5, 0);  // then VALU
+            }
+            // The running reference m_run (scaled units) moves only when a
+            // score exceeds it by more than 2^8 (probabilities stay <= 256);
+            // the PV waves rescale their accumulators by the factor published
+            // with this tile's P.  l_run is this lane's share of the
+            // denominator; the two shares are added at the end.
+            alpha_out = 1.f;
+            if (__any(tmax > m_run + kRescaleLog2)) {
+                const float hmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the head's tile maximum
+                const bool grow = hmax > m_run + kRescaleLog2;
+                const float m_target = grow ? hmax : m_run;
+                const float alpha = fast_exp2(m_run - m_target);  // 0 while nothing was accumulated
+                l_run *= alpha;
+                alpha_out = m_run == -INFINITY ? 1.f : alpha;  // nothing accumulated yet: nothing to rescale
+                m_run = m_target;
+            }
+            if constexpr (kHH == 2) read_k_half(i + 1, 1, av);  // the second eight k-steps
+#pragma unroll
+            for (int j = 0; j < kHalf; ++j)
+#pragma unroll
+                for (int lb = 0; lb < kHH; ++lb)
+                    snext[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kHH == 2 ? j : kHalf + j], qf[lb][kHalf + j], snext[lb], 0, 0, 0);
+            const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+            float psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = fast_exp2(fmaf(sv[r], sl2, neg_m));
+                psum += pr;
+                pb[r >> 3][r & 7] = (__bf16)pr;
+            }
+            l_run += psum;
+#pragma unroll
+            for (int j = 0; j < kHalf * kHH; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x402, kHH == 2 ? 2 : 4, 0);  // then VALU / transcendental
+            }
+            if constexpr (kFetch) {
+                copy_part(row, i + 3, P2{});
+                copy_part(row, i + 3, P3{});
+            }
+#pragma unroll
+            for (int lb = 0; lb < kHH; ++lb) sacc[lb] = snext[lb];
+        };
+        int i = 0;
+        for (; i + 3 < n_tiles; ++i) iteration(i, std::true_type{});
+        for (; i < n_tiles; ++i) iteration(i, std::false_type{});
+
+        // The last tile's P, the output scale of every head and lse.
+        if (n_tiles > 0) publish(xb_end, false, true);
+        if (kHH == 2 || d == 0) {
+            const float l_tot = l_run + __shfl_xor(l_run, 32);  // both halves of the head's keys
+            const int my_head = it.hb * kHeads + sb * 32 + (l & 31);
+            const bool head_ok = my_head < a.H;
+            float f = 0.f, lse2 = -INFINITY;
+            if (a.splits == 1) {
+                const float sig = a.sink != nullptr && head_ok ? sink_raw * kLog2e : -INFINITY;
+                const float M = fmaxf(m_run, sig);
+                if (M != -INFINITY) {
+                    const float em = fast_exp2(m_run - M);
+                    const float den = l_tot * em + fast_exp2(sig - M);
+                    f = em / den;
+                    lse2 = M + fast_log2(den);
+                }
+            } else if (l_tot > 0.f) {
+                f = 1.f / l_tot;
+                lse2 = m_run + fast_log2(l_tot);
+            }
+            if (l < 32) {
+                s_f[sb * 32 + l] = f;
+                if (head_ok) {
+                    if (a.splits == 1) {
+                        if (a.lse != nullptr) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
+                    } else {
+                        a.ws_lse[((int64_t)it.t * a.splits + it.s) * a.H + my_head] = lse2;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // last P and the output scales published; every wave is done with the ring
+    } else {
+        // Accumulators of every head block over dim half d, and the PV
+        // operand of the previous tile.
+        f32x16 oacc[kHH][kMb];
+#pragma unroll
+        for (int hb = 0; hb < kHH; ++hb)
+#pragma unroll
+            for (int mb = 0; mb < kMb; ++mb) oacc[hb][mb] = f32x16{};
+        bf16x8 kt[2 * kMb];
+        // P of a tile (published in xb) times its operand, after the rescale
+        // the softmax asked for.
+        auto pv_step = [&](const uint8_t* xb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int hb = 0; hb < kHH; ++hb) {
+                const bf16x8* pp = (const bf16x8*)(xb + kXP + hb * 2048) + 2 * l;
+                const bf16x8 p0 = pp[0], p1 = pp[1];
+                const float alpha = ((const float*)(xb + kXF + hb * 256))[l];
+                if (__any(alpha != 1.f)) scale_accumulators(oacc[hb], alpha);
+#pragma unroll
+                for (int mb = 0; mb < kMb; ++mb) {
+                    oacc[hb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb], p0, oacc[hb][mb], 0, 0, 0);
+                    oacc[hb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + 1], p1, oacc[hb][mb], 0, 0, 0);
+                }
+            }
+        };
+        auto iteration = [&](int i, auto fetch_tag) __attribute__((always_inline)) {
+            constexpr bool kFetch = decltype(fetch_tag)::value;
+            if (kFetch || i + 2 < n_tiles) wait_vmcnt<8>();
+            else wait_vmcnt<0>();
+            const uint8_t* xb = xbuf(i);
+            __syncthreads();  // see the score waves' loop
+            const uint8_t* row = next_row;
+            if constexpr (kFetch) {
+                next_row = tile_row(i + 4);
+                copy_part(row, i + 3, P0{});
+                copy_part(row, i + 3, P1{});
+            }
+            if (i > 0) pv_step(xb);  // tile i-1, with its operand read last iteration
+            if constexpr (kFetch) {
+                copy_part(row, i + 3, P2{});
+                copy_part(row, i + 3, P3{});
+            }
+            read_kt(i, kt);  // tile i (landed at barrier i-1): its stage is read for the last time
+        };
+        int i = 0;
+        for (; i + 3 < n_tiles; ++i) iteration(i, std::true_type{});
+        for (; i < n_tiles; ++i) iteration(i, std::false_type{});
+
+        __syncthreads();  // see the score waves
+        if (n_tiles > 0) pv_step(xb_end);
+        // Rows of head 32*hb + (l & 31): O^T register r of dim block mb holds
+        // dim 256*d + 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3); 16-byte chunk
+        // c of a row is stored at chunk c ^ (row & 31) of its 1 KiB slot.
+#pragma unroll
+        for (int hb = 0; hb < kHH; ++hb) {
+            const float f = s_f[hb * 32 + (l & 31)];
+            const int r = l & 31;
+            uint8_t* base = &s_tile[0][0] + (hb * 32 + r) * 1024 + 8 * (l >> 5);
+#pragma unroll
+            for (int mb = 0; mb < kMb; ++mb) {
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int c = 32 * d + 4 * mb + qd;
+                    const f32x16& o = oacc[hb][mb];
+                    *(u32x2*)(base + 16 * (c ^ r)) = u32x2{pack_bf16x2(o[4 * qd] * f, o[4 * qd + 1] * f),
+                                                           pack_bf16x2(o[4 * qd + 2] * f, o[4 * qd + 3] * f)};
+                }
+            }
+        }
+    }
+    __syncthreads();  // rows staged
+    // Wave w stores rows w*kRows .. +kRows (heads past H skipped); lane l
+    // moves the row's 16-byte chunk l.  All LDS reads go out first.
+    constexpr int kRows = kHeads / 4;
+    u32x4 v[kRows];
+#pragma unroll
+    for (int e = 0; e < kRows; ++e) {
+        const int r = kRows * w + e;
+        v[e] = *(const u32x4*)(&s_tile[0][0] + r * 1024 + 16 * (l ^ (r & 31)));
+    }
+    const int head0 = it.hb * kHeads + kRows * w;
+    const int n_rows = min(kRows, a.H - head0);  // uniform
+    // Streaming stores: nothing in this kernel reads these rows again.
+    if (a.splits == 1) {
+        uint16_t* orow = a.out + (int64_t)it.t * a.out_s0 + (int64_t)head0 * a.out_s1 + 8 * l;
+#pragma unroll
+        for (int e = 0; e < kRows; ++e) {
+            if (e < n_rows) {
+                __builtin_nontemporal_store(u32x2{v[e][0], v[e][1]}, (u32x2*)(orow + e * a.out_s1));  // 8-byte aligned rows
+                __builtin_nontemporal_store(u32x2{v[e][2], v[e][3]}, (u32x2*)(orow + e * a.out_s1 + 4));
+            }
+        }
+    } else {
+        uint16_t* prow = a.ws_o + (((int64_t)it.t * a.splits + it.s) * a.H + head0) * kHeadDim + 8 * l;
+#pragma unroll
+        for (int e = 0; e < kRows; ++e)
+            if (e < n_rows) __builtin_nontemporal_store(v[e], (u32x4*)(prow + e * kHeadDim));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 KV, narrow layout: one workgroup per (row, block of 16 heads, key
 // split).  The four waves are independent: wave w takes the split's 16-key
 // tiles w, w+4, w+8, ... through a private two-stage LDS ring, keeps its own
@@ -1563,6 +2091,9 @@ hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream
             break;
         case Layout::kWide32:
             hipLaunchKernelGGL(attn_wide_kernel<1>, grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kRoles32:
+            hipLaunchKernelGGL(attn_ws_kernel<1>, grid, dim3(256), 0, stream, a);
             break;
         case Layout::kNarrow:
             hipLaunchKernelGGL(attn_narrow_kernel, grid, dim3(256), 0, stream, a);

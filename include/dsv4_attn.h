@@ -171,31 +171,52 @@ void dsv4_attn_workspace_release(void);
 dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
 
 /*
- * Tuning / test hook: force the bf16 kernel variant by its query heads per
- * workgroup (16: four independent waves on alternate 16-key tiles; 32: four
- * waves on the four quarters of the head dims; 64: two head groups x two dim
- * halves), or 0 for the automatic choice.  Packed FP8 pools always use 64.
- * Process-wide.
+ * Split-kernel variants.  Every variant computes the same attention; they
+ * differ in how a workgroup of four waves divides its heads and head dims:
+ *   DSV4_KERNEL_H16        16 heads per workgroup, four independent waves on
+ *                          alternate 16-key tiles;
+ *   DSV4_KERNEL_H32        32 heads, each wave one quarter of the head dims;
+ *   DSV4_KERNEL_H32_ROLES  32 heads, two waves compute the scores and the
+ *                          softmax (one dim half each), two accumulate P.V
+ *                          (one dim half each);
+ *   DSV4_KERNEL_H64        64 heads, two head groups x two dim halves;
+ *   DSV4_KERNEL_FP8        64 heads on packed FP8 pools (the only variant for
+ *                          that format).
  */
-dsv4_status dsv4_attn_set_heads_per_workgroup(int32_t heads);
+enum {
+    DSV4_KERNEL_AUTO = 0,
+    DSV4_KERNEL_H16 = 1,
+    DSV4_KERNEL_H32 = 2,
+    DSV4_KERNEL_H32_ROLES = 3,
+    DSV4_KERNEL_H64 = 4,
+    DSV4_KERNEL_FP8 = 5
+};
+
+/*
+ * Tuning / test hook: force the bf16 split-kernel variant (DSV4_KERNEL_H16 ..
+ * DSV4_KERNEL_H64), or DSV4_KERNEL_AUTO for the automatic choice.  Packed FP8
+ * pools always use DSV4_KERNEL_FP8.  Any other value returns
+ * DSV4_ERR_INVALID.  Process-wide.
+ */
+dsv4_status dsv4_attn_set_kernel(int32_t kernel);
 
 /*
  * Plan that dsv4_attn_forward would use for these sizes: number of key
- * splits per (row, head block), keys per split, and query heads per
- * workgroup (16, 32 or 64; the kernel variant).  kv_fp8 is nonzero for packed
- * FP8 pools (the two formats run different kernels and are planned
- * differently).  heads_per_workgroup may be NULL.  Host-only, no device
+ * splits per (row, head block), keys per split, and the split-kernel variant
+ * (DSV4_KERNEL_*; its heads per workgroup are 16, 32, 32, 64 or 64).  kv_fp8
+ * is nonzero for packed FP8 pools (the two formats run different kernels and
+ * are planned differently).  kernel may be NULL.  Host-only, no device
  * access.
  */
 dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress_ratio, int32_t window,
                            int32_t c4_width, int32_t extra_pages, int32_t kv_fp8, int32_t* splits,
-                           int32_t* keys_per_split, int32_t* heads_per_workgroup);
+                           int32_t* keys_per_split, int32_t* kernel);
 
 /*
  * Kernel timing on the caller's stream with HIP events.  While enabled, every
  * dsv4_attn_forward records an event before the split kernel, one between it
- * and the merge kernel, and one after the merge kernel (which only runs when
- * a row is split).  The events are timing-only (created without the
+ * and the merge kernel, and one after the merge kernel (only when a row is
+ * split: otherwise there is no merge kernel and its time counts as 0).  The events are timing-only (created without the
  * system-scope fence on record), so they neither flush caches nor stall the
  * work that follows.  Calls made while the stream is being captured into a
  * HIP graph record external event nodes instead, re-recorded on every replay.

@@ -166,15 +166,21 @@ def test_plan_is_host_only_and_sane():
     assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), None) == 0
     assert c.value == 64 and s.value == 10
     assert L.dsv4_attn_set_split_keys(0) == 0
-    h = ctypes.c_int32()
-    # 32 rows of 64 heads fill a quarter of the chip at most: the 32-head kernel
-    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
-    assert h.value in (32, 64)
-    assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
-    assert h.value == 64  # packed FP8 always runs 64-head blocks
-    for forced in (16, 32, 64):
-        assert L.dsv4_attn_set_heads_per_workgroup(forced) == 0
-        assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(h)) == 0
-        assert h.value == forced
-    assert L.dsv4_attn_set_heads_per_workgroup(48) == INVALID
-    assert L.dsv4_attn_set_heads_per_workgroup(0) == 0
+    k = ctypes.c_int32()
+    # 32 rows of 64 heads fill a quarter of the chip at most: a 32-head kernel
+    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 2  # DSV4_KERNEL_H32 (without a GPU the plan assumes 256 compute units)
+    # 128 rows x two 32-head blocks fill the chip without splitting keys: the role kernel, one split
+    assert L.dsv4_attn_plan(128, 64, 4, 128, 512, 64, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 3 and s.value == 1
+    assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 5  # packed FP8 always runs the FP8 kernel
+    for forced in (1, 2, 3, 4):
+        assert L.dsv4_attn_set_kernel(forced) == 0
+        assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+        assert k.value == forced
+        assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+        assert k.value == 5  # FP8 pools ignore the forced bf16 variant
+    for bad in (5, 6, -1, 32):
+        assert L.dsv4_attn_set_kernel(bad) == INVALID
+    assert L.dsv4_attn_set_kernel(0) == 0

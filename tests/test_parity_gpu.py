@@ -91,14 +91,19 @@ def test_gather_workloads_bit_exact(orc, n):
     check_gather(orc, make_config(n))
 
 
-@pytest.fixture
-def heads_per_workgroup(request):
-    """Force one bf16 kernel variant for the test, then restore the automatic choice."""
-    from hybrid_sparse_mqa_amd import dsv4_attn_set_heads_per_workgroup
+# bf16 split-kernel variants (DSV4_KERNEL_*): 0 automatic, 1 16 heads, 2 32 heads
+# (dim quarters), 3 32 heads (score / PV roles), 4 64 heads.
+BF16_KERNELS = [1, 2, 3, 4]
 
-    dsv4_attn_set_heads_per_workgroup(request.param)
+
+@pytest.fixture
+def kernel(request):
+    """Force one bf16 kernel variant for the test, then restore the automatic choice."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_kernel
+
+    dsv4_attn_set_kernel(request.param)
     yield request.param
-    dsv4_attn_set_heads_per_workgroup(0)
+    dsv4_attn_set_kernel(0)
 
 
 def widen_extra_table(case, pages):
@@ -111,15 +116,15 @@ def widen_extra_table(case, pages):
     return dataclasses.replace(case, extra_page_table=wide)
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [0, 16, 32, 64], indirect=True)
+@pytest.mark.parametrize("kernel", [0] + BF16_KERNELS, indirect=True)
 @pytest.mark.parametrize("i", [9, 12, 14, 17])
-def test_extra_table_wider_than_lds_copy(orc, i, heads_per_workgroup):
+def test_extra_table_wider_than_lds_copy(orc, i, kernel):
     case = widen_extra_table(small_case(i), 1100)
-    log(f"wide extra table {SMALL_IDS[i]} heads/workgroup={heads_per_workgroup}")
+    log(f"wide extra table {SMALL_IDS[i]} kernel={kernel}")
     check_gather(orc, case)
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
-    G.compare(out, lse, ro, rl, what=f"wide-{SMALL_IDS[i]}-hpw{heads_per_workgroup}")
+    G.compare(out, lse, ro, rl, what=f"wide-{SMALL_IDS[i]}-k{kernel}")
 
 
 # --------------------------------------------------------------------------
@@ -134,19 +139,19 @@ def test_forward_small(orc, i):
     G.compare(out, lse, ro, rl, what=SMALL_IDS[i])
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [16, 32, 64], indirect=True)
+@pytest.mark.parametrize("kernel", BF16_KERNELS, indirect=True)
 @pytest.mark.parametrize("i", [0, 3, 5, 8, 11, 12, 14, 15, 16], ids=[SMALL_IDS[i] for i in [0, 3, 5, 8, 11, 12, 14, 15, 16]])
-def test_forward_small_each_bf16_kernel(orc, i, heads_per_workgroup):
+def test_forward_small_each_bf16_kernel(orc, i, kernel):
     case = small_case(i)
-    log(f"forward small {SMALL_IDS[i]} heads/workgroup={heads_per_workgroup}")
+    log(f"forward small {SMALL_IDS[i]} kernel={kernel}")
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
-    G.compare(out, lse, ro, rl, what=f"{SMALL_IDS[i]}-hpw{heads_per_workgroup}")
+    G.compare(out, lse, ro, rl, what=f"{SMALL_IDS[i]}-k{kernel}")
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [16, 32, 64], indirect=True)
+@pytest.mark.parametrize("kernel", BF16_KERNELS, indirect=True)
 @pytest.mark.parametrize("keys", [16, 32, 48, 96, 160, 2048])
-def test_forced_split_sizes_each_bf16_kernel(orc, keys, heads_per_workgroup):
+def test_forced_split_sizes_each_bf16_kernel(orc, keys, kernel):
     from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
 
     case = make_case(seq_lens=[3000, 700, 5], n_q=[2, 3, 1], H=100, R=4, seed=31, pad_mode="scatter")
@@ -156,7 +161,7 @@ def test_forced_split_sizes_each_bf16_kernel(orc, keys, heads_per_workgroup):
         out, lse = G.run_forward(case)
     finally:
         dsv4_attn_set_split_keys(0)
-    G.compare(out, lse, ro, rl, what=f"split{keys}-hpw{heads_per_workgroup}")
+    G.compare(out, lse, ro, rl, what=f"split{keys}-k{kernel}")
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -289,9 +294,9 @@ SPIKES = [
 ]
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [0, 16], indirect=True)
+@pytest.mark.parametrize("kernel", [0, 1, 3], indirect=True)
 @pytest.mark.parametrize("name,R,sl,nq,where,visible", SPIKES, ids=[s[0] for s in SPIKES])
-def test_spikes(orc, name, R, sl, nq, where, visible, heads_per_workgroup):
+def test_spikes(orc, name, R, sl, nq, where, visible, kernel):
     case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=77, n_sel=300)
     t = 0  # first row of the request
     p = int(case.seq_lens[0]) - nq + 0
@@ -319,9 +324,9 @@ def test_spikes(orc, name, R, sl, nq, where, visible, heads_per_workgroup):
     assert dominated == visible, (name, rl[t, 0])
 
 
-@pytest.mark.parametrize("heads_per_workgroup", [16, 64], indirect=True)
+@pytest.mark.parametrize("kernel", BF16_KERNELS, indirect=True)
 @pytest.mark.parametrize("R", [0, 128])
-def test_growing_scores(orc, R, heads_per_workgroup):
+def test_growing_scores(orc, R, kernel):
     """Key rows of row 0 blend, along its key list, from random towards
     2 * q[0, head 0], so head 0's scores climb by about 65 (base 2) over the
     pass: its running softmax reference falls far behind later keys several
@@ -340,7 +345,7 @@ def test_growing_scores(orc, R, heads_per_workgroup):
             pool[slot] = grown.view(torch.int16).numpy().view(np.uint16)
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
-    G.compare(out, lse, ro, rl, what=f"growing-R{R}-hpw{heads_per_workgroup}")
+    G.compare(out, lse, ro, rl, what=f"growing-R{R}-k{kernel}")
 
 
 # --------------------------------------------------------------------------
