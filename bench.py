@@ -222,6 +222,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-keys", type=int, default=0, help="force keys per split (0 = library plan)")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="force a bf16 split-kernel variant (DSV4_KERNEL_*, 0 = library choice)")
     ap.add_argument("--sample-every", type=int, default=10,
                     help="time the kernels of every N-th call of the timed replay with HIP events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -244,8 +246,8 @@ def main() -> int:
 
     import torch
 
-    from hybrid_sparse_mqa_amd import (dsv4_attn_forward, dsv4_attn_plan, dsv4_attn_set_split_keys,
-                                       dsv4_attn_timing_enable, dsv4_attn_timing_read)
+    from hybrid_sparse_mqa_amd import (dsv4_attn_forward, dsv4_attn_plan, dsv4_attn_set_kernel,
+                                       dsv4_attn_set_split_keys, dsv4_attn_timing_enable, dsv4_attn_timing_read)
     from synth import make_config
 
     if not torch.cuda.is_available():
@@ -281,6 +283,8 @@ def main() -> int:
 
     if args.split_keys:
         dsv4_attn_set_split_keys(args.split_keys)
+    if args.kernel:
+        dsv4_attn_set_kernel(args.kernel)
     splits, chunk, kernel = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K,
                                    0 if case.extra_page_table is None else case.extra_page_table.shape[1],
                                    kv_fp8=case.kv == "fp8")

@@ -243,13 +243,13 @@ Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
         default: break;
     }
     if (H <= kNarrowHeadsPerBlock) return Layout::kNarrow;
-    // Enough rows for one 32-head workgroup per compute unit without
-    // splitting keys: the score/PV role kernel, whose tile loop is the
-    // fastest and which then needs no merge (measured on C4 verify, 128 rows
-    // x 64 heads).  Otherwise 64-head blocks when rows x splits fill the chip
-    // with splits of at least a few tiles, else 32-head blocks (measured: C128
-    // decode, 64 rows; C4 decode, 32 rows).
-    if ((int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) >= cus) return Layout::kRoles32;
+    // Enough rows for one 32-head workgroup per compute unit with at most
+    // two key splits: the score/PV role kernel, whose tile loop is the
+    // fastest (measured: C4 verify, 128 rows x 64 heads, unsplit; C128
+    // decode, 64 rows, two splits).  Otherwise 64-head blocks when rows x
+    // splits fill the chip with splits of at least a few tiles, else 32-head
+    // blocks (measured: C4 decode, 32 rows).
+    if (2 * (int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) >= cus) return Layout::kRoles32;
     const int64_t wide_rows = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
     return wide_rows * 4 < cus ? Layout::kWide32 : Layout::kWide;
 }

@@ -118,29 +118,15 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
-// LDS byte address lds_row + 16*i (M0 holds the wave-uniform base).  Issued
-// as inline asm so that the compiler does not treat every later LDS access
-// as dependent on it; callers wait with wait_vmcnt() and a barrier.  M0 is
-// saved and restored around the copy, with the one wait state the hardware
-// needs between an M0 write and an LDS-DMA instruction.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_row) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_row);
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(src), "s"(base)
-        : "memory");
-}
-
-// dma16 with a byte offset folded into the instruction (a 13-bit signed
-// immediate).  The instruction adds that offset to the LDS address as well
-// as to the global one, so M0 is set to the destination minus the offset.
+// Direct global -> LDS copy of 16 bytes per lane, with a byte offset OFF
+// folded into the instruction (a 13-bit signed immediate): lane i's bytes
+// from src + OFF land at LDS byte address lds_row + 16*i.  The instruction
+// adds the offset to the LDS address as well as to the global one, so M0
+// (the wave-uniform LDS base) is set to the destination minus the offset.
+// Issued as inline asm so that the compiler does not treat every later LDS
+// access as dependent on it; callers wait with wait_vmcnt() and a barrier.
+// M0 is saved and restored around the copy, with the one wait state the
+// hardware needs between an M0 write and an LDS-DMA instruction.
 template <int OFF>
 __device__ __forceinline__ void dma16_off(const void* src, uint32_t lds_row) {
     static_assert(OFF >= 0 && OFF < 4096, "global offset is 13-bit signed");
@@ -1045,15 +1031,19 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 KV, one workgroup per (query row, block of 32*kHH heads, key split),
-// with the four waves in two roles.  Waves 0 and 1 (score waves) compute the
+// bf16 KV, one workgroup per (query row, block of 32 heads, key split), with
+// the four waves in two roles.  Waves 0 and 1 (score waves) compute the
 // scores of every head of the block over dim half d = w and the softmax;
 // waves 2 and 3 (PV waves) accumulate O for every head of the block over dim
 // half d = w - 2.  Each key operand is therefore read from LDS by one wave
 // per dim half only (the score operand by a score wave, the transposing
 // PV operand by a PV wave), half of what a split by heads reads.  Key rows
-// stream from HBM into a 4-stage LDS ring with direct global->LDS copies,
-// issued by all four waves (8 rows each).
+// stream from HBM into a 4-stage LDS ring with direct global->LDS copies:
+// the first three tiles by all four waves (8 rows each), the later ones by
+// the PV waves alone (16 rows each: their own and the score wave's of the
+// same parity), so that the score waves never wait at the memory queue
+// inside the loop (measured slightly faster than each wave copying its own
+// rows).
 //
 // Tile layout in LDS (32 KiB per stage): as for the score and transposing
 // reads of the dim-half kernels -- rows 8g .. 8g+7 form group g; the 512
@@ -1063,22 +1053,19 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
 // of row 8g + ((p >> 1) & 7).
 //
 // Pipeline, one barrier per tile.  Iteration i:
-//   score waves publish their score partial of tile i for the other score
-//   wave, and P and the rescale factors of tile i-1; after the barrier they
-//   add the other wave's partial, run tile i's softmax interleaved with the
-//   score products of tile i+1;
-//   PV waves, after the barrier, read P of tile i-1, rescale their
-//   accumulators if the reference moved, run the PV product of tile i-1 and
-//   read the PV operand of tile i (held in registers until the next
-//   iteration, so tile i's stage is free at barrier i+1).
-// With kHH = 2 each score wave runs the softmax of one head block (the sum of
-// its own partial and the other wave's); with kHH = 1 both run the block's
-// softmax on the same sum (own + other, in either order: the same value) and
-// wave 0 publishes it.
+//   score waves publish their score partial of tile i (all 32 heads, their
+//   dim half), and P and the rescale factors of tile i-1; after the barrier
+//   each reads both partials of its 16 heads (the block's heads are split
+//   between the two score waves for the softmax), runs tile i's softmax on
+//   their sum, interleaved with the score products of tile i+1;
+//   PV waves, after the barrier, request tile i+3, read P of tile i-1,
+//   rescale their accumulators if the reference moved, run the PV product of
+//   tile i-1 and read the PV operand of tile i (held in registers until the
+//   next iteration, so tile i's stage is free at barrier i+1).
 //
-// LDS: ring 4 x 32 KiB + 2 exchange buffers of 8 KiB partials + kHH x (2 KiB
-// of P + 256 B of factors); the prologue's page-table cache and tile masks
-// live in the exchange buffers until the loop starts.
+// LDS: ring 4 x 32 KiB + 2 exchange buffers (two 4.5 KiB partials, 2 KiB of
+// P, the factors); the prologue's page-table cache, tile masks and the score
+// waves' row addresses live in the exchange buffers until the loop starts.
 // ---------------------------------------------------------------------------
 template <int kHH>
 __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
@@ -1086,18 +1073,23 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
     constexpr int kSteps = kDims / 16;   // score k-steps per tile
     constexpr int kMb = kDims / 32;      // PV dim blocks per wave
     constexpr int kHeads = 32 * kHH;     // heads per workgroup
-    // Exchange buffer: [score wave][chunk q][lane] f32x4 partials, then per
-    // head block P (64 lanes x 32 bytes) and one float per lane (the rescale
-    // factor, and at the end the output scale).
-    constexpr int kXPart = 2 * 64 * 64;            // bytes
-    constexpr int kXP = kXPart;                    // P of block hb at kXP + hb * 2048
-    constexpr int kXF = kXP + kHH * 2048;          // factor of block hb at kXF + hb * 256
-    constexpr int kXBytes = kXF + kHH * 256 + kHH * 128;  // + the output scales at the end
+    static_assert(kHH == 1, "the score waves' softmax layout covers one 32-head block");
+    // Exchange buffer: the two score partials (partial d: fp32 [32 heads][32
+    // keys], rows padded to 144 bytes so that 16 consecutive rows start in
+    // distinct banks), then P in the PV operand layout (64 lanes x 32 bytes),
+    // the rescale factor of each head, and at the end the output scales.
+    constexpr int kRowBytes = 144;
+    constexpr int kPartBytes = 32 * kRowBytes;
+    constexpr int kXP = 2 * kPartBytes;                   // P
+    constexpr int kXF = kXP + 2048;                       // factor of head j at kXF + 4j
+    constexpr int kXBytes = kXF + 128 + 128;              // + the output scales at the end
     __shared__ __attribute__((aligned(1024))) uint8_t s_tile[kStages][kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXBytes];
     uint32_t* s_mask = (uint32_t*)&s_x[0][0];  // one 32-key mask per tile, prologue only
     int32_t* s_table = (int32_t*)&s_x[1][0];   // kTableCap entries, prologue only
     static_assert(kTableCap * 4 <= kXBytes, "page-table cache fits buffer 1");
+    constexpr int kAdOffset = kTableCap * 4;  // score waves' row addresses in buffer 1, prologue only
+    static_assert(kAdOffset + 2 * kAdRegs * 64 * 8 <= kXBytes, "row addresses fit buffer 1");
 
     fetch_args(a);
     Item it;
@@ -1115,25 +1107,18 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
     ExtPrefetch pf;
     prefetch_ext(a, it.t, k0, w, l, tid, pf);
     __builtin_amdgcn_sched_barrier(0);
-    // Score waves: Q^T as the B operand of the scores, for every head block
-    // of the workgroup: lane holds head 32*hb + (l & 31), dims
-    // 256*d + 16*j + 8*(l >> 5) .. +8 of k-step j.  Heads past H read head
-    // H-1; their results are never written.  PV waves load no Q.
-    // Local block 0 is the wave's own softmax block (d with two blocks), local
-    // block kHH-1 the one whose partial it publishes for the other wave.
-    bf16x8 qf[kHH][kSteps];
-    float sink_raw = 0.f;  // the sink logit of the head of this lane's softmax block (read early: it ends the chain)
+    // Score waves: Q^T as the B operand of the scores (lane: head l & 31,
+    // dims 256*d + 16*j + 8*(l >> 5) .. +8 of k-step j).  Heads past H read
+    // head H-1; their results are never written.  PV waves load no Q.
+    bf16x8 qf[kSteps];
+    float sink_raw = 0.f;  // the sink logit of the head of this lane's softmax (read early: it ends the chain)
     if (score) {
-        const int sink_head = min(it.hb * kHeads + (kHH == 2 ? d : 0) * 32 + (l & 31), a.H - 1);
+        const int sink_head = min(it.hb * kHeads + 16 * d + (l & 15), a.H - 1);
         sink_raw = *(a.sink != nullptr ? a.sink + sink_head : (const float*)a.zero_row);
+        const int my_head = it.hb * kHeads + (l & 31);
+        const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(my_head, a.H - 1) * a.q_s1 + d * kDims + 8 * (l >> 5);
 #pragma unroll
-        for (int lb = 0; lb < kHH; ++lb) {
-            const int hb = kHH == 2 ? (lb == 0 ? d : 1 - d) : 0;
-            const int my_head = it.hb * kHeads + hb * 32 + (l & 31);
-            const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(my_head, a.H - 1) * a.q_s1 + d * kDims + 8 * (l >> 5);
-#pragma unroll
-            for (int j = 0; j < kSteps; ++j) qf[lb][j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
-        }
+        for (int j = 0; j < kSteps; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
     }
     __builtin_amdgcn_sched_barrier(0);
     if (!live) return;
@@ -1243,8 +1228,6 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
 
 
     auto xbuf = [&](int i) -> uint8_t* { return &s_x[i & 1][0]; };
-    constexpr int kOwn = 0, kOther = kHH - 1;  // local head blocks of a score wave
-    const int sb = kHH == 2 ? d : 0;           // head block of a score wave's softmax
 
     // The tile copies below go out while Q (the last compiler-visible vector
     // loads) may still be in flight: every explicit vmcnt wait below counts
@@ -1283,7 +1266,16 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
         for (int j = 0; j < 3; ++j) pro[j] = swa_addr(kTileKeys * j + 8 * w + dma_row, pro[j]);
     }
     for (int j = n_early; j < n_first; ++j) fetch_tile(j);
-    __syncthreads();  // tile masks published
+    // The score waves' row addresses of tiles 3 and later, for the PV wave
+    // that copies those rows in the loop (in buffer 1, past the page-table
+    // cache; the buffer's first use in the loop follows the barrier of
+    // iteration 0, by which the PV waves have read them).
+    uint64_t* const s_ad = (uint64_t*)(&s_x[1][0] + kAdOffset);
+    if (score) {
+#pragma unroll
+        for (int u = 0; u < kAdRegs; ++u) s_ad[(d * kAdRegs + u) * 64 + l] = ad[u];
+    }
+    __syncthreads();  // tile masks and the score waves' row addresses published
     const uint32_t tile_mask = s_mask[l & 31];  // lane j: valid keys of tile j
     if (n_tiles > 0) {
         if (n_tiles > 2) wait_vmcnt<16>();
@@ -1293,18 +1285,23 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
     }
     const uint8_t* next_row = tile_row(3);
     uint8_t* const xb_end = xbuf(n_tiles);
-    float* const s_f = (float*)(xb_end + kXF + kHH * 256);  // output scale of head 32*hb + j, at the end
+    float* const s_f = (float*)(xb_end + kXF + 128);  // output scale of head j of the block, at the end
 
     // The two roles run separate loops (so that the compiler allocates each
     // role's registers on its own); each loop has exactly one barrier per
-    // tile, and both issue their waves' share of every tile copy.
+    // tile.  Only the PV waves copy tiles in the loop.
     if (score) {
+        // Scores: wave d computes the partial over dim half d for all 32
+        // heads (MFMA layout: register r of lane l holds head l & 31, key
+        // 8*(r >> 2) + 4*(l >> 5) + (r & 3)), and publishes it.  The softmax
+        // then runs on the sum of both partials in another layout, which
+        // splits the block's heads between the two waves: lane l of wave d
+        // holds head hs = 16d + (l & 15) and keys 8g .. 8g+7, g = l >> 4, so
+        // each wave exponentiates half of the tile.
         const float sl2 = a.scale_log2;
-        const int key_shift = 4 * (l >> 5);  // register r of a score tile: key 8*(r >> 2) + 4*(l >> 5) + (r & 3)
-        float m_run = -INFINITY, l_run = 0.f;
-        f32x16 sacc[kHH];
-#pragma unroll
-        for (int lb = 0; lb < kHH; ++lb) sacc[lb] = f32x16{};
+        const int hs = 16 * d + (l & 15), g = l >> 4;
+        float m_run = -INFINITY, l_run = 0.f;  // per head (the same in its four lanes); l_run: this lane's keys
+        f32x16 sacc = f32x16{};
         if (n_tiles > 0) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -1312,96 +1309,84 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
                 read_k_half(0, h, av);
 #pragma unroll
                 for (int j = 0; j < kSteps / 2; ++j)
-#pragma unroll
-                    for (int lb = 0; lb < kHH; ++lb)
-                        sacc[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[lb][8 * h + j], sacc[lb], 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[8 * h + j], sacc, 0, 0, 0);
             }
         }
-        bf16x8 pb[2] = {bf16x8{}, bf16x8{}};
+        // P of a tile for the PV waves: keys 8g .. 8g+3 of head hs go to PV
+        // lane hs, keys 8g+4 .. 8g+7 to PV lane hs + 32, both at k-step g >> 1,
+        // elements 4*(g & 1) .. +3 (see pv_step).
+        u32x2 p_lo = u32x2{0u, 0u}, p_hi = u32x2{0u, 0u};
         float alpha_out = 1.f;
-        // Publish the partial of tile i for the other score wave and P /
-        // rescale factor of tile i-1 (with one head block, wave 0 only).
+        // Publish this wave's partial of tile i and its heads' P and rescale
+        // factors of tile i-1.
         auto publish = [&](uint8_t* xb, bool with_partial, bool with_p) __attribute__((always_inline)) {
             if (with_partial) {
-                f32x4* mine = (f32x4*)xb + d * 256 + l;
-                const f32x16& v = sacc[kOther];
+                // Row: head l & 31; keys 4c .. 4c+3 (c = 2q + (l >> 5)) at byte 16c.
+                uint8_t* row = xb + d * kPartBytes + (l & 31) * kRowBytes + 16 * (l >> 5);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                for (int q = 0; q < 4; ++q)
+                    *(f32x4*)(row + 32 * q) = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
             }
-            if (with_p && (kHH == 2 || d == 0)) {
-                bf16x8* pp = (bf16x8*)(xb + kXP + sb * 2048) + 2 * l;
-                pp[0] = pb[0];
-                pp[1] = pb[1];
-                ((float*)(xb + kXF + sb * 256))[l] = alpha_out;
+            if (with_p) {
+                uint8_t* pb = xb + kXP + 16 * (g >> 1) + 8 * (g & 1);
+                *(u32x2*)(pb + 32 * hs) = p_lo;
+                *(u32x2*)(pb + 32 * (hs + 32)) = p_hi;
+                if (l < 16) ((float*)(xb + kXF))[hs] = alpha_out;
             }
         };
-        auto iteration = [&](int i, auto fetch_tag) __attribute__((always_inline)) {
-            constexpr bool kFetch = decltype(fetch_tag)::value;
-            // This wave's rows of tile i+1 (tile i+2 may still be in flight).
-            if (kFetch || i + 2 < n_tiles) wait_vmcnt<8>();
+        auto iteration = [&](int i) __attribute__((always_inline)) {
+            // This wave's rows of tile i+1 if it copied them (tiles 1 and 2;
+            // tile 2 may still be in flight at tile 0).
+            if (i == 0 && n_tiles > 2) wait_vmcnt<8>();
             else wait_vmcnt<0>();
             uint8_t* xb = xbuf(i);
             publish(xb, true, i > 0);
             __syncthreads();  // partials of tile i, P of tile i-1 published; tile i+1 landed; tile i-1's stage is free
-            const uint8_t* row = next_row;
-            if constexpr (kFetch) next_row = tile_row(i + 4);
-            // The other score wave's partial of tile i for this wave's block,
-            // and the score operand of tile i+1 (when tile i is the last, that
-            // stage holds stale rows whose scores are discarded).
-            f32x4 part[4];
+            // Both partials of this lane's keys of tile i, and the score
+            // operand of tile i+1 (when tile i is the last, that stage holds
+            // stale rows whose scores are discarded).
+            f32x4 pa[2], pb2[2];
             {
-                const f32x4* op = (const f32x4*)xb + (1 - d) * 256 + l;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) part[q] = op[64 * q];
+                const uint8_t* r0 = xb + hs * kRowBytes + 32 * g;
+                pa[0] = *(const f32x4*)(r0);
+                pa[1] = *(const f32x4*)(r0 + 16);
+                pb2[0] = *(const f32x4*)(r0 + kPartBytes);
+                pb2[1] = *(const f32x4*)(r0 + kPartBytes + 16);
             }
-            // (One block: all sixteen k-steps of the score operand now; two
-            // blocks: the first eight now, the rest after their products.)
-            bf16x8 av[kHH == 2 ? kSteps / 2 : kSteps];
-            if constexpr (kHH == 2) read_k_half(i + 1, 0, av);
-            else read_k(i + 1, av);
-            if constexpr (kFetch) {
-                copy_part(row, i + 3, P0{});
-                copy_part(row, i + 3, P1{});
-            }
+            bf16x8 av[kSteps];
+            read_k(i + 1, av);
             // Score products of tile i+1 in two halves: the first interleaved
-            // with tile i's partial sums, mask and maximum, the second (after
-            // the rescale decision) with its exponentials.
-            f32x16 snext[kHH];
-#pragma unroll
-            for (int lb = 0; lb < kHH; ++lb) snext[lb] = f32x16{};
+            // with tile i's sums, mask and maximum, the second (after the
+            // rescale decision) with its exponentials.
+            f32x16 snext = f32x16{};
             constexpr int kHalf = kSteps / 2;
 #pragma unroll
-            for (int j = 0; j < kHalf; ++j)
+            for (int j = 0; j < kHalf; ++j) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], snext, 0, 0, 0);
+            float sv[8];
 #pragma unroll
-                for (int lb = 0; lb < kHH; ++lb)
-                    snext[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[lb][j], snext[lb], 0, 0, 0);
-            // Scores of tile i: own partial + the other wave's (commutative,
-            // so with one block both waves get the same sum).
-            float sv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r] = sacc[kOwn][r] + part[r >> 2][r & 3];
+            for (int k = 0; k < 8; ++k) sv[k] = pa[k >> 2][k & 3] + pb2[k >> 2][k & 3];
             {
-                const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i) >> key_shift;
+                const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i) >> (8 * g);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sv[r] = ((mine >> (8 * (r >> 2) + (r & 3))) & 1u) ? sv[r] : -INFINITY;
+                for (int k = 0; k < 8; ++k) sv[k] = ((mine >> k) & 1u) ? sv[k] : -INFINITY;
             }
             float smax = sv[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) smax = fmaxf(smax, sv[r]);
+            for (int k = 1; k < 8; ++k) smax = fmaxf(smax, sv[k]);
             const float tmax = smax * sl2;  // scale > 0: the maximum commutes with it
 #pragma unroll
-            for (int j = 0; j < kHalf * kHH; ++j) {
+            for (int j = 0; j < kHalf; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x402, kHH == 2 ? 2 : 5, 0);  // then VALU
+                __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // then VALU
             }
             // The running reference m_run (scaled units) moves only when a
             // score exceeds it by more than 2^8 (probabilities stay <= 256);
             // the PV waves rescale their accumulators by the factor published
-            // with this tile's P.  l_run is this lane's share of the
-            // denominator; the two shares are added at the end.
+            // with this tile's P.
             alpha_out = 1.f;
             if (__any(tmax > m_run + kRescaleLog2)) {
-                const float hmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // the head's tile maximum
+                float hmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                hmax = fmaxf(hmax, __shfl_xor(hmax, 32));  // the head's tile maximum (its four lanes)
                 const bool grow = hmax > m_run + kRescaleLog2;
                 const float m_target = grow ? hmax : m_run;
                 const float alpha = fast_exp2(m_run - m_target);  // 0 while nothing was accumulated
@@ -1409,65 +1394,56 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
                 alpha_out = m_run == -INFINITY ? 1.f : alpha;  // nothing accumulated yet: nothing to rescale
                 m_run = m_target;
             }
-            if constexpr (kHH == 2) read_k_half(i + 1, 1, av);  // the second eight k-steps
 #pragma unroll
             for (int j = 0; j < kHalf; ++j)
-#pragma unroll
-                for (int lb = 0; lb < kHH; ++lb)
-                    snext[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kHH == 2 ? j : kHalf + j], qf[lb][kHalf + j], snext[lb], 0, 0, 0);
+                snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kHalf + j], qf[kHalf + j], snext, 0, 0, 0);
             const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+            float pr[8];
             float psum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pr = fast_exp2(fmaf(sv[r], sl2, neg_m));
-                psum += pr;
-                pb[r >> 3][r & 7] = (__bf16)pr;
+            for (int k = 0; k < 8; ++k) {
+                pr[k] = fast_exp2(fmaf(sv[k], sl2, neg_m));
+                psum += pr[k];
             }
             l_run += psum;
+            p_lo = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+            p_hi = u32x2{pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
 #pragma unroll
-            for (int j = 0; j < kHalf * kHH; ++j) {
+            for (int j = 0; j < kHalf; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x402, kHH == 2 ? 2 : 4, 0);  // then VALU / transcendental
+                __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // then VALU / transcendental
             }
-            if constexpr (kFetch) {
-                copy_part(row, i + 3, P2{});
-                copy_part(row, i + 3, P3{});
-            }
-#pragma unroll
-            for (int lb = 0; lb < kHH; ++lb) sacc[lb] = snext[lb];
+            sacc = snext;
         };
-        int i = 0;
-        for (; i + 3 < n_tiles; ++i) iteration(i, std::true_type{});
-        for (; i < n_tiles; ++i) iteration(i, std::false_type{});
+        for (int i = 0; i < n_tiles; ++i) iteration(i);
 
         // The last tile's P, the output scale of every head and lse.
         if (n_tiles > 0) publish(xb_end, false, true);
-        if (kHH == 2 || d == 0) {
-            const float l_tot = l_run + __shfl_xor(l_run, 32);  // both halves of the head's keys
-            const int my_head = it.hb * kHeads + sb * 32 + (l & 31);
-            const bool head_ok = my_head < a.H;
-            float f = 0.f, lse2 = -INFINITY;
-            if (a.splits == 1) {
-                const float sig = a.sink != nullptr && head_ok ? sink_raw * kLog2e : -INFINITY;
-                const float M = fmaxf(m_run, sig);
-                if (M != -INFINITY) {
-                    const float em = fast_exp2(m_run - M);
-                    const float den = l_tot * em + fast_exp2(sig - M);
-                    f = em / den;
-                    lse2 = M + fast_log2(den);
-                }
-            } else if (l_tot > 0.f) {
-                f = 1.f / l_tot;
-                lse2 = m_run + fast_log2(l_tot);
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);  // all 32 keys of the head
+        const int my_head = it.hb * kHeads + hs;
+        const bool head_ok = my_head < a.H;
+        float f = 0.f, lse2 = -INFINITY;
+        if (a.splits == 1) {
+            const float sig = a.sink != nullptr && head_ok ? sink_raw * kLog2e : -INFINITY;
+            const float M = fmaxf(m_run, sig);
+            if (M != -INFINITY) {
+                const float em = fast_exp2(m_run - M);
+                const float den = l_tot * em + fast_exp2(sig - M);
+                f = em / den;
+                lse2 = M + fast_log2(den);
             }
-            if (l < 32) {
-                s_f[sb * 32 + l] = f;
-                if (head_ok) {
-                    if (a.splits == 1) {
-                        if (a.lse != nullptr) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
-                    } else {
-                        a.ws_lse[((int64_t)it.t * a.splits + it.s) * a.H + my_head] = lse2;
-                    }
+        } else if (l_tot > 0.f) {
+            f = 1.f / l_tot;
+            lse2 = m_run + fast_log2(l_tot);
+        }
+        if (l < 16) {
+            s_f[hs] = f;
+            if (head_ok) {
+                if (a.splits == 1) {
+                    if (a.lse != nullptr) a.lse[(int64_t)it.t * a.lse_s0 + my_head] = lse2 * kLn2;
+                } else {
+                    a.ws_lse[((int64_t)it.t * a.splits + it.s) * a.H + my_head] = lse2;
                 }
             }
         }
@@ -1486,9 +1462,9 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
         auto pv_step = [&](const uint8_t* xb) __attribute__((always_inline)) {
 #pragma unroll
             for (int hb = 0; hb < kHH; ++hb) {
-                const bf16x8* pp = (const bf16x8*)(xb + kXP + hb * 2048) + 2 * l;
+                const bf16x8* pp = (const bf16x8*)(xb + kXP) + 2 * l;
                 const bf16x8 p0 = pp[0], p1 = pp[1];
-                const float alpha = ((const float*)(xb + kXF + hb * 256))[l];
+                const float alpha = ((const float*)(xb + kXF))[l & 31];
                 if (__any(alpha != 1.f)) scale_accumulators(oacc[hb], alpha);
 #pragma unroll
                 for (int mb = 0; mb < kMb; ++mb) {
@@ -1497,22 +1473,55 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
                 }
             }
         };
+        // The score wave of the same parity (whose rows this wave copies from
+        // tile 3 on, with the same lane offsets): its row addresses, and its
+        // copy of one tile part, into its rows' place in the stage.
+        uint64_t ad_s[kAdRegs];
+#pragma unroll
+        for (int u = 0; u < kAdRegs; ++u) ad_s[u] = s_ad[(d * kAdRegs + u) * 64 + l];
+        auto tile_row_s = [&](int tile) -> const uint8_t* {
+            const int u = min(tile >> 3, kMaxSplitKeys / 256 - 1);
+            const uint64_t au = u == 0 ? ad_s[0] : (u == 1 ? ad_s[1] : (u == 2 ? ad_s[2] : ad_s[3]));
+            const int src = 4 * (8 * (tile & 7) + dma_row);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)au);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(au >> 32));
+            return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo) + dma_lane_off;
+        };
+        auto copy_part_s = [&](const uint8_t* row, int tile, auto part) {
+            constexpr int kP = decltype(part)::value;
+            const uint32_t dst = lds_addr(&s_tile[tile % kStages][0]) + d * 8192 + kP * 2048;
+            dma16_off<256 * kP>(row, dst);
+            dma16_off<256 * kP + 128>(row, dst + 1024);
+        };
+        const uint8_t* next_row_s = tile_row_s(3);
         auto iteration = [&](int i, auto fetch_tag) __attribute__((always_inline)) {
             constexpr bool kFetch = decltype(fetch_tag)::value;
-            if (kFetch || i + 2 < n_tiles) wait_vmcnt<8>();
-            else wait_vmcnt<0>();
+            // Tile i+1 (copies of tile i+2 may still be in flight: 8 for tile
+            // 2, from the prologue; 16 for a later one).
+            if (i + 2 < n_tiles) {
+                if (i == 0) wait_vmcnt<8>();
+                else wait_vmcnt<16>();
+            } else {
+                wait_vmcnt<0>();
+            }
             const uint8_t* xb = xbuf(i);
             __syncthreads();  // see the score waves' loop
             const uint8_t* row = next_row;
+            const uint8_t* row_s = next_row_s;
             if constexpr (kFetch) {
                 next_row = tile_row(i + 4);
+                next_row_s = tile_row_s(i + 4);
                 copy_part(row, i + 3, P0{});
+                copy_part_s(row_s, i + 3, P0{});
                 copy_part(row, i + 3, P1{});
+                copy_part_s(row_s, i + 3, P1{});
             }
             if (i > 0) pv_step(xb);  // tile i-1, with its operand read last iteration
             if constexpr (kFetch) {
                 copy_part(row, i + 3, P2{});
+                copy_part_s(row_s, i + 3, P2{});
                 copy_part(row, i + 3, P3{});
+                copy_part_s(row_s, i + 3, P3{});
             }
             read_kt(i, kt);  // tile i (landed at barrier i-1): its stage is read for the last time
         };

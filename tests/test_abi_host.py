@@ -173,6 +173,9 @@ def test_plan_is_host_only_and_sane():
     # 128 rows x two 32-head blocks fill the chip without splitting keys: the role kernel, one split
     assert L.dsv4_attn_plan(128, 64, 4, 128, 512, 64, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 3 and s.value == 1
+    # 64 rows x two 32-head blocks fill the chip with two splits: the role kernel
+    assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 3 and s.value == 2
     assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 5  # packed FP8 always runs the FP8 kernel
     for forced in (1, 2, 3, 4):
