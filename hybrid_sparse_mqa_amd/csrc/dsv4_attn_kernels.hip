@@ -2010,8 +2010,17 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     // Every kernel argument used below, in one round of scalar loads.
     asm volatile("" ::"s"(a.H), "s"(a.splits), "s"(a.ws_lse), "s"(a.ws_o), "s"(a.sink), "s"(a.zero_row), "s"(a.out),
                  "s"(a.out_s0), "s"(a.out_s1), "s"(a.lse), "s"(a.lse_s0));
-    const int t = blockIdx.x;
-    const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+    // Work item (row t, heads 4q .. 4q+3) of workgroup b, laid out like the
+    // split kernels' items (decode_item): XCD b & 7 takes a contiguous run of
+    // items, so a row's merge runs on the XCD that wrote its partials.
+    const int n_quads = (a.H + 3) >> 2;
+    const int n = a.T * n_quads;
+    const int per_xcd = (n + 7) >> 3;
+    const int slot = blockIdx.x >> 3;
+    const int raw = (blockIdx.x & 7) * per_xcd + slot;
+    if (slot >= per_xcd || raw >= n) return;
+    const int t = raw / n_quads;
+    const int head = (raw - t * n_quads) * 4 + (threadIdx.x >> 6);
     const int l = threadIdx.x & 63;
     if (head >= a.H) return;
     const int S = a.splits;
@@ -2112,7 +2121,8 @@ hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream
 }
 
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.T, (unsigned)((a.H + 3) / 4));
+    const int64_t n = (int64_t)a.T * ((a.H + 3) / 4);  // (row, 4 heads) items; 8 XCDs x ceil(n / 8) workgroups
+    const dim3 grid((unsigned)(8 * ((n + 7) / 8)));
     if (a.splits <= 2)
         hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(256), 0, stream, a);
     else if (a.splits <= 4)
