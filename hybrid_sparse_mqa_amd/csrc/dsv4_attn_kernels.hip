@@ -1494,8 +1494,9 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
             dma16_off<256 * kP + 128>(row, dst + 1024);
         };
         const uint8_t* next_row_s = tile_row_s(3);
-        auto iteration = [&](int i, auto fetch_tag) __attribute__((always_inline)) {
+        auto iteration = [&](int i, auto fetch_tag, auto first_tag) __attribute__((always_inline)) {
             constexpr bool kFetch = decltype(fetch_tag)::value;
+            constexpr bool kFirst = decltype(first_tag)::value;  // i == 0: no earlier tile to multiply
             // Tile i+1 (copies of tile i+2 may still be in flight: 8 for tile
             // 2, from the prologue; 16 for a later one).
             if (i + 2 < n_tiles) {
@@ -1516,7 +1517,7 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
                 copy_part(row, i + 3, P1{});
                 copy_part_s(row_s, i + 3, P1{});
             }
-            if (i > 0) pv_step(xb);  // tile i-1, with its operand read last iteration
+            if constexpr (!kFirst) pv_step(xb);  // tile i-1, with its operand read last iteration
             if constexpr (kFetch) {
                 copy_part(row, i + 3, P2{});
                 copy_part_s(row_s, i + 3, P2{});
@@ -1525,9 +1526,15 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
             }
             read_kt(i, kt);  // tile i (landed at barrier i-1): its stage is read for the last time
         };
+        // Iteration 0 is peeled (no PV product yet), so that every loop
+        // iteration runs the product unconditionally: a path around it would
+        // make the compiler copy all accumulators out of the AGPRs on every
+        // iteration, for the loop's exit.
         int i = 0;
-        for (; i + 3 < n_tiles; ++i) iteration(i, std::true_type{});
-        for (; i < n_tiles; ++i) iteration(i, std::false_type{});
+        if (n_tiles > 3) iteration(0, std::true_type{}, std::true_type{});
+        else if (n_tiles > 0) iteration(0, std::false_type{}, std::true_type{});
+        for (i = 1; i + 3 < n_tiles; ++i) iteration(i, std::true_type{}, std::false_type{});
+        for (; i < n_tiles; ++i) iteration(i, std::false_type{}, std::false_type{});
 
         __syncthreads();  // see the score waves
         if (n_tiles > 0) pv_step(xb_end);
