@@ -180,16 +180,6 @@ __device__ __forceinline__ void fetch_args(const AttnArgs& a) {
                  "s"(a.head_blocks), "s"(a.n_items), "s"(a.ext_pages), "s"(a.zero_row));
 }
 
-// Q^T as the B operand of S^T: lane holds head (l & 31) of the wave's half,
-// dims 256*dh + 16*j + 8*(l >> 5) .. +8 for k-step j.  Heads past H read head
-// H-1 (unconditional loads, no branch around them); their scores and outputs
-// are never written.
-__device__ __forceinline__ void load_q(const AttnArgs& a, int t, int head, int dh, int l, bf16x8 (&qf)[16]) {
-    const uint16_t* qrow = a.q + (int64_t)t * a.q_s0 + (int64_t)min(head, a.H - 1) * a.q_s1 + dh * 256 + 8 * (l >> 5);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
-}
-
 // Slot list of keys [k0, k0 + n_here) of row t into s_slot.  One round of
 // loads fetches the request's extra page-table row (cached in LDS) and, per
 // key, its window page entry or its C4 index; every address is clamped into
@@ -1938,12 +1928,41 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 
     if (n_here > 0) issue_loads(0);
-    bf16x8 qf[16];
-    load_q(a, it.t, my_head, dh, l, qf);
-    // Tile 0 and Q are both needed before the first product; waiting for
-    // them here tells the compiler Q is in, so that it does not wait for Q
-    // (and for the next tile's loads issued after it) inside the loop.
+    // Q of the block's 64 heads, copied into LDS with whole-line copies (the
+    // score operand's register layout, one head per lane, would make every
+    // direct load touch 32 lines for 32 bytes each, and the splits of a row
+    // all load the same Q): wave w copies heads 16w .. 16w+15, one 1 KiB row
+    // per instruction, lane i the 16-byte chunk i ^ (h & 15) of head h, into
+    // s_krow (heads 0..31) and s_kt (heads 32..63), which the first tile
+    // overwrites only after Q has been read.  Chunk c of head h then sits at
+    // 16*(c ^ (h & 15)) in its 1 KiB slot.
+    auto q_slot = [&](int h) -> uint8_t* { return h < 32 ? s_krow + h * 1024 : s_kt + (h - 32) * 1024; };
+    {
+        const int head0 = it.hb * kWideHeadsPerBlock;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const int h = 16 * w + n;
+            const uint16_t* src = a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(head0 + h, a.H - 1) * a.q_s1 + 8 * (l ^ (h & 15));
+            dma16_off<0>(src, lds_addr(q_slot(h)));
+        }
+    }
+    // Tile 0 and Q are both needed before the first product; the explicit
+    // wait also tells the compiler that tile 0's loads are in, so that it
+    // does not wait for them (and for the next tile's loads issued after
+    // them) inside the loop.
     wait_vmcnt<0>();
+    __syncthreads();  // Q in LDS
+    bf16x8 qf[16];
+    {
+        const int hl = hh * 32 + (l & 31);
+        const uint8_t* qs = q_slot(hl);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int c = 32 * dh + 2 * j + (l >> 5);
+            qf[j] = *(const bf16x8*)(qs + 16 * (c ^ (l & 15)));
+        }
+    }
+    __syncthreads();  // every wave has read Q: the first tile may overwrite it
     for (int tb = 0; tb < n_here; tb += kTileKeys) {
         commit_tile();
         if (tb + kTileKeys < n_here) issue_loads(tb + kTileKeys);
