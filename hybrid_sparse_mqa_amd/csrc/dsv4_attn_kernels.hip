@@ -86,18 +86,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// Four OCP E4M3FN codes (one per byte) -> four floats, exactly.  The code's
-// exponent/mantissa bits are moved into an IEEE half (same layout, bias 15
-// instead of 7): value(half) * 2^8 = value(e4m3), subnormals included.
-__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
-    const uint32_t even = w & 0x00FF00FFu;          // bytes 0 and 2
-    const uint32_t odd = (w >> 8) & 0x00FF00FFu;    // bytes 1 and 3
-    const uint32_t he = ((even & 0x00800080u) << 8) | ((even & 0x007F007Fu) << 7);
-    const uint32_t ho = ((odd & 0x00800080u) << 8) | ((odd & 0x007F007Fu) << 7);
-    f[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(he & 0xFFFF));
-    f[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(he >> 16));
-    f[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ho & 0xFFFF));
-    f[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ho >> 16));
+// Two OCP E4M3FN codes (bytes 0, 1 of w, or bytes 2, 3 with kHi) -> two
+// bf16 in one word, the first code in the low half: the gfx950 conversion
+// instruction with scale 1.  Every E4M3 value, subnormals included, is exact
+// in bf16 (3 mantissa bits, exponents 2^-9 .. 2^8).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
 }
 
 struct TileRegs {
@@ -1903,11 +1898,8 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             if (l < 56) {
-                float lo[4], hi[4];
-                e4m3x4_to_f32(pre.v[e][0], lo);
-                e4m3x4_to_f32(pre.v[e][1], hi);
-                rows[e] = u32x4{pack_bf16x2(lo[0] * 256.0f, lo[1] * 256.0f), pack_bf16x2(lo[2] * 256.0f, lo[3] * 256.0f),
-                                pack_bf16x2(hi[0] * 256.0f, hi[1] * 256.0f), pack_bf16x2(hi[2] * 256.0f, hi[3] * 256.0f)};
+                rows[e] = u32x4{e4m3x2_to_bf16x2<false>(pre.v[e][0]), e4m3x2_to_bf16x2<true>(pre.v[e][0]),
+                                e4m3x2_to_bf16x2<false>(pre.v[e][1]), e4m3x2_to_bf16x2<true>(pre.v[e][1])};
             } else {
                 rows[e] = pre.v[e];
             }

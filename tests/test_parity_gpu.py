@@ -372,6 +372,31 @@ def test_fp8_all_codes(orc):
     G.compare(out, lse, ro, rl, what="fp8 codes")
 
 
+def test_fp8_decode_bit_exact(orc):
+    """One visible key (position 0, window only), no sink, per-token scale 1:
+    every head's softmax weight is exactly 1, so every output row is the key's
+    dequantised row.  Its 448 codes cycle through all 254 finite E4M3 codes
+    (subnormals and both zeros included), each of which is exact in bf16, so
+    the output must equal the oracle's value exactly, not within tolerance."""
+    from synth.workloads import FP8_ROW_BYTES, FP8_SCALE_OFFSET
+
+    case = make_case(seq_lens=[1], n_q=1, H=64, R=0, kv="fp8", sink=False, seed=5)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    page = int(case.swa_page_table[0, 0])
+    rec = 0  # position 0 is record 0 of the request's first page
+    base = rec * FP8_ROW_BYTES
+    case.swa_pool[page, base:base + 448] = np.resize(codes, 448)
+    case.swa_pool[page, FP8_SCALE_OFFSET + 4 * rec:FP8_SCALE_OFFSET + 4 * rec + 4] = \
+        np.array([1.0], np.float32).view(np.uint8)
+    out, _ = G.run_forward(case)
+    ro, _, _ = orc.attention(case)
+    got = out.float().cpu().numpy()
+    want = torch.from_numpy(ro.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(want, ro.astype(np.float32)), "the expected rows are not bf16-exact"
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} values differ, first at {bad[:4].tolist()}"
+
+
 # --------------------------------------------------------------------------
 # shapes and modes
 # --------------------------------------------------------------------------
