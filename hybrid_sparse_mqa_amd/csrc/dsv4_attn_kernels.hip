@@ -1523,35 +1523,45 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
 
         __syncthreads();  // see the score waves
         if (n_tiles > 0) pv_step(xb_end);
-        // Rows of head 32*hb + (l & 31): O^T register r of dim block mb holds
-        // dim 256*d + 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3); 16-byte chunk
-        // c of a row is stored at chunk c ^ (row & 31) of its 1 KiB slot.
+        // The unscaled fp32 rows, straight from the accumulators, into the
+        // ring (free now): O^T register r of dim block mb holds dim 256*d +
+        // 32*mb + 8*(r >> 2) + 4*(l >> 5) + (r & 3) of head l & 31, i.e. 16-byte
+        // chunk c = 64d + 8mb + 2(r >> 2) + (l >> 5) of the head's 2 KiB row,
+        // stored at chunk c ^ (head & 15) (conflict-free over 16 heads).  The
+        // scaling and the conversion are left to all four waves below.
+        const int r = l & 31;
+        uint8_t* base = &s_tile[0][0] + r * 2048;
 #pragma unroll
-        for (int hb = 0; hb < kHH; ++hb) {
-            const float f = s_f[hb * 32 + (l & 31)];
-            const int r = l & 31;
-            uint8_t* base = &s_tile[0][0] + (hb * 32 + r) * 1024 + 8 * (l >> 5);
+        for (int mb = 0; mb < kMb; ++mb) {
 #pragma unroll
-            for (int mb = 0; mb < kMb; ++mb) {
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int c = 32 * d + 4 * mb + qd;
-                    const f32x16& o = oacc[hb][mb];
-                    *(u32x2*)(base + 16 * (c ^ r)) = u32x2{pack_bf16x2(o[4 * qd] * f, o[4 * qd + 1] * f),
-                                                           pack_bf16x2(o[4 * qd + 2] * f, o[4 * qd + 3] * f)};
-                }
+            for (int qd = 0; qd < 4; ++qd) {
+                const int c = 64 * d + 8 * mb + 2 * qd + (l >> 5);
+                const f32x16& o = oacc[0][mb];
+                *(f32x4*)(base + 16 * (c ^ (r & 15))) = f32x4{o[4 * qd], o[4 * qd + 1], o[4 * qd + 2], o[4 * qd + 3]};
             }
         }
     }
     __syncthreads();  // rows staged
-    // Wave w stores rows w*kRows .. +kRows (heads past H skipped); lane l
-    // moves the row's 16-byte chunk l.  All LDS reads go out first.
+    // Wave w scales, converts and stores rows w*kRows .. +kRows (heads past H
+    // skipped); lane l takes dims 8l .. 8l+7 (chunks 2l, 2l+1) of a row.  All
+    // LDS reads go out first.
     constexpr int kRows = kHeads / 4;
     u32x4 v[kRows];
+    {
+        f32x4 x[kRows][2];
+        float f[kRows];
 #pragma unroll
-    for (int e = 0; e < kRows; ++e) {
-        const int r = kRows * w + e;
-        v[e] = *(const u32x4*)(&s_tile[0][0] + r * 1024 + 16 * (l ^ (r & 31)));
+        for (int e = 0; e < kRows; ++e) {
+            const int r = kRows * w + e;
+            const uint8_t* row = &s_tile[0][0] + r * 2048;
+            x[e][0] = *(const f32x4*)(row + 16 * ((2 * l) ^ (r & 15)));
+            x[e][1] = *(const f32x4*)(row + 16 * ((2 * l + 1) ^ (r & 15)));
+            f[e] = s_f[r];
+        }
+#pragma unroll
+        for (int e = 0; e < kRows; ++e)
+            v[e] = u32x4{pack_bf16x2(x[e][0][0] * f[e], x[e][0][1] * f[e]), pack_bf16x2(x[e][0][2] * f[e], x[e][0][3] * f[e]),
+                         pack_bf16x2(x[e][1][0] * f[e], x[e][1][1] * f[e]), pack_bf16x2(x[e][1][2] * f[e], x[e][1][3] * f[e])};
     }
     const int head0 = it.hb * kHeads + kRows * w;
     const int n_rows = min(kRows, a.H - head0);  // uniform
