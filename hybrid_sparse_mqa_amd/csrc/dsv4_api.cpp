@@ -222,18 +222,14 @@ dsv4_status ensure_zero_row(DeviceState* d) {
     return DSV4_OK;
 }
 
-// Kernel layout.  Heads <= 16: the 16-head kernel (no padding of heads).
-// Otherwise the 64-head kernel, whose waves read each key tile for twice as
-// many heads per LDS read as the 32-head kernel; but when the rows in 64-head
-// blocks fill less than a quarter of the chip, the 32-head kernel, which
-// needs half as many key splits for the same parallelism (fewer partials
-// to write and merge).  Measured on MI355X (rocprofv3, split + merge kernel):
-// C4 decode 32 rows x 640 keys 16.1 + 3.9 us (32-head, 4 splits) vs
-// 17.2 + 4.8 us (64-head, 5 splits); C128 decode 64 rows x 1152 keys
-// 25.4 + 5.5 us (64-head, 4 splits) vs 31.2 + 4.0 us (32-head, 2 splits);
-// C4 verify 128 rows 27.3 + 5.8 us (64-head, 2 splits) vs 34.5 us (32-head,
-// no split).
-Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
+// Kernel layout: FP8 pools -> the FP8 kernel; otherwise the variant forced
+// by dsv4_attn_set_kernel, else the 16-head kernel for at most 16 heads (no
+// padding of heads) and the 32-head score/PV role kernel above that.
+// Measured on MI355X (graph replay, split + merge per call), role kernel vs
+// the best dim-split kernel: C4 decode 32 rows x 640 keys 16.8 vs 17.1 us
+// (32-head, four splits each); C128 decode 64 rows x 1152 keys 30.9 vs
+// 33.2 us (64-head, four splits); C4 verify 128 rows 28.6 vs 31.0 us.
+Layout choose_layout(int32_t H, bool fp8) {
     if (fp8) return Layout::kFp8;
     switch (g_force_kernel) {
         case DSV4_KERNEL_H16: return Layout::kNarrow;
@@ -243,15 +239,12 @@ Layout choose_layout(int cus, int32_t T, int32_t H, bool fp8) {
         default: break;
     }
     if (H <= kNarrowHeadsPerBlock) return Layout::kNarrow;
-    // Enough rows for one 32-head workgroup per compute unit with at most
-    // two key splits: the score/PV role kernel, whose tile loop is the
-    // fastest (measured: C4 verify, 128 rows x 64 heads, unsplit; C128
-    // decode, 64 rows, two splits).  Otherwise 64-head blocks when rows x
-    // splits fill the chip with splits of at least a few tiles, else 32-head
-    // blocks (measured: C4 decode, 32 rows).
-    if (2 * (int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) >= cus) return Layout::kRoles32;
-    const int64_t wide_rows = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
-    return wide_rows * 4 < cus ? Layout::kWide32 : Layout::kWide;
+    // The score/PV role kernel, with 32-head blocks, is the fastest measured
+    // on every bf16 workload with more heads: C4 decode (32 rows, four
+    // splits), C128 decode (64 rows, two splits) and C4 verify (128 rows,
+    // unsplit).  The 32- and 64-head dim-split kernels stay available through
+    // dsv4_attn_set_kernel.
+    return Layout::kRoles32;
 }
 
 int32_t heads_per_block(Layout layout) {
@@ -467,7 +460,7 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
         DeviceState* d = device_state(dev);
         if (d) cus = d->cus;
     }
-    const Layout layout = choose_layout(cus, num_rows, num_heads, kv_fp8 != 0);
+    const Layout layout = choose_layout(num_heads, kv_fp8 != 0);
     plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages),
                 layout, splits, keys_per_split);
     if (kernel != nullptr) *kernel = kernel_id(layout);
@@ -613,7 +606,7 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     a.T = (int32_t)T;
     a.H = (int32_t)H;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const Layout layout = choose_layout(d->cus, a.T, a.H, swa.fp8);
+    const Layout layout = choose_layout(a.H, swa.fp8);
     plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), layout, &a.splits,
                 &a.chunk);
     a.head_blocks = (int32_t)((H + heads_per_block(layout) - 1) / heads_per_block(layout));

@@ -167,9 +167,12 @@ def test_plan_is_host_only_and_sane():
     assert c.value == 64 and s.value == 10
     assert L.dsv4_attn_set_split_keys(0) == 0
     k = ctypes.c_int32()
-    # 32 rows of 64 heads fill a quarter of the chip at most: a 32-head kernel
+    # bf16 with more than 16 heads: the 32-head role kernel, splitting keys to fill the chip
     assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
-    assert k.value == 2  # DSV4_KERNEL_H32 (without a GPU the plan assumes 256 compute units)
+    assert k.value == 3 and s.value == 4  # (without a GPU the plan assumes 256 compute units)
+    # 16 heads or fewer: the 16-head kernel
+    assert L.dsv4_attn_plan(32, 16, 4, 128, 512, 8, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 1
     # 128 rows x two 32-head blocks fill the chip without splitting keys: the role kernel, one split
     assert L.dsv4_attn_plan(128, 64, 4, 128, 512, 64, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 3 and s.value == 1
