@@ -212,6 +212,101 @@ def record_traffic(config: int, split_keys: int, fetch_dir: str, write_dir: str,
     return 0
 
 
+def bench_pack(args) -> int:
+    """The KV store kernel (dsv4_kv_pack_fp8) on its own: `args.pack` bf16 K
+    rows quantised into packed FP8 records at a random permutation of the
+    pool's slots, timed as one HIP graph replay of `steps` calls rotating over
+    enough input copies that they do not stay in the MALL."""
+    import torch
+
+    from hybrid_sparse_mqa_amd import dsv4_kv_pack_fp8
+    from synth.workloads import FP8_PAGE_BYTES, _to_bf16_bits
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = int(args.pack)
+    pages = (n + 255) // 256
+    rng = np.random.default_rng(0)
+    k = rng.standard_normal((n, 512), dtype=np.float32)
+    k *= np.exp(rng.uniform(np.log(1e-3), np.log(1e2), (n, 1))).astype(np.float32)
+    k_bits = _to_bf16_bits(k)
+    slots = rng.permutation(pages * 256)[:n].astype(np.int32)
+    set_bytes = n * 1024 + pages * FP8_PAGE_BYTES
+    n_sets = int(min(16, max(2, -(-3 * MALL_BYTES // set_bytes))))
+    kt = torch.from_numpy(k_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    st = torch.from_numpy(slots).to(dev)
+    sets = [(kt if i == 0 else kt.clone(), torch.zeros((pages, FP8_PAGE_BYTES), dtype=torch.uint8, device=dev))
+            for i in range(n_sets)]
+    # Algorithmic bytes per call: K rows read, slots read, records and scales written.
+    nbytes = n * (1024 + 4 + 576 + 4)
+
+    def step(i):
+        kk, pool = sets[i % n_sets]
+        dsv4_kv_pack_fp8(kk, st, pool)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                step(i)
+        g.replay()  # warm replay (untimed)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "KV store rows/s (bf16 K -> packed FP8 records) + achieved HBM GB/s (% peak)",
+        "value": n / (ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8",
+        "data": "synthetic",
+        "config": {"workload": f"fp8_kv_pack_n{n}", "rows": n, "pages": pages, "input_sets": n_sets,
+                   "cache": "cold-rotated", "timed": "HIP graph replay, events around it on the kernels' stream",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "pack_fp8_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        o = oracle.Oracle()
+        m = min(n, 2048)
+        pool = np.zeros(((m + 255) // 256 + 1, FP8_PAGE_BYTES), np.uint8)
+        sl = np.arange(m, dtype=np.int32)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds / 2:
+            o.pack_fp8(k_bits[:m], sl, pool)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": reps * m / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"{m} of {n} rows x {reps} repetitions (C, one thread), {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +321,8 @@ def main() -> int:
                     help="force a bf16 split-kernel variant (DSV4_KERNEL_*, 0 = library choice)")
     ap.add_argument("--sample-every", type=int, default=10,
                     help="time the kernels of every N-th call of the timed replay with HIP events")
+    ap.add_argument("--pack", type=int, default=0, metavar="ROWS",
+                    help="time the FP8 KV store kernel on ROWS rows instead of the attention")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -243,6 +340,9 @@ def main() -> int:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the attention shards by "
               "request, so N GPUs run N independent copies of this benchmark)", file=sys.stderr)
         return 2
+
+    if args.pack:
+        return bench_pack(args)
 
     import torch
 

@@ -80,6 +80,15 @@ def dsv4_attn_gather_slots(
     return slots, counts
 
 
+def dsv4_kv_pack_fp8(k: torch.Tensor, slots: torch.Tensor, pool: torch.Tensor, stream: Optional[int] = None) -> None:
+    """Quantise K rows (bf16 [n, 512]) into the packed FP8 pool (uint8
+    [pages, 149504], written in place) at ``slots`` (int32 [n], < 0 skips)."""
+    L = N.load()
+    descs = [N.describe(x) for x in (k, slots, pool)]
+    st = N.stream_handle(k.device) if stream is None else stream
+    N.check(L.dsv4_kv_pack_fp8(*[N.ref(d) for d in descs], ctypes.c_void_p(st)))
+
+
 def dsv4_abi_version() -> int:
     return int(N.load().dsv4_abi_version())
 

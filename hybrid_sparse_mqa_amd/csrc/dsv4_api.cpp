@@ -548,6 +548,46 @@ dsv4_status dsv4_attn_gather_slots(const dsv4_tensor* swa_page_table, const dsv4
     return DSV4_OK;
 }
 
+dsv4_status dsv4_kv_pack_fp8(const dsv4_tensor* k, const dsv4_tensor* slots, const dsv4_tensor* pool, void* stream) {
+    DSV4_TRY(check_tensor("k", k, DSV4_BF16, 2, {-1, DSV4_HEAD_DIM}));
+    const int64_t n = k->shape[0];
+    DSV4_TRY(check_tensor("slots", slots, DSV4_I32, 1, {n}));
+    PoolInfo pi{};
+    DSV4_TRY(check_pool("pool", pool, &pi));
+    if (!pi.fp8) return fail(DSV4_ERR_UNSUPPORTED, "pool: the FP8 store needs a packed FP8 pool (u8 pages)");
+    if (n == 0) return DSV4_OK;
+    if (k->stride[0] % 8 != 0 || !aligned16(k->data))
+        return fail(DSV4_ERR_INVALID, "k: rows must be 16-byte aligned (row stride a multiple of 8)");
+    if (n > 1 && k->stride[0] < DSV4_HEAD_DIM) return fail(DSV4_ERR_INVALID, "k: rows overlap");
+    if (pi.pages < 1) return fail(DSV4_ERR_INVALID, "pool: no pages");
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        DSV4_HIP(hipStreamSynchronize(st));
+        std::vector<int32_t> host;
+        DSV4_TRY(fetch(slots, host, 1, n));
+        std::vector<int32_t> seen;
+        for (int64_t i = 0; i < n; ++i) {
+            if (host[i] < 0) continue;
+            if ((int64_t)host[i] >= pi.pages * DSV4_PAGE_SIZE)
+                return fail(DSV4_ERR_CONTRACT, "slots[%lld] = %d beyond the pool's %lld slots", (long long)i, host[i],
+                            (long long)(pi.pages * DSV4_PAGE_SIZE));
+            seen.push_back(host[i]);
+        }
+        std::sort(seen.begin(), seen.end());
+        if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+            return fail(DSV4_ERR_CONTRACT, "slots: a slot appears twice");
+    }
+    PackArgs p{};
+    p.k = (const uint16_t*)k->data;
+    p.k_s0 = k->stride[0];
+    p.slots = (const int32_t*)slots->data;
+    p.n = n;
+    p.pool = (uint8_t*)pool->data;
+    p.page_bytes = DSV4_FP8_PAGE_BYTES;
+    DSV4_HIP(launch_pack_fp8(p, st));
+    return DSV4_OK;
+}
+
 dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
                               const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
                               const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,

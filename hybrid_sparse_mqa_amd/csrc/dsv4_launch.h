@@ -58,8 +58,20 @@ struct GatherArgs {
     int32_t* counts;  // [T, 2]
 };
 
+// KV store: n K rows (bf16 [n, 512], row stride k_s0) into packed FP8
+// records of the pool at slots[i] (skipped if < 0).
+struct PackArgs {
+    const uint16_t* k;
+    int64_t k_s0;
+    const int32_t* slots;  // [n]
+    int64_t n;
+    uint8_t* pool;         // [pages, page_bytes]
+    int64_t page_bytes;
+};
+
 hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& g, hipStream_t stream);
+hipError_t launch_pack_fp8(const PackArgs& p, hipStream_t stream);
 
 }  // namespace dsv4

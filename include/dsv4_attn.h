@@ -126,6 +126,31 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
                               void* stream);
 
 /*
+ * dsv4_kv_pack_fp8 -- the KV store in front of the attention: n new K rows
+ * (with RoPE applied; V = K) quantised into packed FP8 records at given slots
+ * (the cache write of the walk-through page, section 3; the 584-byte FP8 +
+ * bf16 record of the test-matrix page, "packed FP8 nope + BF16 rope").
+ *
+ *  k      bf16 [n, 512], rows 16-byte aligned (row stride a multiple of 8)
+ *  slots  i32 [n]: physical slot of row i (page slot/256, record slot%256), or
+ *         < 0 to skip the row; the non-negative slots must be distinct and
+ *         below pages*256 (a caller contract, checked with DSV4_VALIDATE=1)
+ *  pool   DSV4_U8 [pages, 149504] packed FP8 pool (format above), written:
+ *         for each row, scale = max |k[0..447]| / 448 in fp32 (1 if all
+ *         those dims are zero); record bytes 0..447 = the OCP E4M3FN code of
+ *         k[d] / scale (fp32 division), rounded to the nearest finite value,
+ *         ties to the even code, saturating at +-448, sign from the sign bit;
+ *         bytes 448..575 = k[448..511] unchanged; the page's fp32 scale of the
+ *         record = scale.  Nothing else in the pool is touched.  k must be
+ *         finite.
+ *  stream hipStream_t
+ *
+ * A pool written here is read back exactly by dsv4_attn_forward (code x
+ * scale).  Returns DSV4_ERR_UNSUPPORTED for a bf16 pool.
+ */
+dsv4_status dsv4_kv_pack_fp8(const dsv4_tensor* k, const dsv4_tensor* slots, const dsv4_tensor* pool, void* stream);
+
+/*
  * dsv4_attn_gather_slots -- the paged gather stage on its own: for every row,
  * the physical slots the attention reads, in canonical order (SWA positions
  * ascending, then C4 entries in index-list order with -1 skipped, or C128

@@ -8,7 +8,9 @@ with gcc and wraps it with ctypes.
 
 Parity status: every function is pinned by ``tests/test_oracle_pins.py``
 (brute force over unpaged logical rows, closed forms, invariants, the worked
-examples of the DSV4 walk-through page, the E4M3FN code table and mutants).
+examples of the DSV4 walk-through page, the E4M3FN code table and mutants);
+the FP8 packer by ``tests/test_oracle_pack.py`` (torch's float8_e4m3fn
+conversion, round-trip error bounds, closed forms, the byte layout, mutants).
 """
 from __future__ import annotations
 
@@ -82,6 +84,10 @@ class Oracle:
         L.dsv4o_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.dsv4o_e4m3_to_double.restype = ctypes.c_double
         L.dsv4o_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.dsv4o_e4m3_from_float.restype = ctypes.c_uint8
+        L.dsv4o_e4m3_from_float.argtypes = [ctypes.c_float]
+        L.dsv4o_pack_fp8.restype = ctypes.c_int
+        L.dsv4o_pack_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64]
         L.dsv4o_max_threads.restype = ctypes.c_int
         L.dsv4o_mutant.restype = ctypes.c_int
 
@@ -147,6 +153,20 @@ class Oracle:
             if rc:
                 raise self._err()
         return out, lse, lse_ns
+
+    def pack_fp8(self, k_bits: np.ndarray, slots: np.ndarray, pool: np.ndarray) -> None:
+        """Quantise K rows (bf16 bits [n, 512]) into packed FP8 records of
+        ``pool`` (uint8 [pages, 149504], modified in place) at ``slots``."""
+        k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+        slots = np.ascontiguousarray(slots, dtype=np.int32)
+        assert k_bits.ndim == 2 and k_bits.shape[1] == 512 and slots.shape == (k_bits.shape[0],)
+        assert pool.dtype == np.uint8 and pool.flags.c_contiguous and pool.ndim == 2
+        rc = self.lib.dsv4o_pack_fp8(_ptr(k_bits), _ptr(slots), int(k_bits.shape[0]), _ptr(pool), int(pool.shape[0]))
+        if rc:
+            raise self._err()
+
+    def e4m3_from_float(self, x: float) -> int:
+        return int(self.lib.dsv4o_e4m3_from_float(ctypes.c_float(x)))
 
     def bf16_to_double(self, bits: int) -> float:
         return self.lib.dsv4o_bf16_to_double(bits)

@@ -28,6 +28,8 @@
  *    receives k = v): the value of a key is its full 512-wide row.
  *  - Attention sink (test-matrix page, "attention-sink correction"): one extra
  *    virtual key per head whose score is sink[h] and whose value is zero.
+ *  - KV store (walk-through section 3, test-matrix page's packed FP8 record):
+ *    dsv4o_pack_fp8 quantises K rows into packed FP8 records (see there).
  *
  *  out[t,h,:] = sum_k e^{s_k - m} K_k / (sum_k e^{s_k - m} + e^{sink_h - m}),
  *  s_k = scale * <q[t,h,:], K_k>,  lse = m + ln(denominator).
@@ -326,6 +328,80 @@ int dsv4o_attention(const dsv4o_case* c, const int32_t* rows, int32_t nrows, dou
         }
     }
     return failed ? -1 : 0;
+}
+
+/* ---- KV store: the packed FP8 record -------------------------------------- */
+
+/* Nearest finite OCP E4M3FN value to x, by search over the 127 non-negative
+ * finite codes; of two equally near values the one with the even code (even
+ * mantissa) wins; beyond the largest finite value (448) the nearest one is
+ * 448, so large magnitudes saturate.  The sign of the code is the sign bit
+ * of x (-0.0 and negatives that round to zero give 0x80).  x must be finite. */
+uint8_t dsv4o_e4m3_from_float(float x) {
+    uint32_t bits;
+    memcpy(&bits, &x, sizeof bits);
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int code = 0; code < 0x7F; ++code) {
+        const double d = fabs(dsv4o_e4m3_to_double((uint8_t)code) - a);
+#if DSV4O_MUTANT == 13
+        if (d < best_d || (d == best_d && code > best)) {  /* ties away from zero */
+#else
+        if (d < best_d || (d == best_d && (code & 1) == 0)) {
+#endif
+            best = code;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(best | ((bits >> 31) << 7));
+}
+
+/* The cache write of the walk-through page (section 3, k = v) into the packed
+ * FP8 record of the test-matrix page (448 E4M3FN non-rotary codes + 64 bf16
+ * rotary dims + an fp32 per-token scale, 584 bytes/token; the record layout
+ * inside a page is this library's, see dsv4_attn.h).  Row i of k (bf16 bits
+ * [n, 512]) goes to slot slots[i] of the pool, or nowhere if slots[i] < 0:
+ *   scale  = max_d |nope_d| / 448 in float (1 if every nope dim is zero),
+ *   code_d = the E4M3FN code nearest to nope_d / scale (float division),
+ *   rope   = the 64 rotary bf16 values unchanged.
+ * The float divisions are the reading both the oracle and the kernel take,
+ * so that every code is decided from the same value. */
+int dsv4o_pack_fp8(const uint16_t* k, const int32_t* slots, int64_t n, uint8_t* pool, int64_t pool_pages) {
+    for (int64_t i = 0; i < n; ++i) {
+        const int32_t slot = slots[i];
+        if (slot < 0) continue;
+        const int64_t page = slot / O_PAGE, rec = slot % O_PAGE;
+        if (page >= pool_pages) {
+            set_err("pack: slot %ld beyond the pool's %ld pages", (long)slot, (long)pool_pages);
+            return -1;
+        }
+        const uint16_t* row = k + i * O_D;
+        float nope[O_NOPE];
+        float amax = 0.f;
+        for (int d = 0; d < O_NOPE; ++d) {
+            nope[d] = (float)dsv4o_bf16_to_double(row[d]);
+            amax = fmaxf(amax, fabsf(nope[d]));
+        }
+#if DSV4O_MUTANT == 14
+        const float scale = amax > 0.f ? amax / 447.0f : 1.0f;  /* wrong divisor */
+#else
+        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#endif
+        uint8_t* dst = pool + page * O_FP8_PAGE + rec * O_FP8_REC;
+        for (int d = 0; d < O_NOPE; ++d) dst[d] = dsv4o_e4m3_from_float(nope[d] / scale);
+        for (int d = 0; d < O_ROPE; ++d) {
+#if DSV4O_MUTANT == 15
+            const uint16_t v = row[O_NOPE + (d ^ 1)];  /* rotary dims swapped in pairs */
+#else
+            const uint16_t v = row[O_NOPE + d];
+#endif
+            dst[O_NOPE + 2 * d] = (uint8_t)(v & 0xFF);
+            dst[O_NOPE + 2 * d + 1] = (uint8_t)(v >> 8);
+        }
+        memcpy(pool + page * O_FP8_PAGE + O_FP8_SCALES + 4 * rec, &scale, 4);
+    }
+    return 0;
 }
 
 int dsv4o_max_threads(void) {

@@ -149,6 +149,26 @@ def test_gather_slots_argument_errors():
     assert rc == UNSUPPORTED
 
 
+def test_kv_pack_argument_errors():
+    L = N.load()
+    k = desc(N.DSV4_BF16, [4, 512])
+    slots = desc(N.DSV4_I32, [4])
+    pool = desc(N.DSV4_U8, [2, 149504])
+
+    def call(k_, s_, p_):
+        return L.dsv4_kv_pack_fp8(N.ref(k_), N.ref(s_), N.ref(p_), None)
+
+    assert call(desc(N.DSV4_F32, [4, 512]), slots, pool) == INVALID
+    assert call(desc(N.DSV4_BF16, [4, 448]), slots, pool) == INVALID
+    assert call(k, desc(N.DSV4_I32, [3]), pool) == INVALID
+    assert call(k, slots, desc(N.DSV4_BF16, [512, 512])) == UNSUPPORTED
+    assert "packed FP8" in L.dsv4_last_error().decode()
+    assert call(desc(N.DSV4_BF16, [4, 512], stride=[516, 1]), slots, pool) == INVALID  # rows not 16-byte aligned
+    assert call(k, slots, desc(N.DSV4_U8, [2, 149504], stride=[150000, 1])) == INVALID
+    # no rows: nothing to launch
+    assert call(desc(N.DSV4_BF16, [0, 512]), desc(N.DSV4_I32, [0]), pool) == 0
+
+
 def test_plan_is_host_only_and_sane():
     L = N.load()
     s = ctypes.c_int32()
