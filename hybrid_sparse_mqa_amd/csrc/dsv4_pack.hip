@@ -9,8 +9,8 @@
 // Per row: scale = max |nope| / 448 in float (1 if every non-rotary dim is
 // zero); code = E4M3FN(nope / scale) with the division in float, rounded to
 // the nearest finite value, ties to the even code, large magnitudes
-// saturating to 448; the rotary dims are copied.  HBM-bound: 1 KiB read and
-// 580 bytes written per row, one wave per row.
+// saturating to 448; the rotary dims are copied.  1 KiB read and 580 bytes
+// written per row, one wave per row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,73 +25,115 @@ typedef uint32_t pk_u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRecBytes = 576;
 constexpr int kScaleOffset = 256 * kRecBytes;
 
-// float -> OCP E4M3FN code, round to nearest even, saturating at 448; the
-// sign bit of x becomes the code's (x finite).  Below 2^-6 the codes are the
-// multiples of 2^-9 (subnormals, and 8 -> the smallest normal 2^-6), so the
-// magnitude is rounded to an integer count of 2^-9; above, the float's 23
-// mantissa bits are rounded to 3 (a carry moves into the exponent).
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-    const uint32_t bits = __builtin_bit_cast(uint32_t, x);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const float a = __builtin_fabsf(x);
-    uint32_t mag;
-    if (!(a < 464.0f)) {  // 464 is the midpoint between 448 and the (non-finite) next step
-        mag = 0x7Eu;
-    } else if (a < 0.015625f) {
-        mag = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling; rint rounds half to even
-    } else {
-        uint32_t ab = bits & 0x7FFFFFFFu;
-        ab += 0x7FFFFu + ((ab >> 20) & 1u);
-        mag = min((((ab >> 23) - 120u) << 3) | ((ab >> 20) & 7u), 0x7Eu);
+// Whether a quotient q computed as x * rcp(scale) (within 2 ulp of the
+// correctly rounded x / scale) could round to a different E4M3 code than the
+// exact quotient: only if it lies within a few ulp of a rounding boundary,
+// i.e. of a midpoint between neighbouring codes.  Below 2^-6 the codes are
+// the multiples of 2^-9 (midpoints at odd multiples of 2^-10); above, a
+// midpoint has exactly the top bit set in the 20 mantissa bits that rounding
+// to 3 bits drops (464, the saturation threshold, is one of them).
+__device__ __forceinline__ bool near_midpoint(float q) {
+    const float a = __builtin_fabsf(q);
+    if (a < 0.015625f) {
+        const float t = a * 512.0f;  // exact
+        return __builtin_fabsf(t - __builtin_floorf(t) - 0.5f) < 1e-5f;
     }
-    return sign | mag;
+    return ((__builtin_bit_cast(uint32_t, a) & 0xFFFFFu) - 0x7FFF8u) <= 16u;  // within 8 of 0x80000
+}
+
+// Four floats -> four OCP E4M3FN codes (bytes 0..3 in order) with gfx950's
+// conversion instruction (round to nearest even), after clamping to +-448 so
+// that larger magnitudes saturate (clamping keeps the sign of zeros).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    auto clamp = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), w, true);
+    return (uint32_t)w;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// Wave w of a workgroup packs row 4*blockIdx.x + w; lane l holds dims
-// 8l .. 8l+7 (lanes 0..55 the non-rotary part, 56..63 the rotary part).
-__global__ __launch_bounds__(256) void pack_fp8_kernel(PackArgs p) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int l = threadIdx.x & 63;
-    if (row >= p.n) return;
-    const int32_t slot = p.slots[row];  // uniform over the wave
-    if (slot < 0) return;
-    const pk_u32x4 v = *(const pk_u32x4*)(p.k + row * p.k_s0 + 8 * l);
+constexpr int kRowsPerWave = 4;
+
+// This lane's share of a row's largest non-rotary magnitude (lane l holds
+// dims 8l .. 8l+7 in v: lanes 0..55 the non-rotary part, 56..63 the rotary).
+__device__ __forceinline__ float lane_amax(const pk_u32x4& v, int l) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(v[j])), __builtin_fabsf(bf16_hi(v[j]))));
+    return l < 56 ? amax : 0.f;
+}
+
+// One row, given its largest non-rotary magnitude.
+__device__ __forceinline__ void pack_row(const PackArgs& p, const pk_u32x4& v, int32_t slot, float amax, int l) {
     float f[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         f[2 * j] = bf16_lo(v[j]);
         f[2 * j + 1] = bf16_hi(v[j]);
     }
-    float amax = 0.f;
-    if (l < 56) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, __builtin_fabsf(f[j]));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     uint8_t* page = p.pool + (int64_t)(slot >> 8) * p.page_bytes;
     uint8_t* rec = page + (slot & 255) * kRecBytes;
     if (l < 56) {
-        uint32_t c[8];
+        // The quotients by a reciprocal multiply; where one of the wave's
+        // could round differently from the correctly rounded quotient (or the
+        // scale is subnormal, where the reciprocal overflows), by division.
+        const float r = __builtin_amdgcn_rcpf(scale);
+        float q[8];
+        bool risky = false;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = e4m3_code(f[j] / scale);
-        *(pk_u32x2*)(rec + 8 * l) = pk_u32x2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                             c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+        for (int j = 0; j < 8; ++j) {
+            q[j] = f[j] * r;
+            risky |= near_midpoint(q[j]);
+        }
+        if (__builtin_expect(__any(risky) || !(scale >= 1.17549435e-38f), 0)) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = f[j] / scale;
+        }
+        *(pk_u32x2*)(rec + 8 * l) = pk_u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
     } else {
         *(pk_u32x4*)(rec + 448 + 16 * (l - 56)) = v;
     }
     if (l == 0) *(float*)(page + kScaleOffset + 4 * (slot & 255)) = scale;
 }
 
+// Wave w of workgroup b packs rows kRowsPerWave * (4b + w) + 0 .. kRowsPerWave-1,
+// loading all of them before packing any (more bytes in flight per wave:
+// with one row per wave the loads in flight, not HBM, set the rate).
+__global__ __launch_bounds__(256) void pack_fp8_kernel(PackArgs p) {
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+    const int l = threadIdx.x & 63;
+    if (row0 >= p.n) return;
+    pk_u32x4 v[kRowsPerWave];
+    int32_t slot[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+        const int64_t row = min(row0 + r, p.n - 1);  // rows past n: a valid address, skipped below
+        v[r] = *(const pk_u32x4*)(p.k + row * p.k_s0 + 8 * l);
+        slot[r] = row0 + r < p.n ? p.slots[row] : -1;
+    }
+    // The rows' maxima over the wave, their shuffles interleaved.
+    float amax[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) amax[r] = lane_amax(v[r], l);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) amax[r] = fmaxf(amax[r], __shfl_xor(amax[r], o));
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r)
+        if (slot[r] >= 0) pack_row(p, v[r], slot[r], amax[r], l);
+}
+
 }  // namespace
 
 hipError_t launch_pack_fp8(const PackArgs& p, hipStream_t stream) {
     if (p.n == 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)((p.n + 3) / 4)), dim3(256), 0, stream, p);
+    const int64_t rows_per_block = 4 * kRowsPerWave;
+    hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)((p.n + rows_per_block - 1) / rows_per_block)), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
