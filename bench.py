@@ -284,7 +284,8 @@ def bench_pack(args) -> int:
         "config": {"workload": f"fp8_kv_pack_n{n}", "rows": n, "pages": pages, "input_sets": n_sets,
                    "cache": "cold-rotated", "timed": "HIP graph replay, events around it on the kernels' stream",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "pack_fp8_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "pack_fp8_kernel<4>" if n >= 16384 else "pack_fp8_kernel<1>",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
         "cpu_baseline": None,

@@ -54,8 +54,6 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-constexpr int kRowsPerWave = 4;
-
 // This lane's share of a row's largest non-rotary magnitude (lane l holds
 // dims 8l .. 8l+7 in v: lanes 0..55 the non-rotary part, 56..63 the rotary).
 __device__ __forceinline__ float lane_amax(const pk_u32x4& v, int l) {
@@ -100,8 +98,10 @@ __device__ __forceinline__ void pack_row(const PackArgs& p, const pk_u32x4& v, i
 }
 
 // Wave w of workgroup b packs rows kRowsPerWave * (4b + w) + 0 .. kRowsPerWave-1,
-// loading all of them before packing any (more bytes in flight per wave:
-// with one row per wave the loads in flight, not HBM, set the rate).
+// loading all of them before packing any.  Several rows per wave put more
+// bytes in flight per wave (large calls); one row per wave gives the most
+// waves and the shortest chain per wave (small calls, e.g. a decode step).
+template <int kRowsPerWave>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(PackArgs p) {
     const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
     const int l = threadIdx.x & 63;
@@ -131,9 +131,14 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(PackArgs p) {
 
 hipError_t launch_pack_fp8(const PackArgs& p, hipStream_t stream) {
     if (p.n == 0) return hipSuccess;
-    const int64_t rows_per_block = 4 * kRowsPerWave;
-    hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)((p.n + rows_per_block - 1) / rows_per_block)), dim3(256), 0,
-                       stream, p);
+    // Four rows per wave once that still gives every SIMD several waves
+    // (measured: 65536 rows 29.4 us with four, 31.5 us with one; 64 rows
+    // 2.6 us with one, 5.0 us with four).
+    if (p.n >= 16384) {
+        hipLaunchKernelGGL(pack_fp8_kernel<4>, dim3((unsigned)((p.n + 15) / 16)), dim3(256), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL(pack_fp8_kernel<1>, dim3((unsigned)((p.n + 3) / 4)), dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

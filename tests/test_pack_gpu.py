@@ -55,9 +55,10 @@ def _compare(orc, k_bits, slots, pages, what):
     assert bad.size == 0, f"{what}: {len(bad)} bytes differ, first at {bad[:4].tolist()}"
 
 
-def test_pack_random_rows_bit_exact(orc):
+@pytest.mark.parametrize("n", [1000, 16384 + 5])  # one row per wave; four per wave with a ragged tail
+def test_pack_random_rows_bit_exact(orc, n):
     rng = np.random.default_rng(1)
-    pages, n = 5, 1000
+    pages = (n + 255) // 256 + 1
     k = _varied_rows(rng, n)
     slots = rng.permutation(pages * 256)[:n].astype(np.int32)
     slots[rng.random(n) < 0.1] = -1                       # skipped rows leave the pool untouched
