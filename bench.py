@@ -308,6 +308,81 @@ def bench_pack(args) -> int:
     return 0
 
 
+def bench_topk(args) -> int:
+    """The C4 top-k kernel (dsv4_c4_topk) on its own: `args.topk` rows of
+    2^18 candidate scores each (the C4 entries of a 1M-token context), K = 512,
+    timed as one HIP graph replay of `steps` calls rotating over enough score
+    copies that they do not stay in the MALL."""
+    import torch
+
+    from hybrid_sparse_mqa_amd import dsv4_c4_topk
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, n, K = int(args.topk), 1 << 18, 512
+    rng = np.random.default_rng(0)
+    scores = rng.standard_normal((T, n), dtype=np.float32)
+    n_sets = int(min(32, max(2, -(-3 * MALL_BYTES // (T * n * 4)))))
+    st = torch.from_numpy(scores).to(dev)
+    sets = [st if i == 0 else st.clone() for i in range(n_sets)]
+    nc = torch.full((T,), n, dtype=torch.int32, device=dev)
+    outs = [torch.empty((T, K), dtype=torch.int32, device=dev) for _ in range(2)]
+    nbytes = T * n * 4 + T * K * 4  # scores read once, indices written
+
+    def step(i):
+        dsv4_c4_topk(sets[i % n_sets], nc, K, indices=outs[i & 1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                step(i)
+        g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "C4 top-512 selections/s (query rows over 2^18 candidates) + achieved HBM GB/s (% peak)",
+        "value": T / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"c4_topk512_b{T}_n262144", "rows": T, "candidates": n, "k": K,
+                   "input_sets": n_sets, "cache": "cold-rotated",
+                   "timed": "HIP graph replay, events around it on the kernels' stream", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "topk_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.topk import topk_select
+
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds / 2:
+            topk_select(scores, np.full(T, n), K)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": reps * T / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"all {T} rows x {reps} repetitions (numpy lexsort), {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +399,8 @@ def main() -> int:
                     help="time the kernels of every N-th call of the timed replay with HIP events")
     ap.add_argument("--pack", type=int, default=0, metavar="ROWS",
                     help="time the FP8 KV store kernel on ROWS rows instead of the attention")
+    ap.add_argument("--topk", type=int, default=0, metavar="ROWS",
+                    help="time the C4 top-512 kernel on ROWS rows of 2^18 candidates instead of the attention")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -344,6 +421,8 @@ def main() -> int:
 
     if args.pack:
         return bench_pack(args)
+    if args.topk:
+        return bench_topk(args)
 
     import torch
 

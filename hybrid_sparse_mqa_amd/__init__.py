@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     dsv4_attn_forward,
     dsv4_attn_gather_slots,
     dsv4_kv_pack_fp8,
+    dsv4_c4_topk,
     dsv4_attn_plan,
     dsv4_attn_set_kernel,
     dsv4_attn_set_split_keys,

@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
         L.dsv4_attn_gather_slots.restype = ctypes.c_int
         L.dsv4_attn_gather_slots.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
                                              ctypes.c_void_p]
+        L.dsv4_c4_topk.restype = ctypes.c_int
+        L.dsv4_c4_topk.argtypes = [P, P, P, ctypes.c_void_p]
         L.dsv4_kv_pack_fp8.restype = ctypes.c_int
         L.dsv4_kv_pack_fp8.argtypes = [P, P, P, ctypes.c_void_p]
         L.dsv4_last_error.restype = ctypes.c_char_p

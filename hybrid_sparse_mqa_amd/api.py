@@ -89,6 +89,19 @@ def dsv4_kv_pack_fp8(k: torch.Tensor, slots: torch.Tensor, pool: torch.Tensor, s
     N.check(L.dsv4_kv_pack_fp8(*[N.ref(d) for d in descs], ctypes.c_void_p(st)))
 
 
+def dsv4_c4_topk(scores: torch.Tensor, num_candidates: torch.Tensor, k: int = 512,
+                 indices: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """Per row, the k highest of scores[t, :num_candidates[t]] (ties: the lower
+    index), ascending, then -1: int32 [T, k], the C4 index lists."""
+    L = N.load()
+    if indices is None:
+        indices = torch.empty((scores.shape[0], k), dtype=torch.int32, device=scores.device)
+    descs = [N.describe(x) for x in (scores, num_candidates, indices)]
+    st = N.stream_handle(scores.device) if stream is None else stream
+    N.check(L.dsv4_c4_topk(*[N.ref(d) for d in descs], ctypes.c_void_p(st)))
+    return indices
+
+
 def dsv4_abi_version() -> int:
     return int(N.load().dsv4_abi_version())
 

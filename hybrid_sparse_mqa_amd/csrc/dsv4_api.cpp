@@ -588,6 +588,40 @@ dsv4_status dsv4_kv_pack_fp8(const dsv4_tensor* k, const dsv4_tensor* slots, con
     return DSV4_OK;
 }
 
+dsv4_status dsv4_c4_topk(const dsv4_tensor* scores, const dsv4_tensor* num_candidates, const dsv4_tensor* indices,
+                         void* stream) {
+    DSV4_TRY(check_tensor("scores", scores, DSV4_F32, 2, {-1, -1}));
+    const int64_t T = scores->shape[0], ld = scores->shape[1];
+    DSV4_TRY(check_tensor("num_candidates", num_candidates, DSV4_I32, 1, {T}));
+    DSV4_TRY(check_tensor("indices", indices, DSV4_I32, 2, {T, -1}));
+    const int64_t K = indices->shape[1];
+    if (K < 1 || K > kTopkMaxK) return fail(DSV4_ERR_UNSUPPORTED, "indices: width %lld, expected 1..%d", (long long)K, kTopkMaxK);
+    if (T > INT32_MAX || ld > INT32_MAX) return fail(DSV4_ERR_UNSUPPORTED, "scores: too large");
+    if (T == 0) return DSV4_OK;
+    if (T > 1 && indices->stride[0] < K) return fail(DSV4_ERR_INVALID, "indices: rows overlap");
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        DSV4_HIP(hipStreamSynchronize(st));
+        std::vector<int32_t> host;
+        DSV4_TRY(fetch(num_candidates, host, 1, T));
+        for (int64_t t = 0; t < T; ++t)
+            if (host[t] < 0 || host[t] > ld)
+                return fail(DSV4_ERR_CONTRACT, "num_candidates[%lld] = %d outside 0..%lld", (long long)t, host[t],
+                            (long long)ld);
+    }
+    TopkArgs a{};
+    a.scores = (const float*)scores->data;
+    a.s_ld = scores->stride[0];
+    a.n_cand = (const int32_t*)num_candidates->data;
+    a.out = (int32_t*)indices->data;
+    a.out_ld = indices->stride[0];
+    a.T = (int32_t)T;
+    a.K = (int32_t)K;
+    a.ld = (int32_t)ld;
+    DSV4_HIP(launch_topk(a, st));
+    return DSV4_OK;
+}
+
 dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
                               const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
                               const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,

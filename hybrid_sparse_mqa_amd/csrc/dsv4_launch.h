@@ -69,9 +69,22 @@ struct PackArgs {
     int64_t page_bytes;
 };
 
+// C4 top-k: per row t, the K highest of scores[t][0 .. n_cand[t]) (ties: the
+// lower index), ascending, then -1, into out[t][0 .. K).
+constexpr int kTopkMaxK = 2048;
+struct TopkArgs {
+    const float* scores;  // [T, s_ld]
+    int64_t s_ld;
+    const int32_t* n_cand;  // [T]
+    int32_t* out;           // [T, out_ld]
+    int64_t out_ld;
+    int32_t T, K, ld;       // ld: candidates per row available (n_cand is clamped to it)
+};
+
 hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& g, hipStream_t stream);
 hipError_t launch_pack_fp8(const PackArgs& p, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 }  // namespace dsv4

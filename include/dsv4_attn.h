@@ -151,6 +151,27 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
 dsv4_status dsv4_kv_pack_fp8(const dsv4_tensor* k, const dsv4_tensor* slots, const dsv4_tensor* pool, void* stream);
 
 /*
+ * dsv4_c4_topk -- the C4 index lists in front of the attention: per query
+ * row, the K candidate compressed entries with the highest indexer scores
+ * (overview page, "what V4 changed": the indexer keeps the top 512
+ * compressed entries per query; its kernel section names a TopK kernel).
+ *
+ *  scores          f32 [T, ld]: scores[t][c] of candidate c (finite); only
+ *                  c < num_candidates[t] is read
+ *  num_candidates  i32 [T]: candidates of row t, 0 <= n <= ld (for C4 at
+ *                  position p, floor((p+1)/4)); a caller contract, checked
+ *                  with DSV4_VALIDATE=1
+ *  indices         i32 [T, K], 1 <= K <= 2048, written: the kept candidates
+ *                  in ascending order, then -1 (all n when n <= K).  Kept: the
+ *                  K highest scores; of equal scores the lower index first;
+ *                  -0.0 equals +0.0.  The result is the c4_indices argument
+ *                  of dsv4_attn_forward.
+ *  stream          hipStream_t
+ */
+dsv4_status dsv4_c4_topk(const dsv4_tensor* scores, const dsv4_tensor* num_candidates, const dsv4_tensor* indices,
+                         void* stream);
+
+/*
  * dsv4_attn_gather_slots -- the paged gather stage on its own: for every row,
  * the physical slots the attention reads, in canonical order (SWA positions
  * ascending, then C4 entries in index-list order with -1 skipped, or C128

@@ -169,6 +169,21 @@ def test_kv_pack_argument_errors():
     assert call(desc(N.DSV4_BF16, [0, 512]), desc(N.DSV4_I32, [0]), pool) == 0
 
 
+def test_c4_topk_argument_errors():
+    L = N.load()
+
+    def call(s_, n_, i_):
+        return L.dsv4_c4_topk(N.ref(s_), N.ref(n_), N.ref(i_), None)
+
+    sc, nc = desc(N.DSV4_F32, [4, 1000]), desc(N.DSV4_I32, [4])
+    assert call(sc, nc, desc(N.DSV4_I32, [4, 0])) == UNSUPPORTED
+    assert call(sc, nc, desc(N.DSV4_I32, [4, 4096])) == UNSUPPORTED
+    assert call(desc(N.DSV4_BF16, [4, 1000]), nc, desc(N.DSV4_I32, [4, 512])) == INVALID
+    assert call(sc, desc(N.DSV4_I32, [3]), desc(N.DSV4_I32, [4, 512])) == INVALID
+    assert call(sc, nc, desc(N.DSV4_I32, [5, 512])) == INVALID
+    assert call(desc(N.DSV4_F32, [0, 1000]), desc(N.DSV4_I32, [0]), desc(N.DSV4_I32, [0, 512])) == 0
+
+
 def test_plan_is_host_only_and_sane():
     L = N.load()
     s = ctypes.c_int32()

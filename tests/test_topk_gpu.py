@@ -1,0 +1,95 @@
+"""GPU parity of the C4 top-k selection (dsv4_c4_topk) against the oracle
+(oracle/topk.py): the index lists must be identical (integer work)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as oracle_mod
+from oracle.topk import topk_select
+from synth import make_case
+from tests import gpu_util as G
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def _gpu(scores, n, k):
+    from hybrid_sparse_mqa_amd import dsv4_c4_topk
+
+    s = torch.from_numpy(np.ascontiguousarray(scores, np.float32)).cuda()
+    c = torch.from_numpy(np.ascontiguousarray(n, np.int32)).cuda()
+    out = dsv4_c4_topk(s, c, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check(scores, n, k, what):
+    got = _gpu(scores, n, k)
+    want = topk_select(scores, n, k)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} entries differ, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("k", [512, 64, 1])
+def test_topk_ties_and_ragged_rows(k):
+    rng = np.random.default_rng(k)
+    T, ld = 12, 3000
+    scores = rng.integers(-20, 21, (T, ld)).astype(np.float32)   # many ties at the threshold
+    scores[1] = rng.standard_normal(ld).astype(np.float32)      # no ties
+    scores[2, ::3] = -0.0                                        # -0 ties with +0
+    scores[2, 1::3] = 0.0
+    scores[3] = 7.0                                              # all tied
+    n = np.array([ld, ld, ld, ld, 0, 1, k - 1 if k > 1 else 0, k, k + 1, 1000, 2999, 17], np.int32)
+    log(f"topk: {T} rows, k={k}")
+    _check(scores, n, k, f"k={k}")
+
+
+def test_topk_million_token_rows():
+    """Eight rows of 2^18 candidates (C4 entries of a 1M-token context)."""
+    rng = np.random.default_rng(5)
+    T, ld = 8, 1 << 18
+    scores = rng.standard_normal((T, ld)).astype(np.float32)
+    scores[1] = np.round(scores[1] * 4) / 4                      # heavy ties
+    scores[2] = 1.0                                              # all tied
+    n = np.full(T, ld, np.int32)
+    n[3] = ld - 12345
+    log("topk: 8 rows x 2^18 candidates")
+    _check(scores, n, 512, "1M context")
+
+
+def test_topk_feeds_the_attention():
+    """Index lists selected on the GPU from random scores over each row's
+    visible compressed entries, used as c4_indices: the attention matches the
+    oracle's on the oracle's selection (the same lists)."""
+    case = make_case(seq_lens=[3000, 4500], n_q=[1, 4], H=16, R=4, K=512, seed=6)
+    rng = np.random.default_rng(6)
+    pos = []
+    for r in range(case.B):
+        lo, hi = int(case.qo_indptr[r]), int(case.qo_indptr[r + 1])
+        pos += [int(case.seq_lens[r]) - (hi - lo) + j for j in range(hi - lo)]
+    n = np.array([(p + 1) // 4 for p in pos], np.int32)
+    ld = int(n.max())
+    scores = rng.standard_normal((case.T, ld)).astype(np.float32)
+    # The generator backs only the compressed entries some row of the request
+    # selected (the rest of the pool is poison): give the others a very low
+    # score, so that every selection stays on backed entries (each row has at
+    # least 512 of them).
+    for r in range(case.B):
+        lo, hi = int(case.qo_indptr[r]), int(case.qo_indptr[r + 1])
+        backed = np.unique(case.c4_indices[lo:hi][case.c4_indices[lo:hi] >= 0])
+        mask = np.ones(ld, bool)
+        mask[backed] = False
+        scores[lo:hi, mask] = -1e30
+    got = _gpu(scores, n, 512)
+    want = topk_select(scores, n, 512)
+    assert np.array_equal(got, want)
+    case = dataclasses.replace(case, c4_indices=got.astype(np.int32))
+    out, lse = G.run_forward(case)
+    ro, rl, _ = oracle_mod.Oracle().attention(dataclasses.replace(case, c4_indices=want.astype(np.int32)))
+    G.compare(out, lse, ro, rl, what="topk -> attention")
