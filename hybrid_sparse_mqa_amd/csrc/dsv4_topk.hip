@@ -28,7 +28,8 @@ __device__ __forceinline__ uint32_t score_key(float x) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-constexpr int kBins = 4096;  // digits of 12, 10 and 10 bits
+constexpr int kBins = 4096;     // digits of 12, 10 and 10 bits
+constexpr int kCompCap = 4096;  // candidates kept in LDS after the first pass
 
 // Adds one to hist[bin] for the active lanes.  The lanes that share the first
 // active lane's bin add with one atomic: keys concentrated in a few bins (a
@@ -127,6 +128,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ uint32_t pick[2];
     __shared__ uint32_t count;
     __shared__ int32_t sel[kTopkMaxK];
+    __shared__ uint32_t ckey[kCompCap];
+    __shared__ int32_t cidx[kCompCap];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int K = a.K;
@@ -143,9 +146,43 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     constexpr int kShift[3] = {20, 10, 0}, kNb[3] = {4096, 1024, 1024};
     uint32_t prefix = 0, pmask = 0, need = (uint32_t)K, n_eq = 0;
     auto key_of = [&](int c) { return score_key(row[c]); };
-    for (int p = 0; p < 3; ++p) {
+    radix_pass<true>(hist, pick, n, kShift[0], kNb[0], need, key_of, [](int, uint32_t) { return true; }, &n_eq);
+    const uint32_t d0 = pick[0];
+    need -= pick[1];
+    // The candidates whose first digit is d0 or above: every one that can be
+    // kept.  Usually few; then they move to LDS (key, index) and the other
+    // passes and the selection run there instead of over all n candidates.
+    const uint32_t n_top = pick[1] + n_eq;
+    const bool compact = n_top <= (uint32_t)kCompCap;
+    prefix = d0 << kShift[0];
+    pmask = (uint32_t)(kNb[0] - 1) << kShift[0];
+    if (compact) {
+        if (tid == 0) count = 0;
+        __syncthreads();
+        for (int c0 = 0; c0 < n; c0 += kThreads * kUnroll) {
+            uint32_t k[kUnroll];
+#pragma unroll
+            for (int j = 0; j < kUnroll; ++j) k[j] = key_of(min(c0 + tid + kThreads * j, n - 1));
+#pragma unroll
+            for (int j = 0; j < kUnroll; ++j) {
+                const int c = c0 + tid + kThreads * j;
+                if (c < n && (k[j] >> kShift[0]) >= d0) {
+                    const uint32_t pos = atomicAdd(&count, 1u);  // exactly n_top of them (bounded for safety)
+                    if (pos < (uint32_t)kCompCap) {
+                        ckey[pos] = k[j];
+                        cidx[pos] = c;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const int m = compact ? (int)n_top : n;  // elements the remaining passes walk
+    auto elem_key = [&](int e) { return compact ? ckey[e] : key_of(e); };
+    auto elem_idx = [&](int e) { return compact ? cidx[e] : e; };
+    for (int p = 1; p < 3; ++p) {
         const uint32_t pm = pmask, pf = prefix;
-        radix_pass<true>(hist, pick, n, kShift[p], kNb[p], need, key_of,
+        radix_pass<true>(hist, pick, m, kShift[p], kNb[p], need, elem_key,
                          [=](int, uint32_t v) { return (v & pm) == pf; }, &n_eq);
         need -= pick[1];
         prefix |= pick[0] << kShift[p];
@@ -158,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         const uint32_t T = prefix;
         for (int p = 0; p < 3; ++p) {
             const uint32_t im = imask, ipf = ip;
-            radix_pass<false>(hist, pick, n, kShift[p], kNb[p], ineed, [](int c) { return (uint32_t)c; },
-                              [=](int c, uint32_t v) { return score_key(row[c]) == T && (v & im) == ipf; }, &n_in);
+            radix_pass<false>(hist, pick, m, kShift[p], kNb[p], ineed, [&](int e) { return (uint32_t)elem_idx(e); },
+                              [&, T, im, ipf](int e, uint32_t v) { return elem_key(e) == T && (v & im) == ipf; }, &n_in);
             ineed -= pick[1];
             ip |= pick[0] << kShift[p];
             imask |= (uint32_t)(kNb[p] - 1) << kShift[p];
@@ -168,16 +205,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
     if (tid == 0) count = 0;
     __syncthreads();
-    for (int c0 = 0; c0 < n; c0 += kThreads * kUnroll) {
+    for (int e0 = 0; e0 < m; e0 += kThreads * kUnroll) {
         uint32_t k[kUnroll];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) k[j] = score_key(row[min(c0 + tid + kThreads * j, n - 1)]);
+        for (int j = 0; j < kUnroll; ++j) k[j] = elem_key(min(e0 + tid + kThreads * j, m - 1));
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
-            const int c = c0 + tid + kThreads * j;
-            if (c < n && (k[j] > prefix || (k[j] == prefix && c < last))) {
-                const uint32_t pos = atomicAdd(&count, 1u);  // exactly K of them (bounded for safety)
-                if (pos < (uint32_t)kTopkMaxK) sel[pos] = c;
+            const int e = e0 + tid + kThreads * j;
+            if (e < m) {
+                const int32_t c = elem_idx(e);
+                if (k[j] > prefix || (k[j] == prefix && c < last)) {
+                    const uint32_t pos = atomicAdd(&count, 1u);  // exactly K of them (bounded for safety)
+                    if (pos < (uint32_t)kTopkMaxK) sel[pos] = c;
+                }
             }
         }
     }
