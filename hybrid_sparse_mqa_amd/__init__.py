@@ -7,6 +7,7 @@ does, and raises if it has not been built.
 """
 from .api import (  # noqa: F401
     dsv4_abi_version,
+    dsv4_attn_debug_keys,
     dsv4_attn_forward,
     dsv4_attn_gather_slots,
     dsv4_kv_pack_fp8,

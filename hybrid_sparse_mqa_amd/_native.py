@@ -67,7 +67,7 @@ def load() -> ctypes.CDLL:
         L.dsv4_last_error.restype = ctypes.c_char_p
         L.dsv4_abi_version.restype = ctypes.c_int32
         L.dsv4_attn_workspace_reserve.restype = ctypes.c_int
-        L.dsv4_attn_workspace_reserve.argtypes = [ctypes.c_size_t]
+        L.dsv4_attn_workspace_reserve.argtypes = [ctypes.c_size_t, ctypes.c_void_p]
         L.dsv4_attn_workspace_release.restype = None
         L.dsv4_attn_set_split_keys.restype = ctypes.c_int
         L.dsv4_attn_set_split_keys.argtypes = [ctypes.c_int32]
@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
         L.dsv4_attn_timing_read.restype = ctypes.c_int
         L.dsv4_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_int64)]
+        L.dsv4_attn_debug_keys.restype = ctypes.c_int
+        L.dsv4_attn_debug_keys.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64]
         _lib = L
         return L
 

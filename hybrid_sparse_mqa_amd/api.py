@@ -136,12 +136,23 @@ def dsv4_attn_plan(num_rows, num_heads, compress_ratio, window, c4_width=0, extr
     return s.value, c.value, k.value
 
 
-def dsv4_attn_workspace_reserve(nbytes: int) -> None:
-    N.check(N.load().dsv4_attn_workspace_reserve(int(nbytes)))
+def dsv4_attn_workspace_reserve(nbytes: int, stream: Optional[int] = None) -> None:
+    st = N.stream_handle() if stream is None else stream
+    N.check(N.load().dsv4_attn_workspace_reserve(int(nbytes), ctypes.c_void_p(st)))
 
 
 def dsv4_attn_workspace_release() -> None:
     N.load().dsv4_attn_workspace_release()
+
+
+def dsv4_attn_debug_keys(keys: Optional[torch.Tensor], masks: Optional[torch.Tensor] = None) -> None:
+    """Test hook: while ``keys`` (int64, device) is given, forward calls run the
+    recording builds of the split kernels (see dsv4_attn.h); None stops it."""
+    if keys is None:
+        N.check(N.load().dsv4_attn_debug_keys(None, 0, None, 0))
+        return
+    N.check(N.load().dsv4_attn_debug_keys(ctypes.c_void_p(keys.data_ptr()), keys.numel(),
+                                          ctypes.c_void_p(masks.data_ptr()), masks.numel()))
 
 
 def dsv4_attn_timing_enable(enable: bool) -> None:

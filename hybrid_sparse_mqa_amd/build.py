@@ -34,17 +34,27 @@ def compile_flags():
     ]
 
 
+def _compile(src: str, verbose: bool) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(CSRC, src + ".o")
+    cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", path, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}")
+    if verbose and r.stdout:
+        print(r.stdout, file=sys.stderr)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
-    objs = []
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(CSRC, src + ".o")
-        cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", path, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), file=sys.stderr)
-        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-        objs.append(obj)
+    """Compile every HIP source (in parallel) and link the shared library;
+    returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)

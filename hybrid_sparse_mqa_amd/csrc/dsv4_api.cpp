@@ -19,6 +19,13 @@
 
 using namespace dsv4;
 
+// 4 KiB of zeros in each device's copy of the code object (zero-initialised
+// at load): unused C4 entries and keys past a split read it, so every copy
+// stays in bounds and masked keys contribute zeros.  No kernel writes it.
+// (Not const: the device compiler drops const device data that no device code
+// references, and the runtime then has no device symbol for the host's.)
+static __device__ __attribute__((aligned(256))) uint8_t g_zero_row[4096];
+
 namespace {
 
 thread_local std::string g_err;
@@ -172,16 +179,25 @@ int64_t extra_bound(int32_t R, int32_t K, int32_t P_extra) {
 }
 
 // ---- device properties and workspace ---------------------------------------
+
 struct DeviceState {
     int cus = 0;
     void* ws = nullptr;  // split partials
     size_t ws_bytes = 0;
-    void* zero_row = nullptr;  // 4 KiB of zeros, read in place of unused keys
+    // Buffers replaced by a larger one.  A HIP graph captured earlier may
+    // still write into them, so they live until dsv4_attn_workspace_release.
+    std::vector<void*> retired;
+    const void* zero_row = nullptr;  // device address of g_zero_row
 };
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
 int32_t g_force_split_keys = 0;
 int32_t g_force_kernel = DSV4_KERNEL_AUTO;  // bf16 pools only
+// Test hook: key recording (dsv4_attn_debug_keys).
+uint64_t* g_dbg_keys = nullptr;
+int64_t g_dbg_keys_cap = 0;
+uint32_t* g_dbg_masks = nullptr;
+int64_t g_dbg_masks_cap = 0;
 
 DeviceState* device_state(int dev) {
     if (dev < 0) return nullptr;
@@ -195,30 +211,37 @@ DeviceState* device_state(int dev) {
     return &d;
 }
 
-dsv4_status ensure_workspace(DeviceState* d, size_t bytes) {
-    if (d->ws_bytes >= bytes) return DSV4_OK;
-    if (d->ws != nullptr) {
-        DSV4_HIP(hipDeviceSynchronize());
-        DSV4_HIP(hipFree(d->ws));
-        d->ws = nullptr;
-        d->ws_bytes = 0;
-    }
-    size_t want = std::max(bytes, (size_t)16 << 20);
-    if (hipMalloc(&d->ws, want) != hipSuccess) {
-        d->ws = nullptr;
-        return fail(DSV4_ERR_WORKSPACE, "hipMalloc of %zu workspace bytes failed", want);
-    }
-    d->ws_bytes = want;
-    return DSV4_OK;
+bool stream_capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return false;
+    return cs != hipStreamCaptureStatusNone;
 }
 
 dsv4_status ensure_zero_row(DeviceState* d) {
     if (d->zero_row != nullptr) return DSV4_OK;
     void* p = nullptr;
-    if (hipMalloc(&p, 4096) != hipSuccess) return fail(DSV4_ERR_WORKSPACE, "hipMalloc of the zero row failed");
-    DSV4_HIP(hipMemset(p, 0, 4096));
-    DSV4_HIP(hipDeviceSynchronize());
-    d->zero_row = p;  // kept for the life of the process
+    DSV4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(g_zero_row)));
+    d->zero_row = p;
+    return DSV4_OK;
+}
+
+// Grows the workspace to at least `bytes` (at least doubling, so that a
+// growing sequence of calls allocates O(log) times).  A call made while its
+// stream is being captured never allocates: hipMalloc is not a stream
+// operation and would break or escape the capture.
+dsv4_status ensure_workspace(DeviceState* d, size_t bytes, hipStream_t st) {
+    if (d->ws_bytes >= bytes) return DSV4_OK;
+    if (stream_capturing(st))
+        return fail(DSV4_ERR_WORKSPACE,
+                    "the call needs %zu workspace bytes but %zu are reserved, and the stream is being captured; "
+                    "call dsv4_attn_workspace_reserve with the largest size before capturing",
+                    bytes, d->ws_bytes);
+    size_t want = std::max({bytes, (size_t)16 << 20, 2 * d->ws_bytes});
+    void* p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) return fail(DSV4_ERR_WORKSPACE, "hipMalloc of %zu workspace bytes failed", want);
+    if (d->ws != nullptr) d->retired.push_back(d->ws);
+    d->ws = p;
+    d->ws_bytes = want;
     return DSV4_OK;
 }
 
@@ -467,26 +490,42 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
     return DSV4_OK;
 }
 
-dsv4_status dsv4_attn_workspace_reserve(size_t bytes) {
+dsv4_status dsv4_attn_workspace_reserve(size_t bytes, void* stream) {
     int dev = 0;
     DSV4_HIP(hipGetDevice(&dev));
     std::lock_guard<std::mutex> lk(g_mu);
-    return ensure_workspace(device_state(dev), bytes);
+    DeviceState* d = device_state(dev);
+    DSV4_TRY(ensure_zero_row(d));
+    return ensure_workspace(d, bytes, (hipStream_t)stream);
 }
 
 void dsv4_attn_workspace_release(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     for (size_t i = 0; i < g_dev.size(); ++i) {
-        if (g_dev[i].ws == nullptr) continue;
+        DeviceState& d = g_dev[i];
+        if (d.ws == nullptr && d.retired.empty()) continue;
         int cur = 0;
         if (hipGetDevice(&cur) == hipSuccess && hipSetDevice((int)i) == hipSuccess) {
             (void)hipDeviceSynchronize();
-            (void)hipFree(g_dev[i].ws);
+            if (d.ws != nullptr) (void)hipFree(d.ws);
+            for (void* p : d.retired) (void)hipFree(p);
             (void)hipSetDevice(cur);
         }
-        g_dev[i].ws = nullptr;
-        g_dev[i].ws_bytes = 0;
+        d.ws = nullptr;
+        d.ws_bytes = 0;
+        d.retired.clear();
     }
+}
+
+dsv4_status dsv4_attn_debug_keys(void* keys, int64_t keys_cap, void* masks, int64_t masks_cap) {
+    if (keys != nullptr && (keys_cap < 0 || masks == nullptr || masks_cap < 0))
+        return fail(DSV4_ERR_INVALID, "debug keys: need both buffers and non-negative capacities");
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_dbg_keys = (uint64_t*)keys;
+    g_dbg_keys_cap = keys ? keys_cap : 0;
+    g_dbg_masks = keys ? (uint32_t*)masks : nullptr;
+    g_dbg_masks_cap = keys ? masks_cap : 0;
+    return DSV4_OK;
 }
 
 dsv4_status dsv4_attn_timing_enable(int32_t enable) {
@@ -696,9 +735,19 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     if (a.splits > 1) {
         const size_t n_part = (size_t)T * a.splits * H;
         const size_t bytes_o = n_part * DSV4_HEAD_DIM * sizeof(uint16_t);
-        DSV4_TRY(ensure_workspace(d, bytes_o + n_part * sizeof(float)));
+        DSV4_TRY(ensure_workspace(d, bytes_o + n_part * sizeof(float), st));
         a.ws_o = (uint16_t*)d->ws;
         a.ws_lse = (float*)((char*)d->ws + bytes_o);
+    }
+
+    if (g_dbg_keys != nullptr) {
+        const int64_t units = (int64_t)a.T * a.head_blocks * a.splits;
+        if (units * a.chunk > g_dbg_keys_cap || units * 32 > g_dbg_masks_cap)
+            return fail(DSV4_ERR_INVALID, "debug keys: buffers hold %lld / %lld entries, the call needs %lld / %lld",
+                        (long long)g_dbg_keys_cap, (long long)g_dbg_masks_cap, (long long)(units * a.chunk),
+                        (long long)(units * 32));
+        a.dbg_keys = g_dbg_keys;
+        a.dbg_masks = g_dbg_masks;
     }
 
     TimingRec rec{};

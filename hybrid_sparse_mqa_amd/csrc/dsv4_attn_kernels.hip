@@ -164,6 +164,11 @@ __device__ __forceinline__ bool decode_item(const AttnArgs& a, Item& it) {
     return live;
 }
 
+// Recording builds (the test hook): work-item index of the key records.
+__device__ __forceinline__ int64_t dbg_unit(const AttnArgs& a, const Item& it) {
+    return ((int64_t)it.t * a.head_blocks + it.hb) * a.splits + it.s;
+}
+
 // The kernel arguments that the first round of loads depends on, made
 // available at one point so that they arrive in one round of scalar loads
 // (left to itself the compiler fetches them in several dependent rounds, each
@@ -686,7 +691,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs g) {
 // list, per-tile key masks and page-table cache live in the exchange
 // buffers until the loop starts.
 // ---------------------------------------------------------------------------
-template <int kHH>
+template <int kHH, bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     constexpr int kGroup = 4 / kHH;          // waves per head group (dim slices)
     constexpr int kDims = kHeadDim / kGroup;  // head dims per wave
@@ -784,9 +789,20 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
+    // Recording builds: lanes 0, 2, .., 14 (one per copied row, dma_row 0..7,
+    // chunk offset 16*(w & 1)) record the row address of key 8*grp + dma_row
+    // of the tile.
+    auto dbg_row = [&](const uint8_t* row, int tile, int grp) {
+        if constexpr (kDbg) {
+            if ((l & 0x31) == 0)
+                a.dbg_keys[dbg_unit(a, it) * a.chunk + kTileKeys * tile + 8 * grp + dma_row] =
+                    (uint64_t)(uintptr_t)(row - dma_lane_off);
+        }
+    };
     auto fetch_tile = [&](int tile) {
         const uint8_t* row = tile < 3 ? (const uint8_t*)(uintptr_t)(tile == 0 ? pro[0] : (tile == 1 ? pro[1] : pro[2])) + dma_lane_off
                                       : tile_row(tile);
+        dbg_row(row, tile, w);
         copy_part(row, tile, P0{});
         copy_part(row, tile, P1{});
         copy_part(row, tile, P2{});
@@ -874,6 +890,9 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
     for (int j = n_early; j < n_first; ++j) fetch_tile(j);
     __syncthreads();  // tile masks published
     const uint32_t tile_mask = s_mask[l & 31];  // lane j: valid keys of tile j
+    if constexpr (kDbg) {
+        if (w == 0 && l < n_tiles) a.dbg_masks[dbg_unit(a, it) * 32 + l] = tile_mask;
+    }
     f32x16 sacc = f32x16{};
     if (n_tiles > 0) {
         if (n_tiles > 2) wait_vmcnt<16>();
@@ -921,7 +940,10 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
         }
         bf16x8 av[kSteps];
         read_k(i + 1, av);
-        if constexpr (kFetch) copy_part(row, i + 3, P0{});
+        if constexpr (kFetch) {
+            dbg_row(row, i + 3, w);
+            copy_part(row, i + 3, P0{});
+        }
 
         // PV of tile i-1 (operands from the previous iteration), interleaved
         // with the first half of tile i's softmax.  Register r of a score tile
@@ -1052,7 +1074,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
 // P, the factors); the prologue's page-table cache, tile masks and the score
 // waves' row addresses live in the exchange buffers until the loop starts.
 // ---------------------------------------------------------------------------
-template <int kHH>
+template <int kHH, bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
     constexpr int kDims = kHeadDim / 2;  // head dims per wave (a dim half)
     constexpr int kSteps = kDims / 16;   // score k-steps per tile
@@ -1165,9 +1187,20 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
+    // Recording builds: lanes 0, 2, .., 14 (one per copied row, dma_row 0..7,
+    // chunk offset 16*(w & 1)) record the row address of key 8*grp + dma_row
+    // of the tile.
+    auto dbg_row = [&](const uint8_t* row, int tile, int grp) {
+        if constexpr (kDbg) {
+            if ((l & 0x31) == 0)
+                a.dbg_keys[dbg_unit(a, it) * a.chunk + kTileKeys * tile + 8 * grp + dma_row] =
+                    (uint64_t)(uintptr_t)(row - dma_lane_off);
+        }
+    };
     auto fetch_tile = [&](int tile) {
         const uint8_t* row = tile < 3 ? (const uint8_t*)(uintptr_t)(tile == 0 ? pro[0] : (tile == 1 ? pro[1] : pro[2])) + dma_lane_off
                                       : tile_row(tile);
+        dbg_row(row, tile, w);
         copy_part(row, tile, P0{});
         copy_part(row, tile, P1{});
         copy_part(row, tile, P2{});
@@ -1262,6 +1295,9 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
     }
     __syncthreads();  // tile masks and the score waves' row addresses published
     const uint32_t tile_mask = s_mask[l & 31];  // lane j: valid keys of tile j
+    if constexpr (kDbg) {
+        if (w == 0 && l < n_tiles) a.dbg_masks[dbg_unit(a, it) * 32 + l] = tile_mask;
+    }
     if (n_tiles > 0) {
         if (n_tiles > 2) wait_vmcnt<16>();
         else if (n_tiles > 1) wait_vmcnt<8>();
@@ -1497,6 +1533,8 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
             if constexpr (kFetch) {
                 next_row = tile_row(i + 4);
                 next_row_s = tile_row_s(i + 4);
+                dbg_row(row, i + 3, w);
+                dbg_row(row_s, i + 3, d);
                 copy_part(row, i + 3, P0{});
                 copy_part_s(row_s, i + 3, P0{});
                 copy_part(row, i + 3, P1{});
@@ -1604,6 +1642,7 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
 // kk, and the transposing PV read of dim block db sits at a per-lane base +
 // 512*db; both are conflict-free over every 16 lanes.
 // ---------------------------------------------------------------------------
+template <bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
     constexpr int kTile = kNarrowTileKeys * 1024;  // 16 KiB
     constexpr int kH = kNarrowHeadsPerBlock;
@@ -1657,6 +1696,9 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
         const bool swa = k0 + key < rk.n_swa;
         const uint8_t* row = slot >= 0 ? (swa ? a.swa_pool : a.ext_pool) + (int64_t)slot * (swa ? a.swa_row_bytes : a.ext_row_bytes)
                                        : a.zero_row;
+        if constexpr (kDbg) {
+            if (l < 16) a.dbg_keys[dbg_unit(a, it) * a.chunk + key] = (uint64_t)(uintptr_t)row;  // dma_row == l
+        }
         const uint8_t* src = row + 16 * (l >> 4);
         const uint32_t dst = ring_w + (n & 1) * kTile;
         dma16_off<0>(src, dst);
@@ -1856,6 +1898,7 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
 // bf16; the per-token scale multiplies the fp32 non-rotary score partial and
 // is folded into P for the non-rotary PV tiles.
 // ---------------------------------------------------------------------------
+template <bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_krow[kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[4 * 512 * 16];
@@ -1898,6 +1941,9 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             const int rec = slot & 255;
             const uint8_t* row = slot >= 0 ? page + rec * kFp8RecBytes : a.zero_row;
             const uint8_t* scp = slot >= 0 ? page + kFp8ScaleOffset + 4 * rec : a.zero_row;
+            if constexpr (kDbg) {
+                if (l == 0) a.dbg_keys[dbg_unit(a, it) * a.chunk + i] = (uint64_t)(uintptr_t)row;
+            }
             pre.v[e] = *(const u32x4*)(row + (l < 56 ? 8 * l : kNope + 16 * (l - 56)));
             pre.sc[e] = *(const float*)scp;
         }
@@ -2125,26 +2171,34 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+template <bool kDbg>
+void launch_split(const AttnArgs& a, Layout layout, dim3 grid, hipStream_t stream) {
+    switch (layout) {
+        case Layout::kFp8:
+            hipLaunchKernelGGL(attn_fp8_kernel<kDbg>, grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kWide:
+            hipLaunchKernelGGL((attn_wide_kernel<2, kDbg>), grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kWide32:
+            hipLaunchKernelGGL((attn_wide_kernel<1, kDbg>), grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kRoles32:
+            hipLaunchKernelGGL((attn_ws_kernel<1, kDbg>), grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kNarrow:
+            hipLaunchKernelGGL(attn_narrow_kernel<kDbg>, grid, dim3(256), 0, stream, a);
+            break;
+    }
+}
+
 hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream) {
     const int per_xcd = (a.n_items + 7) / 8;
     const dim3 grid((unsigned)(8 * per_xcd));
-    switch (layout) {
-        case Layout::kFp8:
-            hipLaunchKernelGGL(attn_fp8_kernel, grid, dim3(256), 0, stream, a);
-            break;
-        case Layout::kWide:
-            hipLaunchKernelGGL(attn_wide_kernel<2>, grid, dim3(256), 0, stream, a);
-            break;
-        case Layout::kWide32:
-            hipLaunchKernelGGL(attn_wide_kernel<1>, grid, dim3(256), 0, stream, a);
-            break;
-        case Layout::kRoles32:
-            hipLaunchKernelGGL(attn_ws_kernel<1>, grid, dim3(256), 0, stream, a);
-            break;
-        case Layout::kNarrow:
-            hipLaunchKernelGGL(attn_narrow_kernel, grid, dim3(256), 0, stream, a);
-            break;
-    }
+    if (a.dbg_keys != nullptr)
+        launch_split<true>(a, layout, grid, stream);
+    else
+        launch_split<false>(a, layout, grid, stream);
     return hipGetLastError();
 }
 

@@ -48,6 +48,13 @@ struct AttnArgs {
     uint16_t* ws_o;           // bf16 [T, splits, H, 512] normalised partial outputs
     float* ws_lse;            // [T, splits, H] base-2 partial log-sum-exp
     const uint8_t* zero_row;  // >= 1 KiB of zeros, read in place of unused keys
+    // Test hook (null in normal calls; then the plain kernel builds run): the
+    // recording builds write, for work item (t, hb, s) and split key k, the
+    // address of the KV row they copied into dbg_keys[((t * head_blocks + hb)
+    // * splits + s) * chunk + k], and the masking kernels the valid-key mask
+    // of each 32-key tile into dbg_masks[(...) * 32 + tile].
+    uint64_t* dbg_keys;
+    uint32_t* dbg_masks;
 };
 
 struct GatherArgs {

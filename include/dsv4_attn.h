@@ -43,8 +43,10 @@
  *    contents (index ranges, page ids, qo_indptr[B] == T, n_q <= seq_len) are
  *    a caller contract; with DSV4_VALIDATE=1 in the environment the library
  *    copies them to the host (synchronously) and checks them first.
- *  - Calls on one device that share the library workspace must not overlap
- *    (serialise them on one stream or across streams).
+ *  - Split partial results go to one library workspace per device.  Calls on
+ *    one device whose kernels could run at the same time (different streams
+ *    without an ordering between them) race on it and give wrong results:
+ *    serialise them (one stream, or events between streams).
  */
 #ifndef DSV4_ATTN_H_
 #define DSV4_ATTN_H_
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define DSV4_ABI_VERSION 1
+#define DSV4_ABI_VERSION 2
 
 /* Element types of a descriptor. */
 enum {
@@ -197,14 +199,25 @@ const char* dsv4_last_error(void);
 int32_t dsv4_abi_version(void);
 
 /*
- * Library workspace for split-KV partial results, one per device, grown on
- * demand by dsv4_attn_forward (hipMalloc, which
- * synchronises the device; call once with the largest sizes before capturing
- * a HIP graph).
- * dsv4_attn_workspace_reserve pre-allocates at least `bytes` on the current
- * device; dsv4_attn_workspace_release frees it after synchronising.
+ * Library workspace for split-KV partial results, one per device (split
+ * kernel -> merge kernel).  dsv4_attn_forward grows it on demand with
+ * hipMalloc (which synchronises the device), except while `stream` is being
+ * captured into a HIP graph: then it never allocates and returns
+ * DSV4_ERR_WORKSPACE if the workspace is too small.  A buffer replaced by a
+ * larger one is kept until dsv4_attn_workspace_release, so graphs captured
+ * earlier stay valid.
+ *
+ * dsv4_attn_workspace_reserve makes the current device's workspace at least
+ * `bytes` large (call it, outside any capture, with the largest size the
+ * captured calls need: T x splits x H x 1028 bytes, splits from
+ * dsv4_attn_plan) and sets up the rest of the library's per-device state, so
+ * that a graph may capture the process's first forward call.  `stream` is the
+ * stream the caller is about to capture (used to refuse growth under
+ * capture).  dsv4_attn_workspace_release synchronises every device that holds
+ * a workspace and frees it; graphs that captured forward calls must not be
+ * replayed afterwards.
  */
-dsv4_status dsv4_attn_workspace_reserve(size_t bytes);
+dsv4_status dsv4_attn_workspace_reserve(size_t bytes, void* stream);
 void dsv4_attn_workspace_release(void);
 
 /*
@@ -262,17 +275,42 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
  * Kernel timing on the caller's stream with HIP events.  While enabled, every
  * dsv4_attn_forward records an event before the split kernel, one between it
  * and the merge kernel, and one after the merge kernel (only when a row is
- * split: otherwise there is no merge kernel and its time counts as 0).  The events are timing-only (created without the
- * system-scope fence on record), so they neither flush caches nor stall the
- * work that follows.  Calls made while the stream is being captured into a
- * HIP graph record external event nodes instead, re-recorded on every replay.
- * dsv4_attn_timing_read waits for the recorded events and returns the summed
- * milliseconds of the split kernels and of the merge kernels (either pointer
- * may be NULL) and the number of calls recorded, then clears the record; for
- * graph-captured calls it reports the most recent replay.
+ * split: otherwise there is no merge kernel and its time counts as 0).  The
+ * events are timing-only (created without the system-scope fence on record),
+ * so they neither flush caches nor stall the work that follows.  Calls made
+ * while the stream is being captured into a HIP graph record external event
+ * nodes instead, re-recorded on every replay.  dsv4_attn_timing_read waits
+ * for the recorded events and returns the summed milliseconds of the split
+ * kernels and of the merge kernels (either pointer may be NULL) and the
+ * number of calls recorded, then clears the record; for graph-captured calls
+ * it reports the most recent replay.  An interval holds its kernel plus the
+ * events' own cost (a few percent of a 20 us kernel).
  */
 dsv4_status dsv4_attn_timing_enable(int32_t enable);
 dsv4_status dsv4_attn_timing_read(double* split_ms, double* merge_ms, int64_t* calls);
+
+/*
+ * Test hook, not for production calls: record the KV rows the split kernels
+ * read.  While `keys` is non-NULL, dsv4_attn_forward launches the recording
+ * build of its split kernel (the same source, plus stores of what it
+ * resolved), which writes for each work item -- row t, head block b of
+ * dsv4_attn_plan's kernel, split s -- and each key k of the split
+ * (0 <= k < keys_per_split, in the kernel's own key order):
+ *   keys[((t * head_blocks + b) * splits + s) * keys_per_split + k]
+ *       (uint64) = device address of the KV row it copied for that key
+ *       (for packed FP8, the row's 576-byte record); the library's zero row
+ *       for an unused C4 entry or a key past the split's end;
+ *   masks[((t * head_blocks + b) * splits + s) * 32 + tile]
+ *       (uint32, DSV4_KERNEL_H32 / _H32_ROLES / _H64 only) = the valid-key
+ *       mask of each 32-key tile (bit k: key 32 * tile + k enters the softmax).
+ * Entries a kernel does not reach keep their previous contents.  The
+ * 32- and 64-head kernels walk a split's compressed entries first, then its
+ * window keys; the 16-head and FP8 kernels the window first.  keys_cap and
+ * masks_cap are the buffers' entry counts; a forward call that would write
+ * past them returns DSV4_ERR_INVALID.  NULL keys switches recording off.
+ * Process-wide; device pointers.
+ */
+dsv4_status dsv4_attn_debug_keys(void* keys, int64_t keys_cap, void* masks, int64_t masks_cap);
 
 #ifdef __cplusplus
 }

@@ -18,4 +18,6 @@ from .workloads import (  # noqa: F401
     PAGE_SIZE,
     make_case,
     make_config,
+    quantize_fp8_rows,
+    store_float_rows,
 )

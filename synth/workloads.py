@@ -93,16 +93,36 @@ def _to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def quantize_fp8_rows(nope: np.ndarray, rope_bits: np.ndarray):
+    """Packed-FP8 storage of float32 non-rotary dims [n, 448] and bf16 rotary
+    bits [n, 64]: per-token scale amax/448 (1 for an all-zero row) and the
+    E4M3FN codes of nope/scale through torch's conversion."""
+    nope = np.ascontiguousarray(nope, dtype=np.float32)
+    n = nope.shape[0]
+    amax = np.abs(nope).max(axis=1) if n else np.zeros(0, np.float32)
+    scales = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = _to_e4m3_codes(nope / scales[:, None])
+    return (codes, scales, np.ascontiguousarray(rope_bits, dtype=np.uint16))
+
+
 def _draw_rows(rng: np.random.Generator, n: int, kv: str):
     """Draw ``n`` KV rows ~ N(0,1) in the pool's storage format."""
     if kv == "bf16":
         return _to_bf16_bits(rng.standard_normal((n, D_HEAD), dtype=np.float32))
     nope = rng.standard_normal((n, D_NOPE), dtype=np.float32)
     rope = _to_bf16_bits(rng.standard_normal((n, D_ROPE), dtype=np.float32))
-    amax = np.abs(nope).max(axis=1) if n else np.zeros(0, np.float32)
-    scales = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    codes = _to_e4m3_codes(nope / scales[:, None])
-    return (codes, scales, rope)
+    return quantize_fp8_rows(nope, rope)
+
+
+def store_float_rows(pool: np.ndarray, kv: str, slots, rows_f32: np.ndarray) -> None:
+    """Write float32 rows [n, 512] at physical slots, cast to the pool's
+    storage format (bf16, or packed FP8 via quantize_fp8_rows)."""
+    slots = np.asarray(slots, dtype=np.int64).reshape(-1)
+    rows_f32 = np.asarray(rows_f32, dtype=np.float32).reshape(len(slots), D_HEAD)
+    if kv == "bf16":
+        _store_rows(pool, kv, slots, _to_bf16_bits(rows_f32))
+    else:
+        _store_rows(pool, kv, slots, quantize_fp8_rows(rows_f32[:, :D_NOPE], _to_bf16_bits(rows_f32[:, D_NOPE:])))
 
 
 def _rows_take(rows, sel):
@@ -158,6 +178,7 @@ def make_case(
     decoy_frac: float = 0.125,
     keep_logical: bool = False,
     scale: Optional[float] = None,
+    index_sets: int = 1,
     name: str = "case",
 ) -> Case:
     """Build one seeded batch.
@@ -169,6 +190,11 @@ def make_case(
     padding to width ``K`` (``pad_mode`` "tail" or "scatter").
     Draw order: q, sink, per-request token rows, compressed rows, indices,
     page permutations.
+
+    ``index_sets > 1`` (R == 4, benchmark rotation): ``index_sets - 1`` more
+    index lists per row, each drawn like the first from a second generator,
+    are stored in ``meta["c4_sets"]`` ([index_sets, T, K], set 0 being
+    ``c4_indices``), and every entry any of them names is backed.
     """
     if R not in (0, 4, 128):
         raise ValueError(f"compress ratio {R}")
@@ -226,8 +252,18 @@ def make_case(
                 c4[t, where] = sel
             else:
                 c4[t, :m] = sel
+        c4_sets = [c4]
+        if index_sets > 1:
+            rng_sets = np.random.Generator(np.random.PCG64(seed + 104729))
+            for _ in range(index_sets - 1):
+                extra = np.full((T, K), -1, dtype=np.int64)
+                for t in range(T):
+                    vis = int((row_pos[t] + 1) // 4)
+                    m = min(want, vis, K)
+                    extra[t, :m] = rng_sets.choice(vis, size=m, replace=False) if m else np.zeros(0, np.int64)
+                c4_sets.append(extra)
         for r in range(B):
-            rows_r = c4[qo_indptr[r]:qo_indptr[r + 1]]
+            rows_r = np.concatenate([cs[qo_indptr[r]:qo_indptr[r + 1]].reshape(-1) for cs in c4_sets])
             ids = np.unique(rows_r[rows_r >= 0])
             cmp_ids.append(ids)
             cmp_rows.append(_draw_rows(rng, len(ids), kv))
@@ -307,7 +343,8 @@ def make_case(
         poison_swa_page=poison_swa,
         poison_extra_page=poison_extra,
         logical=logical,
-        meta={"row_req": row_req, "row_pos": row_pos, "seed": seed},
+        meta={"row_req": row_req, "row_pos": row_pos, "seed": seed,
+              **({"c4_sets": np.stack(c4_sets).astype(np.int32)} if R == 4 and index_sets > 1 else {})},
     )
 
 
@@ -338,8 +375,10 @@ CONFIGS = {
 }
 
 
-def make_config(n: int, seed: Optional[int] = None, keep_logical: bool = False, batch: Optional[int] = None) -> Case:
-    """Inputs for workload ``n`` (1..5); default seed ``1000 + n``."""
+def make_config(n: int, seed: Optional[int] = None, keep_logical: bool = False, batch: Optional[int] = None,
+                index_sets: int = 1) -> Case:
+    """Inputs for workload ``n`` (1..5); default seed ``1000 + n``.
+    ``index_sets`` (C4 workloads): see make_case."""
     if seed is None:
         seed = 1000 + n
     name = CONFIGS[n]["name"]
@@ -348,16 +387,18 @@ def make_config(n: int, seed: Optional[int] = None, keep_logical: bool = False, 
     if n == 2:
         B = batch or 32
         sl = np.random.Generator(np.random.PCG64(seed + 7919)).integers(4096, 8192, size=B, endpoint=True)
-        return make_case(seq_lens=sl, n_q=1, H=64, R=4, seed=seed, keep_logical=keep_logical, name=name)
+        return make_case(seq_lens=sl, n_q=1, H=64, R=4, seed=seed, keep_logical=keep_logical,
+                         index_sets=index_sets, name=name)
     if n == 3:
         B = batch or 64
         return make_case(seq_lens=[131072] * B, n_q=1, H=64, R=128, seed=seed, keep_logical=keep_logical, name=name)
     if n == 4:
         B = batch or 32
         pre = np.random.Generator(np.random.PCG64(seed + 7919)).integers(32768, 65536, size=B, endpoint=True)
-        return make_case(seq_lens=pre + 4, n_q=4, H=64, R=4, seed=seed, keep_logical=keep_logical, name=name)
+        return make_case(seq_lens=pre + 4, n_q=4, H=64, R=4, seed=seed, keep_logical=keep_logical,
+                         index_sets=index_sets, name=name)
     if n == 5:
         B = batch or 8
         return make_case(seq_lens=[1048576] * B, n_q=1, H=64, R=4, kv="fp8", seed=seed,
-                         keep_logical=keep_logical, name=name)
+                         keep_logical=keep_logical, index_sets=index_sets, name=name)
     raise KeyError(n)

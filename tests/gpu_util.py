@@ -92,3 +92,30 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows=None, what=""):
     rel = num / den
     assert rel.max() <= REL_L2, f"{what}: relative L2 error {rel.max():.3g}"
     return float(err.max()), float(le.max()), float(rel.max())
+
+
+def expected_keys(orc, case, t, compressed_first):
+    """Row t's key list in a split kernel's order, from the oracle's canonical
+    gather: entries ("swa" | "ext", physical slot), or None for an unused C4
+    entry (the kernels keep its place, read the zero row and mask it out).
+    compressed_first: the 32- and 64-head kernels' order (compressed entries,
+    then the window); otherwise the window first."""
+    swa, ext = orc.gather(case, t)
+    swa_l = [("swa", int(s)) for s in swa]
+    if case.R == 4:
+        it = iter(ext)
+        ext_l = [None if int(c) < 0 else ("ext", int(next(it))) for c in case.c4_indices[t]]
+        assert next(it, None) is None
+    else:
+        ext_l = [("ext", int(s)) for s in ext]
+    return ext_l + swa_l if compressed_first else swa_l + ext_l
+
+
+def spike_slot(case, pool_name, slot, t, head=0, mult=8.0):
+    """Overwrite physical slot `slot` of a pool with mult * q[t, head] (in the
+    pool's storage format): that key dominates head `head` of row t if and
+    only if the row reads it."""
+    from synth import store_float_rows
+
+    qv = torch.from_numpy(case.q[t, head].view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    store_float_rows(getattr(case, pool_name), case.kv, [slot], (mult * qv)[None, :])

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert N.load().dsv4_abi_version() == 1
+    assert N.load().dsv4_abi_version() == 2
 
 
 def desc(dtype, shape, stride=None, data=FAKE):

@@ -2,12 +2,14 @@
 
 * gather stage: slot lists and counts bit-exact, every row, all workloads;
 * attention: every row of small cases (page edges, window edges, verify,
-  multi-request, ragged, H from 1 to 128, W 1/3/128, bf16 and FP8) and sampled
-  rows of the five full-size workloads in the benchmark's launch plan;
+  multi-request, ragged, H from 1 to 128, W 1/3/128, bf16 and FP8) and every
+  row of the five full-size workloads in the benchmark's launch plan;
 * invariants on the GPU: physical page permutation is bit-identical, forced
   split sizes agree, repeated calls are bit-identical;
-* sink variants, spike tests at every visibility edge, the full E4M3 code
-  table, empty passes, strided tensors, validate mode.
+* sink variants; spike tests at every visibility edge and at split
+  boundaries, on every kernel variant including FP8; the full E4M3 code
+  table; empty passes, strided tensors, validate mode, graph capture.
+(The bit-exact key sets of the split kernels themselves: test_keys_gpu.py.)
 """
 import dataclasses
 import os
@@ -187,14 +189,14 @@ def test_forward_random(orc, seed):
 # full-size workloads, benchmark launch plan, sampled rows
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-def test_forward_workloads_sampled(orc, n):
+def test_forward_workloads_all_rows(orc, n):
+    """The five full-size workloads in the benchmark's launch plan, every row
+    against the oracle."""
     case = make_config(n)
-    rng = np.random.default_rng(n)
-    rows = sorted(set([0, case.T - 1] + list(rng.choice(case.T, size=min(case.T, 6), replace=False))))
-    log(f"forward workload {n} ({case.name}) rows={rows}")
+    log(f"forward workload {n} ({case.name}) all {case.T} rows")
     out, lse = G.run_forward(case)
-    ro, rl, _ = orc.attention(case, rows=rows)
-    e = G.compare(out, lse, ro, rl, rows=rows, what=case.name)
+    ro, rl, _ = orc.attention(case)
+    e = G.compare(out, lse, ro, rl, what=case.name)
     log(f"  max abs err {e[0]:.3g}  lse err {e[1]:.3g}  rel L2 {e[2]:.3g}")
 
 
@@ -274,14 +276,6 @@ def test_sink_variants(orc, variant):
 # spike tests: a key pointing along q[t, 0] must dominate head 0 exactly when
 # it is visible to the row
 # --------------------------------------------------------------------------
-def _spike(case, t, pool_name, table, r, x):
-    """Overwrite logical position x of request r with 8 * q[t, 0]."""
-    slot = int(table[r, x // 256]) * 256 + x % 256
-    row = case.q[t, 0].copy()
-    big = (torch.from_numpy(row.view(np.int16)).view(torch.bfloat16).float() * 8).to(torch.bfloat16)
-    getattr(case, pool_name)[slot] = big.view(torch.int16).numpy().view(np.uint16)
-
-
 SPIKES = [
     # (name, R, seq_lens, n_q, where, visible)
     ("window first", 0, [1000], 1, "tok:p-W+1", True),
@@ -290,38 +284,128 @@ SPIKES = [
     ("c128 last visible", 128, [1026], 4, "cmp:vis-1", True),
     ("c128 first hidden", 128, [1026], 4, "cmp:vis", False),
     ("c4 listed", 4, [3000], 2, "c4:listed", True),
+    ("c4 last used entry", 4, [3000], 2, "c4:last", True),
     ("c4 unlisted", 4, [3000], 2, "c4:unlisted", False),
 ]
+# (kernel forced, kv): every bf16 variant, the automatic choice, and FP8.
+VARIANTS = [(0, "bf16"), (1, "bf16"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (0, "fp8")]
+VARIANT_IDS = ["auto", "h16", "h32", "roles", "h64", "fp8"]
 
 
-@pytest.mark.parametrize("kernel", [0, 1, 3], indirect=True)
+@pytest.fixture
+def variant(request):
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_kernel
+
+    k, kv = request.param
+    dsv4_attn_set_kernel(k)
+    yield k, kv
+    dsv4_attn_set_kernel(0)
+
+
+def _slot(table, r, x):
+    return int(table[r, x // 256]) * 256 + x % 256
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS, indirect=True)
 @pytest.mark.parametrize("name,R,sl,nq,where,visible", SPIKES, ids=[s[0] for s in SPIKES])
-def test_spikes(orc, name, R, sl, nq, where, visible, kernel):
-    case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=77, n_sel=300)
+def test_spikes(orc, name, R, sl, nq, where, visible, variant):
+    _, kv = variant
+    case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=77, n_sel=300, kv=kv)
     t = 0  # first row of the request
     p = int(case.seq_lens[0]) - nq + 0
     kind, pos = where.split(":")
     if kind == "tok":
         x = {"p-W+1": p - case.W + 1, "p-W": p - case.W, "p+1": p + 1}[pos]
-        _spike(case, t, "swa_pool", case.swa_page_table, 0, x)
+        G.spike_slot(case, "swa_pool", _slot(case.swa_page_table, 0, x), t)
     elif kind == "cmp":
         vis = (p + 1) // 128
         x = vis - 1 if pos == "vis-1" else vis
         assert x < int(case.seq_lens[0]) // 128
-        _spike(case, t, "extra_pool", case.extra_page_table, 0, x)
+        G.spike_slot(case, "extra_pool", _slot(case.extra_page_table, 0, x), t)
     else:
         listed = case.c4_indices[t][case.c4_indices[t] >= 0]
         if pos == "listed":
             x = int(listed[17])
+        elif pos == "last":
+            x = int(listed[-1])  # index n_sel - 1 of the list, followed by -1 padding
+            assert case.c4_indices[t][len(listed)] == -1
         else:
             vis = (p + 1) // 4
             x = int(np.setdiff1d(np.arange(vis), listed)[3])
-        _spike(case, t, "extra_pool", case.extra_page_table, 0, x)
+        G.spike_slot(case, "extra_pool", _slot(case.extra_page_table, 0, x), t)
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
     G.compare(out, lse, ro, rl, what=name)
     dominated = rl[t, 0] > 50.0
     assert dominated == visible, (name, rl[t, 0])
+
+
+@pytest.mark.parametrize("variant", VARIANTS[1:], ids=VARIANT_IDS[1:], indirect=True)
+@pytest.mark.parametrize("R", [4, 128])
+@pytest.mark.parametrize("keys", [32, 64, 96])
+def test_spikes_at_split_boundaries(orc, keys, R, variant):
+    """Under forced split sizes, a spike on the first and on the last key of
+    a split (in the kernel's own key order), and on the row's last key, must
+    each dominate: no split boundary drops or duplicates a key."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
+
+    kernel, kv = variant
+    compressed_first = kernel in (2, 3, 4)
+    base = dict(seq_lens=[2600], n_q=2, H=64, R=R, seed=88, kv=kv, n_sel=200, pad_mode="scatter")
+    probe = make_case(**base)
+    t = 1
+    order = G.expected_keys(orc, probe, t, compressed_first)
+    n = len(order)
+    chunk = -(-keys // (16 if kernel == 1 else 32)) * (16 if kernel == 1 else 32)
+    where = sorted({i for i in (chunk - 1, chunk, 2 * chunk - 1, 2 * chunk, 3 * chunk - 1, n - 1) if 0 <= i < n})
+    dsv4_attn_set_split_keys(keys)
+    try:
+        for i in where:
+            if order[i] is None:  # an unused C4 entry: the nearest used key before it
+                i = max(j for j in range(i) if order[j] is not None)
+            case = make_case(**base)
+            pool, slot = order[i]
+            G.spike_slot(case, "swa_pool" if pool == "swa" else "extra_pool", slot, t)
+            out, lse = G.run_forward(case)
+            ro, rl, _ = orc.attention(case)
+            G.compare(out, lse, ro, rl, what=f"boundary key {i} split {keys} R{R} k{kernel} {kv}")
+            assert rl[t, 0] > 50.0, (i, rl[t, 0])
+    finally:
+        dsv4_attn_set_split_keys(0)
+
+
+@pytest.mark.parametrize("R", [0, 128])
+def test_growing_scores_fp8(orc, R):
+    """The growing-score test on packed FP8 pools: every key row of row 0 is
+    re-stored (quantised) as the blend towards 2 * q[0, head 0]."""
+    from synth import store_float_rows
+
+    case = make_case(seq_lens=[40000, 300], n_q=[1, 2], H=64, R=R, seed=54, kv="fp8")
+    q0 = torch.from_numpy(case.q[0, 0].view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    swa, ext = orc.gather(case, 0)
+    n = len(swa) + len(ext)
+    rng = np.random.default_rng(9)
+    for pool_name, slots, base in (("swa_pool", swa, 0), ("extra_pool", ext, len(swa))):
+        beta = (base + np.arange(len(slots))) / max(n - 1, 1)
+        rows = (1.0 - beta)[:, None] * rng.standard_normal((len(slots), 512)) + beta[:, None] * 2.0 * q0[None, :]
+        store_float_rows(getattr(case, pool_name), "fp8", slots, rows.astype(np.float32))
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"growing-fp8-R{R}")
+
+
+@pytest.mark.parametrize("keys", [32, 64, 160, 1024])
+def test_forced_split_sizes_fp8(orc, keys):
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
+
+    case = make_case(seq_lens=[3000, 700, 5], n_q=[2, 3, 1], H=100, R=4, seed=31, pad_mode="scatter", kv="fp8")
+    ro, rl, _ = orc.attention(case)
+    dsv4_attn_set_split_keys(keys)
+    try:
+        out, lse = G.run_forward(case)
+    finally:
+        dsv4_attn_set_split_keys(0)
+    G.compare(out, lse, ro, rl, what=f"fp8 split{keys}")
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS, indirect=True)
@@ -432,11 +516,11 @@ def test_validate_mode_rejects_bad_index(monkeypatch):
 
 
 # --------------------------------------------------------------------------
-# split arrival counters and graph capture
+# interleaved plans, workspace growth and graph capture
 # --------------------------------------------------------------------------
-def test_interleaved_calls_reset_split_counters():
-    """Alternating cases with different split plans must stay bit-identical:
-    every merging workgroup leaves its arrival counter at zero."""
+def test_interleaved_calls_bit_identical():
+    """Alternating cases with different split plans (and so different
+    workspace layouts) stay bit-identical to their first results."""
     from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
 
     cases = [small_case(12), small_case(15), make_case(seq_lens=[2000] * 9, n_q=1, H=64, R=128, seed=4)]
@@ -452,6 +536,55 @@ def test_interleaved_calls_reset_split_counters():
                         assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
             finally:
                 dsv4_attn_set_split_keys(0)
+
+
+def test_reserve_then_capture_first_forward():
+    """After releasing the workspace, a reserve followed by a capture whose
+    forward is the first call since then works and replays correctly; without
+    the reserve the captured call refuses to allocate (DSV4_ERR_WORKSPACE)
+    instead of breaking the capture."""
+    from hybrid_sparse_mqa_amd import (Dsv4Error, dsv4_attn_forward, dsv4_attn_plan, dsv4_attn_workspace_release,
+                                       dsv4_attn_workspace_reserve)
+
+    case = make_case(seq_lens=[3000, 5000, 700], n_q=[1, 4, 2], H=64, R=4, seed=14)
+    g = G.to_gpu(case)
+    splits, _, _ = dsv4_attn_plan(case.T, case.H, case.R, case.W, case.K, case.extra_page_table.shape[1])
+    assert splits > 1  # the call needs the workspace
+    ref_out, ref_lse = G.run_forward(case, g)
+
+    def call(out, lse):
+        dsv4_attn_forward(g["q"], g["swa_pool"], g["swa_page_table"], g["extra_pool"], g["extra_page_table"],
+                          g["c4_indices"], g["seq_lens"], g["qo_indptr"], g["sink"], case.R, case.W, case.scale,
+                          out=out, lse=lse)
+
+    out = torch.zeros_like(ref_out)
+    lse = torch.zeros_like(ref_lse)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    dsv4_attn_workspace_release()
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(Dsv4Error, match="ERR_WORKSPACE"):
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                call(out, lse)
+    torch.cuda.synchronize()
+    dsv4_attn_workspace_reserve(case.T * splits * case.H * 1028, stream.cuda_stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            call(out, lse)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), rep
+        G.run_forward(make_case(seq_lens=[9000] * 40, n_q=1, H=64, R=128, seed=4))  # grows the workspace
+    # The buffer the graph captured is kept after growth: replays stay correct.
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
 
 
 def test_graph_capture_replays_match_eager():
