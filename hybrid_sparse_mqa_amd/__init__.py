@@ -9,6 +9,8 @@ from .api import (  # noqa: F401
     dsv4_abi_version,
     dsv4_attn_debug_keys,
     dsv4_attn_forward,
+    dsv4_attn_forward_noalloc,
+    dsv4_attn_noalloc_scratch_bytes,
     dsv4_attn_gather_slots,
     dsv4_kv_pack_fp8,
     dsv4_c4_topk,

@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
         L.dsv4_attn_forward.restype = ctypes.c_int
         L.dsv4_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                         P, P, ctypes.c_void_p]
+        L.dsv4_attn_forward_noalloc.restype = ctypes.c_int
+        L.dsv4_attn_forward_noalloc.argtypes = L.dsv4_attn_forward.argtypes
+        L.dsv4_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.dsv4_attn_gather_slots.restype = ctypes.c_int
         L.dsv4_attn_gather_slots.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
                                              ctypes.c_void_p]

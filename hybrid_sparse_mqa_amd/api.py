@@ -30,8 +30,10 @@ def dsv4_attn_forward(
     lse: Optional[torch.Tensor] = None,
     return_lse: bool = True,
     stream: Optional[int] = None,
+    noalloc: bool = False,
 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """SWA + (C4 | C128) attention of every query row; returns (out, lse)."""
+    """SWA + (C4 | C128) attention of every query row; returns (out, lse).
+    noalloc: call dsv4_attn_forward_noalloc instead."""
     L = N.load()
     T, H = q.shape[0], q.shape[1]
     if out is None:
@@ -41,10 +43,20 @@ def dsv4_attn_forward(
     descs = [N.describe(x) for x in (q, swa_pool, swa_page_table, extra_pool, extra_page_table, c4_indices,
                                      seq_lens, qo_indptr, sink, out, lse)]
     st = N.stream_handle(q.device) if stream is None else stream
-    N.check(L.dsv4_attn_forward(
-        *[N.ref(d) for d in descs[:9]], int(compress_ratio), int(window), float(scale),
-        N.ref(descs[9]), N.ref(descs[10]), ctypes.c_void_p(st)))
+    fn = L.dsv4_attn_forward_noalloc if noalloc else L.dsv4_attn_forward
+    N.check(fn(*[N.ref(d) for d in descs[:9]], int(compress_ratio), int(window), float(scale),
+               N.ref(descs[9]), N.ref(descs[10]), ctypes.c_void_p(st)))
     return out, lse
+
+
+def dsv4_attn_forward_noalloc(*args, **kwargs) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """dsv4_attn_forward through the no-allocation entry point (pass ``out``
+    and ``lse`` to allocate nothing here either)."""
+    return dsv4_attn_forward(*args, noalloc=True, **kwargs)
+
+
+def dsv4_attn_noalloc_scratch_bytes() -> int:
+    return int(N.load().dsv4_attn_noalloc_scratch_bytes())
 
 
 def dsv4_attn_gather_slots(

@@ -26,6 +26,13 @@ using namespace dsv4;
 // references, and the runtime then has no device symbol for the host's.)
 static __device__ __attribute__((aligned(256))) uint8_t g_zero_row[4096];
 
+// Split partials of dsv4_attn_forward_noalloc, for callers that cannot
+// allocate: one copy per device, held until the process ends.  Host code
+// must never pass `scratch` itself to a kernel (that is a host-side stand-in):
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -188,6 +195,7 @@ struct DeviceState {
     // still write into them, so they live until dsv4_attn_workspace_release.
     std::vector<void*> retired;
     const void* zero_row = nullptr;  // device address of g_zero_row
+    void* scratch = nullptr;         // device address of `scratch`
 };
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
@@ -222,6 +230,14 @@ dsv4_status ensure_zero_row(DeviceState* d) {
     void* p = nullptr;
     DSV4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(g_zero_row)));
     d->zero_row = p;
+    return DSV4_OK;
+}
+
+dsv4_status ensure_scratch(DeviceState* d) {
+    if (d->scratch != nullptr) return DSV4_OK;
+    void* p = nullptr;
+    DSV4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    d->scratch = p;
     return DSV4_OK;
 }
 
@@ -661,12 +677,18 @@ dsv4_status dsv4_c4_topk(const dsv4_tensor* scores, const dsv4_tensor* num_candi
     return DSV4_OK;
 }
 
-dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
-                              const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
-                              const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,
-                              const dsv4_tensor* qo_indptr, const dsv4_tensor* sink, int32_t compress_ratio,
-                              int32_t window, float scale, const dsv4_tensor* out, const dsv4_tensor* lse,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both forward entry points.  noalloc: split partials go to the static
+// `scratch` array (calls whose partials do not fit are refused) and the
+// timing hook is ignored (its events would be created on demand).
+dsv4_status forward_impl(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
+                         const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
+                         const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens, const dsv4_tensor* qo_indptr,
+                         const dsv4_tensor* sink, int32_t compress_ratio, int32_t window, float scale,
+                         const dsv4_tensor* out, const dsv4_tensor* lse, void* stream, bool noalloc) {
     if (q == nullptr) return fail(DSV4_ERR_INVALID, "q: NULL descriptor");
     DSV4_TRY(check_tensor("q", q, DSV4_BF16, 3, {-1, -1, DSV4_HEAD_DIM}));
     const int64_t T = q->shape[0], H = q->shape[1];
@@ -735,9 +757,22 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     if (a.splits > 1) {
         const size_t n_part = (size_t)T * a.splits * H;
         const size_t bytes_o = n_part * DSV4_HEAD_DIM * sizeof(uint16_t);
-        DSV4_TRY(ensure_workspace(d, bytes_o + n_part * sizeof(float), st));
-        a.ws_o = (uint16_t*)d->ws;
-        a.ws_lse = (float*)((char*)d->ws + bytes_o);
+        const size_t need = bytes_o + n_part * sizeof(float);
+        void* ws = nullptr;
+        if (noalloc) {
+            if (need > kScratchBytes)
+                return fail(DSV4_ERR_WORKSPACE,
+                            "the call's split partials need %zu bytes, above the %zu-byte static scratch of the "
+                            "no-allocation entry point (T x splits x H x 1028 bytes)",
+                            need, kScratchBytes);
+            DSV4_TRY(ensure_scratch(d));
+            ws = d->scratch;
+        } else {
+            DSV4_TRY(ensure_workspace(d, need, st));
+            ws = d->ws;
+        }
+        a.ws_o = (uint16_t*)ws;
+        a.ws_lse = (float*)((char*)ws + bytes_o);
     }
 
     if (g_dbg_keys != nullptr) {
@@ -751,7 +786,8 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
     }
 
     TimingRec rec{};
-    if (g_timing) {
+    const bool timing = g_timing && !noalloc;
+    if (timing) {
         rec.e0 = take_event();
         rec.e1 = take_event();
         rec.e2 = a.splits > 1 ? take_event() : nullptr;  // no merge kernel: no interval to time
@@ -759,13 +795,39 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
         DSV4_HIP(record_event(rec.e0, st));
     }
     DSV4_HIP(launch_attention(a, layout, st));
-    if (g_timing) DSV4_HIP(record_event(rec.e1, st));
+    if (timing) DSV4_HIP(record_event(rec.e1, st));
     if (a.splits > 1) DSV4_HIP(launch_merge(a, st));
-    if (g_timing) {
+    if (timing) {
         if (rec.e2 != nullptr) DSV4_HIP(record_event(rec.e2, st));
         g_timing_recs.push_back(rec);
     }
     return DSV4_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool, const dsv4_tensor* swa_page_table,
+                              const dsv4_tensor* extra_pool, const dsv4_tensor* extra_page_table,
+                              const dsv4_tensor* c4_indices, const dsv4_tensor* seq_lens,
+                              const dsv4_tensor* qo_indptr, const dsv4_tensor* sink, int32_t compress_ratio,
+                              int32_t window, float scale, const dsv4_tensor* out, const dsv4_tensor* lse,
+                              void* stream) {
+    return forward_impl(q, swa_pool, swa_page_table, extra_pool, extra_page_table, c4_indices, seq_lens, qo_indptr,
+                        sink, compress_ratio, window, scale, out, lse, stream, false);
+}
+
+dsv4_status dsv4_attn_forward_noalloc(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
+                                      const dsv4_tensor* swa_page_table, const dsv4_tensor* extra_pool,
+                                      const dsv4_tensor* extra_page_table, const dsv4_tensor* c4_indices,
+                                      const dsv4_tensor* seq_lens, const dsv4_tensor* qo_indptr,
+                                      const dsv4_tensor* sink, int32_t compress_ratio, int32_t window, float scale,
+                                      const dsv4_tensor* out, const dsv4_tensor* lse, void* stream) {
+    return forward_impl(q, swa_pool, swa_page_table, extra_pool, extra_page_table, c4_indices, seq_lens, qo_indptr,
+                        sink, compress_ratio, window, scale, out, lse, stream, true);
+}
+
+size_t dsv4_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"

@@ -128,6 +128,30 @@ dsv4_status dsv4_attn_forward(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
                               void* stream);
 
 /*
+ * dsv4_attn_forward_noalloc -- dsv4_attn_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, kernels, plan and
+ * results as dsv4_attn_forward, but it never allocates: the split partials go
+ * to a static per-device scratch array of dsv4_attn_noalloc_scratch_bytes()
+ * bytes (32 MiB) that the library's code object holds on every device it is
+ * loaded on until the process ends.  A call whose partials would not fit
+ * (T x splits x H x 1028 bytes; splits from dsv4_attn_plan) returns
+ * DSV4_ERR_WORKSPACE before any launch.  Every call on a device shares that
+ * device's scratch: calls on one device that could run at the same time
+ * (different streams without an ordering between them) race and give wrong
+ * results.  The timing hook does not apply to this entry point.
+ */
+dsv4_status dsv4_attn_forward_noalloc(const dsv4_tensor* q, const dsv4_tensor* swa_pool,
+                                      const dsv4_tensor* swa_page_table, const dsv4_tensor* extra_pool,
+                                      const dsv4_tensor* extra_page_table, const dsv4_tensor* c4_indices,
+                                      const dsv4_tensor* seq_lens, const dsv4_tensor* qo_indptr,
+                                      const dsv4_tensor* sink, int32_t compress_ratio, int32_t window, float scale,
+                                      const dsv4_tensor* out, const dsv4_tensor* lse, void* stream);
+
+/* Size in bytes of the no-allocation entry point's static scratch. */
+size_t dsv4_attn_noalloc_scratch_bytes(void);
+
+/*
  * dsv4_kv_pack_fp8 -- the KV store in front of the attention: n new K rows
  * (with RoPE applied; V = K) quantised into packed FP8 records at given slots
  * (the cache write of the walk-through page, section 3; the 584-byte FP8 +
