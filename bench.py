@@ -394,7 +394,8 @@ def bench_topk(args) -> int:
         "config": {"workload": f"c4_topk512_b{T}_n262144", "rows": T, "candidates": n, "k": K,
                    "input_sets": n_sets, "cache": "cold-rotated",
                    "timed": "HIP graph replay, events around it on the kernels' stream", "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "topk_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "topk_chunk_kernel + topk_finish_kernel (one call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
         "cpu_baseline": None,

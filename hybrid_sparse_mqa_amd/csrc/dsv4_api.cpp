@@ -196,7 +196,9 @@ struct DeviceState {
     std::vector<void*> retired;
     const void* zero_row = nullptr;  // device address of g_zero_row
     void* scratch = nullptr;         // device address of `scratch`
+    uint32_t* topk_count = nullptr;  // per-row counter and flag of the long-row top-k path, zero between calls
 };
+constexpr int kTopkMaxRowsSplit = 65535;  // rows of a long-row top-k call (grid y)
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
 int32_t g_force_split_keys = 0;
@@ -230,6 +232,22 @@ dsv4_status ensure_zero_row(DeviceState* d) {
     void* p = nullptr;
     DSV4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(g_zero_row)));
     d->zero_row = p;
+    return DSV4_OK;
+}
+
+// The long-row top-k counters: allocated and zeroed once per device (outside
+// any capture); every call leaves them at zero.
+dsv4_status ensure_topk_count(DeviceState* d, hipStream_t st) {
+    if (d->topk_count != nullptr) return DSV4_OK;
+    if (stream_capturing(st))
+        return fail(DSV4_ERR_WORKSPACE, "the top-k counters are not set up and the stream is being captured; call "
+                                        "dsv4_attn_workspace_reserve before capturing");
+    void* p = nullptr;
+    if (hipMalloc(&p, 2 * sizeof(uint32_t) * kTopkMaxRowsSplit) != hipSuccess)
+        return fail(DSV4_ERR_WORKSPACE, "hipMalloc of the top-k counters failed");
+    DSV4_HIP(hipMemset(p, 0, 2 * sizeof(uint32_t) * kTopkMaxRowsSplit));
+    DSV4_HIP(hipDeviceSynchronize());
+    d->topk_count = (uint32_t*)p;  // kept for the life of the process
     return DSV4_OK;
 }
 
@@ -512,6 +530,7 @@ dsv4_status dsv4_attn_workspace_reserve(size_t bytes, void* stream) {
     std::lock_guard<std::mutex> lk(g_mu);
     DeviceState* d = device_state(dev);
     DSV4_TRY(ensure_zero_row(d));
+    DSV4_TRY(ensure_topk_count(d, (hipStream_t)stream));
     return ensure_workspace(d, bytes, (hipStream_t)stream);
 }
 
@@ -673,6 +692,16 @@ dsv4_status dsv4_c4_topk(const dsv4_tensor* scores, const dsv4_tensor* num_candi
     a.T = (int32_t)T;
     a.K = (int32_t)K;
     a.ld = (int32_t)ld;
+    const size_t ws_bytes = T <= kTopkMaxRowsSplit ? topk_workspace_bytes(T, ld, K) : 0;
+    int dev = 0;
+    DSV4_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (ws_bytes > 0) {  // long rows: several workgroups per row, survivor lists in the workspace
+        DeviceState* d = device_state(dev);
+        DSV4_TRY(ensure_topk_count(d, st));
+        DSV4_TRY(ensure_workspace(d, ws_bytes, st));
+        topk_bind_workspace(a, d->ws, d->topk_count);
+    }
     DSV4_HIP(launch_topk(a, st));
     return DSV4_OK;
 }

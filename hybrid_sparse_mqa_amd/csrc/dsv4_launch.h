@@ -79,6 +79,9 @@ struct PackArgs {
 // C4 top-k: per row t, the K highest of scores[t][0 .. n_cand[t]) (ties: the
 // lower index), ascending, then -1, into out[t][0 .. K).
 constexpr int kTopkMaxK = 2048;
+constexpr int kTopkBins = 4096;      // first radix digit: the top 12 key bits
+constexpr int kTopkChunk = 16384;    // candidates per workgroup, multi-workgroup path
+constexpr int kTopkSplitMin = 32768; // rows this long (ld) take the multi-workgroup path
 struct TopkArgs {
     const float* scores;  // [T, s_ld]
     int64_t s_ld;
@@ -86,7 +89,17 @@ struct TopkArgs {
     int32_t* out;           // [T, out_ld]
     int64_t out_ld;
     int32_t T, K, ld;       // ld: candidates per row available (n_cand is clamped to it)
+    // Multi-workgroup path (ws_list null: one workgroup per row).  The
+    // counters are zero between calls (zeroed when the workspace is
+    // allocated, and by the finishing kernel after use).
+    uint64_t* ws_list;   // [T, ws_cap] (key << 32) | index of each chunk's survivors
+    int64_t ws_cap;
+    uint32_t* ws_count;  // [T, 2]: survivors appended so far, list-incomplete flag
 };
+// List workspace bytes of the multi-workgroup path for T rows (0 if ld is
+// short); binding takes the list workspace and the per-row counters.
+size_t topk_workspace_bytes(int64_t T, int64_t ld, int64_t K);
+void topk_bind_workspace(TopkArgs& a, void* ws, uint32_t* counters);
 
 hipError_t launch_attention(const AttnArgs& a, Layout layout, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, hipStream_t stream);

@@ -193,6 +193,13 @@ dsv4_status dsv4_kv_pack_fp8(const dsv4_tensor* k, const dsv4_tensor* slots, con
  *                  -0.0 equals +0.0.  The result is the c4_indices argument
  *                  of dsv4_attn_forward.
  *  stream          hipStream_t
+ *
+ * Rows of ld >= 32768 candidates (up to 65535 rows) use several workgroups
+ * per row: the scores are read once, each 16384-candidate chunk appends its
+ * own top K to the row's list in the library workspace (about 8 x (K + 1024)
+ * bytes per chunk; see dsv4_attn_workspace_reserve: it grows on demand,
+ * never under stream capture, and calls that could run at the same time on
+ * one device race on it), and one workgroup per row selects from the list.
  */
 dsv4_status dsv4_c4_topk(const dsv4_tensor* scores, const dsv4_tensor* num_candidates, const dsv4_tensor* indices,
                          void* stream);

@@ -93,3 +93,71 @@ def test_topk_feeds_the_attention():
     out, lse = G.run_forward(case)
     ro, rl, _ = oracle_mod.Oracle().attention(dataclasses.replace(case, c4_indices=want.astype(np.int32)))
     G.compare(out, lse, ro, rl, what="topk -> attention")
+
+
+# --------------------------------------------------------------------------
+# Long rows (ld >= 32768): several workgroups per row build the first-digit
+# histogram and compact the threshold digit's candidates; one finishes.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("k", [512, 2048, 1])
+def test_topk_long_rows_ragged(k):
+    rng = np.random.default_rng(100 + k)
+    ld = 1 << 17
+    n = np.array([0, 1, k - 1, k, k + 1, 16383, 16384, 16385, 50000, ld - 1, ld], np.int32)
+    n = np.clip(n, 0, ld)
+    T = len(n)
+    scores = rng.standard_normal((T, ld)).astype(np.float32)
+    scores[5] = np.round(scores[5] * 8) / 8          # ties at every digit
+    scores[6, ::2] = -0.0                             # -0 ties with +0
+    scores[6, 1::2] = 0.0
+    log(f"topk long rows: {T} x {ld}, k={k}")
+    _check(scores, n, k, f"long k={k}")
+
+
+@pytest.mark.parametrize("ld", [20000, 1 << 18], ids=["one-workgroup", "multi-workgroup"])
+def test_topk_narrow_band(ld):
+    """Scores 1 + 1e-4 N(0,1): nearly every candidate shares the first digit
+    (far more than the 4096 the LDS list holds) without being tied, so the
+    later digits and, for rounded values, the index tie-break decide."""
+    rng = np.random.default_rng(7)
+    T = 4
+    scores = (1.0 + 1e-4 * rng.standard_normal((T, ld))).astype(np.float32)
+    scores[1] = (1.0 + 1e-4 * np.round(rng.standard_normal(ld) * 16) / 16).astype(np.float32)
+    n = np.array([ld, ld, ld - 1000, 9000], np.int32)
+    log(f"topk narrow band ld={ld}")
+    _check(scores, n, 512, f"narrow band ld={ld}")
+
+
+@pytest.mark.parametrize("ld", [30000, 1 << 17], ids=["one-workgroup", "multi-workgroup"])
+@pytest.mark.parametrize("n_bin", [4095, 4096, 4097])
+def test_topk_threshold_digit_at_list_capacity(ld, n_bin):
+    """Exactly n_bin candidates share the top first digit (values in
+    [1, 1.125), some of them tied) and the rest lie far below: the threshold
+    digit holds 4095, 4096 (the LDS list capacity) or 4097 candidates."""
+    rng = np.random.default_rng(n_bin)
+    T = 3
+    scores = rng.uniform(-4.0, 0.5, (T, ld)).astype(np.float32)
+    for t in range(T):
+        where = rng.choice(ld, size=n_bin, replace=False)
+        vals = rng.uniform(1.0, 1.125, n_bin).astype(np.float32)
+        vals[: n_bin // 4] = np.float32(1.0625)  # a block of ties inside the digit
+        scores[t, where] = vals
+    n = np.full(T, ld, np.int32)
+    log(f"topk threshold digit of {n_bin}, ld={ld}")
+    _check(scores, n, 512, f"digit {n_bin} ld={ld}")
+
+
+def test_topk_one_chunk_overflows_its_stage():
+    """One 16384-candidate chunk holds 5000 equal scores above every other
+    candidate (more survivors than a chunk stages), while the row's total
+    stays under its list capacity: the row must still come out exact."""
+    rng = np.random.default_rng(11)
+    T, ld = 3, 1 << 18
+    scores = rng.standard_normal((T, ld)).astype(np.float32)
+    scores[0, 100:5100] = 5.0
+    scores[1, 20000:25000] = 5.0
+    scores[2, 20000:22000] = 5.0  # fits the stage: the normal path
+    n = np.full(T, ld, np.int32)
+    log("topk one chunk overflowing")
+    for k in (512, 2048):
+        _check(scores, n, k, f"stage overflow k={k}")
