@@ -34,6 +34,8 @@ import numpy as np  # noqa: E402
 
 METRIC = "decode attention tokens/s + achieved HBM GB/s (% peak), C4/C128 at batch×ctx"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 << 20
 KV_ROW_BYTES = {"bf16": 1024, "fp8": 584}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -84,7 +86,27 @@ def algorithmic_bytes(case) -> dict:
             ext_rows += len(np.unique(ids[ids >= 0]))
     kv = (swa_rows + ext_rows) * KV_ROW_BYTES[case.kv]
     return dict(total=q + out + lse + idx + kv, kv=kv, q=q, out=out, lse=lse, idx=idx,
-                kv_rows=swa_rows + ext_rows)
+                kv_rows=swa_rows + ext_rows, flops=attention_flops(case))
+
+
+def attention_flops(case) -> int:
+    """Multiply-add work of one call: per query row and key, 2*H*512 for the
+    scores and 2*H*512 for P.V (keys: the window plus the used C4 entries or
+    the visible C128 entries of the row)."""
+    total_keys = 0
+    for r in range(case.B):
+        lo_t, hi_t = int(case.qo_indptr[r]), int(case.qo_indptr[r + 1])
+        n_q = hi_t - lo_t
+        L = int(case.seq_lens[r])
+        for t in range(lo_t, hi_t):
+            p = L - n_q + (t - lo_t)
+            keys = min(case.W, p + 1)
+            if case.R == 128:
+                keys += (p + 1) // 128
+            elif case.R == 4:
+                keys += int((case.c4_indices[t] >= 0).sum())
+            total_keys += keys
+    return 4 * case.H * 512 * total_keys
 
 
 def describe_workload(n, case) -> dict:
@@ -420,7 +442,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3,
-                    help="workload 1..5 (default 3: C128 decode, batch 64 x 128K, the largest)")
+                    help="workload 1..7 (default 3: C128 decode, batch 64 x 128K, the largest decode workload; "
+                         "6 and 7 are the C4 and C128 sparse-prefill workloads)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -592,6 +615,11 @@ def main() -> int:
     merge_avg_ms = merge_ms / calls
     kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
     achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
+    tflops = ab["flops"] / (split_avg_ms * 1e-3) / 1e12
+    # The bound the split kernel sits under: HBM below the ridge point
+    # (decode and verify), the bf16 MFMA peak above it (prefill: 2048 rows
+    # per request bring 64 KiB of Q and of out per row and ~1 MFLOP per key).
+    mfma_bound = ab["flops"] / max(kernel_bytes, 1) > RIDGE_FLOP_PER_BYTE
     kernel_name = split_kernel_name(kernel)
 
     traffic = None
@@ -630,7 +658,19 @@ def main() -> int:
             "eager_split_kernel_event_ms": e_split / max(e_calls, 1),
             "eager_merge_kernel_event_ms": e_merge / max(e_calls, 1),
         },
-        "roofline": {
+        "roofline": ({
+            "bound": "mfma",
+            "kernel": kernel_name,
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": ab["flops"],
+            "algorithmic_bytes_per_launch": kernel_bytes,
+            "hbm_gbs": achieved,
+            "avg_launch_ms": split_avg_ms,
+        } if mfma_bound else {
             "bound": "hbm",
             "kernel": kernel_name,
             "achieved": achieved,
@@ -639,8 +679,10 @@ def main() -> int:
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kernel_bytes,
+            "algorithmic_flops_per_launch": ab["flops"],
+            "mfma_tflops": tflops,
             "avg_launch_ms": split_avg_ms,
-        },
+        }),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

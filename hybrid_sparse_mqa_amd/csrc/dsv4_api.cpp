@@ -281,12 +281,16 @@ dsv4_status ensure_workspace(DeviceState* d, size_t bytes, hipStream_t st) {
 
 // Kernel layout: FP8 pools -> the FP8 kernel; otherwise the variant forced
 // by dsv4_attn_set_kernel, else the 16-head kernel for at most 16 heads (no
-// padding of heads) and the 32-head score/PV role kernel above that.
-// Measured on MI355X (graph replay, split + merge per call), role kernel vs
-// the best dim-split kernel: C4 decode 32 rows x 640 keys 16.8 vs 17.1 us
-// (32-head, four splits each); C128 decode 64 rows x 1152 keys 30.9 vs
-// 33.2 us (64-head, four splits); C4 verify 128 rows 28.6 vs 31.0 us.
-Layout choose_layout(int32_t H, bool fp8) {
+// padding of heads); above that the 64-head kernel when the rows alone give
+// every compute unit at least two 64-head workgroups (prefill / extend:
+// compute-bound, and a 64-head tile does twice the MFMA work per LDS tile
+// copy), else the 32-head score/PV role kernel.  Measured on MI355X (graph
+// replay per call): C4 prefill 4 x 2048 rows 1.02 ms (64-head) vs 1.28 ms
+// (roles); C128 prefill 0.74 vs 0.94 ms; decode and verify (32-128 rows):
+// roles fastest -- C4 decode 32 rows 16.8 vs 17.1 us (32-head dim split),
+// C128 decode 64 rows 30.9 vs 33.2 us (64-head), C4 verify 128 rows 28.6 vs
+// 31.0 us.
+Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8) {
     if (fp8) return Layout::kFp8;
     switch (g_force_kernel) {
         case DSV4_KERNEL_H16: return Layout::kNarrow;
@@ -296,11 +300,8 @@ Layout choose_layout(int32_t H, bool fp8) {
         default: break;
     }
     if (H <= kNarrowHeadsPerBlock) return Layout::kNarrow;
-    // The score/PV role kernel, with 32-head blocks, is the fastest measured
-    // on every bf16 workload with more heads: C4 decode (32 rows, four
-    // splits), C128 decode (64 rows, two splits) and C4 verify (128 rows,
-    // unsplit).  The 32- and 64-head dim-split kernels stay available through
-    // dsv4_attn_set_kernel.
+    const int64_t blocks64 = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
+    if (blocks64 >= 2 * (int64_t)cus) return Layout::kWide;
     return Layout::kRoles32;
 }
 
@@ -517,7 +518,7 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
         DeviceState* d = device_state(dev);
         if (d) cus = d->cus;
     }
-    const Layout layout = choose_layout(num_heads, kv_fp8 != 0);
+    const Layout layout = choose_layout(num_rows, num_heads, cus, kv_fp8 != 0);
     plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages),
                 layout, splits, keys_per_split);
     if (kernel != nullptr) *kernel = kernel_id(layout);
@@ -770,7 +771,7 @@ dsv4_status forward_impl(const dsv4_tensor* q, const dsv4_tensor* swa_pool, cons
     a.T = (int32_t)T;
     a.H = (int32_t)H;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const Layout layout = choose_layout(a.H, swa.fp8);
+    const Layout layout = choose_layout(a.T, a.H, d->cus, swa.fp8);
     plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), layout, &a.splits,
                 &a.chunk);
     a.head_blocks = (int32_t)((H + heads_per_block(layout) - 1) / heads_per_block(layout));

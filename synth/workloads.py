@@ -372,13 +372,25 @@ CONFIGS = {
         name="c4_decode_fp8_b8_s1m_h64",
         desc="C4 decode, batch 8, seq_len 1048576 (262144 C4 candidates), top-512, FP8-packed KV",
     ),
+    # Sparse prefill / extend: many query rows per request, each with its
+    # own causal window and (C4) its own top-512 index list.
+    6: dict(
+        name="c4_prefill_b4x2048_p32k_h64",
+        desc="C4 sparse prefill, 4 requests x 2048 new rows after a 32768-token prefix, per-row top-512 C4 entries",
+    ),
+    7: dict(
+        name="c128_prefill_b4x2048_p32k_h64",
+        desc="C128 prefill, 4 requests x 2048 new rows after a 32768-token prefix, every visible C128 entry",
+    ),
 }
 
 
 def make_config(n: int, seed: Optional[int] = None, keep_logical: bool = False, batch: Optional[int] = None,
-                index_sets: int = 1) -> Case:
-    """Inputs for workload ``n`` (1..5); default seed ``1000 + n``.
-    ``index_sets`` (C4 workloads): see make_case."""
+                index_sets: int = 1, rows: Optional[int] = None) -> Case:
+    """Inputs for workload ``n`` (1..7); default seed ``1000 + n``.
+    ``index_sets`` (C4 workloads): see make_case.  ``batch`` overrides the
+    number of requests (for the prefill workloads, ``rows`` the rows per
+    request)."""
     if seed is None:
         seed = 1000 + n
     name = CONFIGS[n]["name"]
@@ -401,4 +413,9 @@ def make_config(n: int, seed: Optional[int] = None, keep_logical: bool = False, 
         B = batch or 8
         return make_case(seq_lens=[1048576] * B, n_q=1, H=64, R=4, kv="fp8", seed=seed,
                          keep_logical=keep_logical, index_sets=index_sets, name=name)
+    if n in (6, 7):
+        B = batch or 4
+        n_q = rows or 2048
+        return make_case(seq_lens=[32768 + n_q] * B, n_q=n_q, H=64, R=4 if n == 6 else 128, seed=seed,
+                         keep_logical=keep_logical, index_sets=index_sets if n == 6 else 1, name=name)
     raise KeyError(n)

@@ -196,3 +196,11 @@ def test_keys_workloads_default_plan(orc, n):
 def test_keys_workloads_other_kernels(orc, n, kernel):
     case = make_config(n)
     check_keys(orc, case, kernel, what=f"{case.name}-k{kernel}")
+
+
+@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64])
+@pytest.mark.parametrize("n", [6, 7])
+def test_keys_prefill_reduced(orc, n, kernel):
+    """Prefill rows (2 requests x 96 rows): every row's keys, bit-exact."""
+    case = make_config(n, batch=2, rows=96)
+    check_keys(orc, case, kernel, what=f"{case.name}-reduced-k{kernel}")

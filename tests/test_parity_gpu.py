@@ -662,3 +662,35 @@ def test_timing_events_eager_and_captured():
         split_ms, merge_ms, n = dsv4_attn_timing_read() if rep == 1 else (1.0, 0.0, 2)
         assert n == 2 and split_ms > 0 and merge_ms >= 0
     assert dsv4_attn_timing_read()[2] == 0
+
+
+# --------------------------------------------------------------------------
+# sparse prefill / extend: many query rows per request, each with its own
+# causal window and (C4) its own top-512 list
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [6, 7])
+def test_prefill_workloads_sampled_rows(orc, n):
+    """The two full-size prefill workloads (4 requests x 2048 rows) in the
+    benchmark's launch plan: the first and last rows of every request and 120
+    random ones against the oracle."""
+    case = make_config(n)
+    rng = np.random.default_rng(n)
+    ends = [int(x) for r in range(case.B) for x in (case.qo_indptr[r], case.qo_indptr[r + 1] - 1)]
+    rows = sorted(set(ends + list(rng.choice(case.T, size=120, replace=False))))
+    log(f"prefill workload {n} ({case.name}) {len(rows)} rows of {case.T}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case, rows=rows)
+    e = G.compare(out, lse, ro, rl, rows=rows, what=case.name)
+    log(f"  max abs err {e[0]:.3g}  lse err {e[1]:.3g}  rel L2 {e[2]:.3g}")
+
+
+@pytest.mark.parametrize("kernel", [0] + BF16_KERNELS, indirect=True)
+@pytest.mark.parametrize("n", [6, 7])
+def test_prefill_reduced_all_rows(orc, n, kernel):
+    """The prefill shapes at 2 requests x 192 rows (a ragged 192 = 1.5 x 128
+    rows, window edges inside the pass), every row, every bf16 variant."""
+    case = make_config(n, batch=2, rows=192)
+    log(f"prefill reduced {n} kernel={kernel} T={case.T}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"{case.name}-reduced-k{kernel}")
