@@ -14,7 +14,9 @@ import threading
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdsv4_attn.so")
+# DSV4_ATTN_LIB may name another build of the same library (for example one
+# whose host code carries sanitizers); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("DSV4_ATTN_LIB") or os.path.join(HERE, "libdsv4_attn.so")
 
 DSV4_BF16, DSV4_F32, DSV4_I32, DSV4_U8 = 1, 2, 3, 4
 STATUS = {0: "OK", 1: "ERR_INVALID", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP", 5: "ERR_CONTRACT"}

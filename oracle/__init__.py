@@ -67,6 +67,8 @@ class Oracle:
     """ctypes handle on one compiled oracle library."""
 
     def __init__(self, path: Optional[str] = None, mutant: int = 0):
+        if path is None and mutant == 0 and os.environ.get("DSV4O_LIB"):
+            path = os.environ["DSV4O_LIB"]  # another build of the same source (e.g. with sanitizers)
         if path is None:
             path = lib_path(mutant)
             if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):

@@ -53,10 +53,12 @@ def test_e4m3fn_table_matches_torch(orc):
 def test_bf16_all_patterns_match_torch(orc):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     ref = bruteforce.bf16_bits_to_f64(bits)
-    got = np.array([orc.bf16_to_double(int(b)) for b in bits[::97]])
-    r = ref[::97]
-    assert np.array_equal(np.isnan(r), np.isnan(got))
-    assert np.array_equal(r[~np.isnan(r)], got[~np.isnan(got)])
+    got = np.array([orc.bf16_to_double(int(b)) for b in bits])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    assert np.array_equal(ref[~np.isnan(ref)], got[~np.isnan(got)])
+    # bit patterns, so that +0/-0 and the infinities are told apart too
+    ok = ~np.isnan(ref)
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
 
 
 # --------------------------------------------------------------------------
