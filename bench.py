@@ -220,7 +220,7 @@ def record_traffic(config: int, split_keys: int, fetch_dir: str, write_dir: str,
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the
     attention, and of a plain copy of known size) into HBM bytes per launch of
     the split kernel, stored with a hash of the kernel sources."""
-    from synth import make_config
+    from synth import make_config, tile_requests
 
     case = make_config(config)
     from hybrid_sparse_mqa_amd import dsv4_attn_plan
@@ -445,6 +445,9 @@ def main() -> int:
                     help="workload 1..7 (default 3: C128 decode, batch 64 x 128K, the largest decode workload; "
                          "6 and 7 are the C4 and C128 sparse-prefill workloads)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="workload 5 only: requests per call, a multiple of 8 (copies of the 8 requests, each "
+                         "copy reading through its own C4 index lists)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-keys", type=int, default=0, help="force keys per split (0 = library plan)")
@@ -483,7 +486,7 @@ def main() -> int:
 
     from hybrid_sparse_mqa_amd import (dsv4_attn_forward, dsv4_attn_plan, dsv4_attn_set_kernel,
                                        dsv4_attn_set_split_keys, dsv4_attn_timing_enable, dsv4_attn_timing_read)
-    from synth import make_config
+    from synth import make_config, tile_requests
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -491,13 +494,25 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    # Workload 5's call touches only ~4 MB, so its cold rotation varies the C4
-    # index lists (and Q) over disjoint sets drawn from the same pools.
+    # Workload 5's call touches only ~4 MB per 8 requests, so its cold
+    # rotation varies the C4 index lists (and Q) over disjoint sets drawn
+    # from the same pools.  --batch B runs B/8 copies of the 8 requests, copy
+    # k reading through its own index set (synth.tile_requests), so that the
+    # batch sweep at 1M tokens needs no per-request pools.
+    copies = 1
+    if args.batch:
+        if args.config != 5 or args.batch % 8:
+            print("--batch applies to workload 5 and takes a multiple of 8", file=sys.stderr)
+            return 2
+        copies = args.batch // 8
     idx_sets = 0
-    if args.config == 5 and not args.sets:
-        # distinct bytes per set: its C4 rows (8 rows x 512 x 584 B) and its Q copy
-        idx_sets = int(-(-3 * MALL_BYTES // (8 * 512 * 584 + 8 * 64 * 1024)))
+    if args.config == 5:
+        # distinct bytes per rotation step: C4 rows (8 x 512 x 584 B) and Q per copy
+        steps_needed = int(-(-3 * MALL_BYTES // (copies * (8 * 512 * 584 + 8 * 64 * 1024))))
+        idx_sets = (args.sets or max(2, steps_needed)) * copies
     case = make_config(args.config, index_sets=max(1, idx_sets))
+    if copies > 1:
+        case = tile_requests(case, copies)
     ab = algorithmic_bytes(case)
     bf = torch.bfloat16
 

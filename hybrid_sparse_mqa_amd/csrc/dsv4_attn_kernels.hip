@@ -1893,81 +1893,135 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Packed FP8 KV: rows staged through registers (one tile ahead), decoded, and
-// written to LDS row-major and as 8-key columns.  E4M3 codes are exact in
-// bf16; the per-token scale multiplies the fp32 non-rotary score partial and
-// is folded into P for the non-rotary PV tiles.
+// Packed FP8 KV.  The raw records stream into a 4-stage LDS ring with direct
+// global->LDS copies (three tiles in flight while one is computed); each wave
+// copies and decodes its own 8 keys of a tile (so the ring needs no barrier),
+// writing them as bf16 to LDS row-major and as 8-key columns.  E4M3 codes are
+// exact in bf16; the per-token scale multiplies the fp32 non-rotary score
+// partial and is folded into P for the non-rotary PV tiles.
+//
+// Ring stage: wave w's 8 records of the tile (key group_key(w, e) at record
+// e) at byte w * 4608 + 576 * e, each record's 576 bytes as stored (448 codes,
+// 64 bf16 rotary dims); the 8 scales in a separate 32-byte slot per wave.
 // ---------------------------------------------------------------------------
+constexpr int kFp8Stages = 4;
+constexpr int kFp8RawWave = 8 * kFp8RecBytes;          // one wave's records of a tile
+constexpr int kFp8RawStage = 4 * kFp8RawWave;
+constexpr int kFp8CopiesPerTile = 6;                   // per wave: 5 record copies + 1 scale copy
+
+// Direct global -> LDS copy of 4 bytes per lane: lane i's bytes land at LDS
+// byte address lds_base + 4*i (see dma16_off).
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base)
+        : "memory");
+}
+
 template <bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_krow[kTileKeys * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t s_kt[4 * 512 * 16];
     __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kFp8Stages][kFp8RawStage];
+    __shared__ __attribute__((aligned(16))) float s_rsc[kFp8Stages][kTileKeys];
     __shared__ int32_t s_slot[kMaxSplitKeys];
-    __shared__ int32_t s_table[kTableCap];
     __shared__ __attribute__((aligned(16))) float s_scale[kTileKeys];
+    // The page-table cache is needed only while the slot list is built, before
+    // the exchange buffer's first use.
+    int32_t* const s_table = (int32_t*)s_sx;
+    static_assert(kTableCap * 4 <= sizeof(s_sx), "page-table cache fits the exchange buffer");
 
     fetch_args(a);
     Item it;
     if (!decode_item(a, it)) return;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int hh = w >> 1, dh = w & 1;
-    const int my_head = it.hb * kWideHeadsPerBlock + hh * 32 + (l & 31);
-    const bool head_ok = my_head < a.H;
 
-    // Q is requested with the first tile's rows (below), not before the
-    // metadata: loads complete in order, so every wait on the chain request
-    // bounds -> slot list -> first tile would otherwise wait for Q as well.
     const RowKeys rk = row_keys(a.m, it.t, l);
     const int k0 = it.s * a.chunk;
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
+    const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
     build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
 
-    // Loads of one tile: lane l < 56 takes codes 8l .. 8l+7 of each record
-    // (in the low 8 bytes of a 16-byte load that stays inside the record),
-    // lanes 56..63 the rotary dims 8(l-56) .. +8; every lane also loads the
-    // key's scale.  Unused keys read the zero row (codes, rotary dims and
-    // scale all zero), so no load sits under a branch and all of them are in
-    // flight together.
-    TileRegs pre;
-    auto issue_loads = [&](int tb) {
+    // Copies of tile j into stage j % 4: five 16-byte copies per lane over
+    // the wave's 8 x 36 record chunks (chunk f = 64 i + l is chunk f % 36 of
+    // record f / 36; the last copy has 32 lanes), and one 4-byte copy of the
+    // scales (lanes 0..7).  Lane k < 32 resolves the record and scale
+    // addresses of tile key k; each copying lane fetches its key's addresses
+    // with a cross-lane permute.  Unused keys read the zero row (codes,
+    // rotary dims and scale all zero).
+    int src_lane[5], chunk_off[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int f = 64 * i + l;
+        const int e = min(f / 36, 7);
+        src_lane[i] = 4 * group_key(w, e);
+        chunk_off[i] = 16 * (f - 36 * (f / 36));
+    }
+    const int sc_src = 4 * group_key(w, l & 7);
+    auto bperm64 = [](int src4, uint64_t v) -> uint64_t {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)(uint32_t)v);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)(uint32_t)(v >> 32));
+        return ((uint64_t)hi << 32) | lo;
+    };
+    auto issue_tile = [&](int j) {
+        const int tb = j * kTileKeys;
+        uint64_t rec_ad, sc_ad;
+        {
+            const int key = tb + (l & 31);
+            const int32_t slot = key < n_here ? s_slot[key] : -1;
+            const uint8_t* page = (k0 + key < rk.n_swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
+            rec_ad = (uint64_t)(uintptr_t)(slot >= 0 ? page + (slot & 255) * kFp8RecBytes : a.zero_row);
+            sc_ad = (uint64_t)(uintptr_t)(slot >= 0 ? page + kFp8ScaleOffset + 4 * (slot & 255) : a.zero_row);
+        }
+        if constexpr (kDbg) {
+            if (l < 32) a.dbg_keys[dbg_unit(a, it) * a.chunk + tb + l] = rec_ad;
+        }
+        const uint32_t dst = lds_addr(&s_raw[j % kFp8Stages][w * kFp8RawWave]);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const uint8_t* row = (const uint8_t*)(uintptr_t)bperm64(src_lane[i], rec_ad);
+            if (i < 4 || l < 32) dma16_off<0>(row + chunk_off[i], dst + 1024 * i);
+        }
+        const void* scp = (const void*)(uintptr_t)bperm64(sc_src, sc_ad);
+        if (l < 8) dma4(scp, lds_addr(&s_rsc[j % kFp8Stages][8 * w]));
+    };
+    // Decode of the wave's 8 keys of tile j (its own copies, landed): lane
+    // l < 56 takes codes 8l .. 8l+7 of each record (the first 8 of the 16
+    // bytes it reads), lanes 56..63 the rotary dims 8(l-56) .. +8.  No branch:
+    // every lane reads and converts, and the result is selected.
+    const bool nope_lane = l < 56;
+    const int rd_off = nope_lane ? 8 * l : kNope + 16 * (l - 56);
+    auto commit_tile = [&](int j) {
+        const uint8_t* raw = &s_raw[j % kFp8Stages][w * kFp8RawWave] + rd_off;
+        u32x2 lo[8], hi[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int i = tb + group_key(w, e);
-            const int32_t slot = i < n_here ? s_slot[i] : -1;
-            const bool swa = k0 + i < rk.n_swa;
-            const uint8_t* page = (swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
-            const int rec = slot & 255;
-            const uint8_t* row = slot >= 0 ? page + rec * kFp8RecBytes : a.zero_row;
-            const uint8_t* scp = slot >= 0 ? page + kFp8ScaleOffset + 4 * rec : a.zero_row;
-            if constexpr (kDbg) {
-                if (l == 0) a.dbg_keys[dbg_unit(a, it) * a.chunk + i] = (uint64_t)(uintptr_t)row;
-            }
-            pre.v[e] = *(const u32x4*)(row + (l < 56 ? 8 * l : kNope + 16 * (l - 56)));
-            pre.sc[e] = *(const float*)scp;
+            lo[e] = *(const u32x2*)(raw + e * kFp8RecBytes);
+            hi[e] = *(const u32x2*)(raw + e * kFp8RecBytes + 8);
         }
-    };
-
-    auto commit_tile = [&]() {
+        const float sc = s_rsc[j % kFp8Stages][8 * w + (l & 7)];
         u32x4 rows[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if (l < 56) {
-                rows[e] = u32x4{e4m3x2_to_bf16x2<false>(pre.v[e][0]), e4m3x2_to_bf16x2<true>(pre.v[e][0]),
-                                e4m3x2_to_bf16x2<false>(pre.v[e][1]), e4m3x2_to_bf16x2<true>(pre.v[e][1])};
-            } else {
-                rows[e] = pre.v[e];
-            }
+            const uint32_t c0 = e4m3x2_to_bf16x2<false>(lo[e][0]), c1 = e4m3x2_to_bf16x2<true>(lo[e][0]);
+            const uint32_t c2 = e4m3x2_to_bf16x2<false>(lo[e][1]), c3 = e4m3x2_to_bf16x2<true>(lo[e][1]);
+            rows[e] = nope_lane ? u32x4{c0, c1, c2, c3} : u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) *(u32x4*)(s_krow + krow_offset(group_key(w, e), l)) = rows[e];
 #pragma unroll
         for (int i = 0; i < 8; ++i) *(u32x4*)(s_kt + kt_offset(w, 8 * l + i)) = transpose_col(rows, i);
-        if (l == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_scale[group_key(w, e)] = pre.sc[e];
-        }
+        if (l < 8) s_scale[group_key(w, l)] = sc;
     };
 
     f32x16 oacc[8];
@@ -1975,7 +2029,6 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    if (n_here > 0) issue_loads(0);
     // Q of the block's 64 heads, copied into LDS with whole-line copies (the
     // score operand's register layout, one head per lane, would make every
     // direct load touch 32 lines for 32 bytes each, and the splits of a row
@@ -1983,7 +2036,8 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     // per instruction, lane i the 16-byte chunk i ^ (h & 15) of head h, into
     // s_krow (heads 0..31) and s_kt (heads 32..63), which the first tile
     // overwrites only after Q has been read.  Chunk c of head h then sits at
-    // 16*(c ^ (h & 15)) in its 1 KiB slot.
+    // 16*(c ^ (h & 15)) in its 1 KiB slot.  The first three tiles' copies go
+    // out right after Q's.
     auto q_slot = [&](int h) -> uint8_t* { return h < 32 ? s_krow + h * 1024 : s_kt + (h - 32) * 1024; };
     {
         const int head0 = it.hb * kWideHeadsPerBlock;
@@ -1994,11 +2048,13 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             dma16_off<0>(src, lds_addr(q_slot(h)));
         }
     }
-    // Tile 0 and Q are both needed before the first product; the explicit
-    // wait also tells the compiler that tile 0's loads are in, so that it
-    // does not wait for them (and for the next tile's loads issued after
-    // them) inside the loop.
-    wait_vmcnt<0>();
+    const int n_first = min(n_tiles, kFp8Stages - 1);
+    for (int j = 0; j < n_first; ++j) issue_tile(j);
+    // Q and tile 0 landed (this wave's copies; the barrier makes them
+    // everyone's).
+    if (n_first == 3) wait_vmcnt<2 * kFp8CopiesPerTile>();
+    else if (n_first == 2) wait_vmcnt<kFp8CopiesPerTile>();
+    else wait_vmcnt<0>();
     __syncthreads();  // Q in LDS
     bf16x8 qf[16];
     {
@@ -2011,9 +2067,20 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
         }
     }
     __syncthreads();  // every wave has read Q: the first tile may overwrite it
-    for (int tb = 0; tb < n_here; tb += kTileKeys) {
-        commit_tile();
-        if (tb + kTileKeys < n_here) issue_loads(tb + kTileKeys);
+    for (int j = 0; j < n_tiles; ++j) {
+        const int tb = j * kTileKeys;
+        if (j > 0) {
+            // This wave's copies of tile j (those of j+1 and j+2 may still be
+            // in flight).  The empty asm keeps the compiler from moving the
+            // ring reads above the wait.
+            if (j + 2 < n_tiles) wait_vmcnt<2 * kFp8CopiesPerTile>();
+            else if (j + 1 < n_tiles) wait_vmcnt<kFp8CopiesPerTile>();
+            else wait_vmcnt<0>();
+            asm volatile("" ::: "memory");
+        }
+        commit_tile(j);
+        // Stage (j+3) % 4 held tile j-1, which this wave decoded last iteration.
+        if (j + kFp8Stages - 1 < n_tiles) issue_tile(j + kFp8Stages - 1);
         const int kv = tb + (l & 31);
         const bool valid = l < 32 && kv < n_here && s_slot[kv] >= 0;
         const uint64_t vmask = __ballot(valid);

@@ -20,4 +20,5 @@ from .workloads import (  # noqa: F401
     make_config,
     quantize_fp8_rows,
     store_float_rows,
+    tile_requests,
 )

@@ -348,6 +348,55 @@ def make_case(
     )
 
 
+def tile_requests(case: Case, copies: int) -> Case:
+    """A batch of ``copies`` x B requests made from a C4 case built with
+    ``index_sets`` a multiple of ``copies`` (batch sweeps at full context
+    length without backing every request's pool separately).
+
+    Copy k of request r (request k*B + r) keeps r's sequence length, page
+    tables, pools and Q rows and reads through the C4 lists of index set k;
+    ``meta["c4_sets"]`` of the result holds group j of the original sets
+    (sets j*copies .. j*copies + copies - 1, one per copy) as its set j.
+    Every entry any original set names is backed, so every copy reads
+    backed rows; copies of one request share physical pages, and their lists
+    are independent draws."""
+    if copies < 1:
+        raise ValueError("copies >= 1")
+    if copies == 1:
+        return case
+    sets = case.meta.get("c4_sets")
+    if case.R != 4 or sets is None or sets.shape[0] < copies or sets.shape[0] % copies:
+        raise ValueError("need a C4 case whose index_sets is a multiple of copies")
+    T0 = case.T
+    groups = sets.reshape(sets.shape[0] // copies, copies * T0, sets.shape[2])
+    n_q = np.diff(case.qo_indptr.astype(np.int64))
+    qo = np.zeros(copies * case.B + 1, dtype=np.int64)
+    qo[1:] = np.cumsum(np.tile(n_q, copies))
+    row_req = np.concatenate([case.meta["row_req"] + k * case.B for k in range(copies)])
+    return Case(
+        name=case.name,
+        H=case.H,
+        W=case.W,
+        R=case.R,
+        kv=case.kv,
+        scale=case.scale,
+        seq_lens=np.tile(case.seq_lens, copies),
+        qo_indptr=qo.astype(np.int32),
+        q=np.concatenate([case.q] * copies),
+        sink=case.sink,
+        swa_pool=case.swa_pool,
+        swa_page_table=np.tile(case.swa_page_table, (copies, 1)),
+        extra_pool=case.extra_pool,
+        extra_page_table=np.tile(case.extra_page_table, (copies, 1)),
+        c4_indices=np.ascontiguousarray(groups[0]),
+        poison_swa_page=case.poison_swa_page,
+        poison_extra_page=case.poison_extra_page,
+        logical=None,
+        meta={"row_req": row_req, "row_pos": np.tile(case.meta["row_pos"], copies), "seed": case.meta["seed"],
+              "c4_sets": np.ascontiguousarray(groups), "copies": copies},
+    )
+
+
 # --------------------------------------------------------------------------
 # The five workload shapes (decode and MTP target-verify)
 # --------------------------------------------------------------------------

@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import oracle as oracle_mod
-from synth import make_case, make_config
+from synth import make_case, make_config, tile_requests
 from tests import gpu_util as G
 
 pytestmark = [pytest.mark.gpu,
@@ -197,6 +197,18 @@ def test_forward_workloads_all_rows(orc, n):
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
     e = G.compare(out, lse, ro, rl, what=case.name)
+    log(f"  max abs err {e[0]:.3g}  lse err {e[1]:.3g}  rel L2 {e[2]:.3g}")
+
+
+def test_forward_fp8_1m_tiled_batch_all_rows(orc):
+    """The FP8 1M-token decode at a larger batch, built as the benchmark's
+    batch sweep builds it (copies of two requests, each copy through its own
+    C4 lists): 32 rows, every row against the oracle."""
+    case = tile_requests(make_config(5, batch=2, index_sets=16), 16)
+    log(f"forward {case.name} tiled to {case.B} requests")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    e = G.compare(out, lse, ro, rl, what="fp8-1m-tiled")
     log(f"  max abs err {e[0]:.3g}  lse err {e[1]:.3g}  rel L2 {e[2]:.3g}")
 
 
