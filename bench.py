@@ -436,6 +436,46 @@ def bench_topk(args) -> int:
     return 0
 
 
+def bench_stream(args) -> int:
+    """Achievable HBM bandwidth on this device, for context beside the 8 TB/s
+    peak the roofline fractions use: torch's own kernels reading (a sum over
+    a 1 GiB bf16 tensor), writing (a fill) and copying (read + write), each
+    far larger than the 256 MB MALL, timed with events over repeated calls."""
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    n = 1 << 29  # bf16 elements: 1 GiB
+    x = torch.randn(n, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(fn, nbytes, reps=args.steps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+    read = timed(lambda: torch.sum(x, dim=0, dtype=torch.float32, out=acc), 2 * n)
+    write = timed(lambda: y.fill_(1.0), 2 * n)
+    copy = timed(lambda: y.copy_(x), 4 * n)
+    print(json.dumps({
+        "metric": "achievable HBM bandwidth (torch kernels, 1 GiB operands)",
+        "unit": "GB/s", "read_gbs": read, "write_gbs": write, "copy_gbs": copy,
+        "read_frac": read / HBM_PEAK_GBS, "write_frac": write / HBM_PEAK_GBS, "copy_frac": copy / HBM_PEAK_GBS,
+        "peak": HBM_PEAK_GBS, "reps": args.steps,
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,6 +499,8 @@ def main() -> int:
                     help="time the FP8 KV store kernel on ROWS rows instead of the attention")
     ap.add_argument("--topk", type=int, default=0, metavar="ROWS",
                     help="time the C4 top-512 kernel on ROWS rows of 2^18 candidates instead of the attention")
+    ap.add_argument("--stream", action="store_true",
+                    help="measure achievable HBM read / write / copy bandwidth with torch kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -477,6 +519,8 @@ def main() -> int:
               "request, so N GPUs run N independent copies of this benchmark)", file=sys.stderr)
         return 2
 
+    if args.stream:
+        return bench_stream(args)
     if args.pack:
         return bench_pack(args)
     if args.topk:

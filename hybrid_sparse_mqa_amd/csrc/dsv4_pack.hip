@@ -25,27 +25,14 @@ typedef uint32_t pk_u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRecBytes = 576;
 constexpr int kScaleOffset = 256 * kRecBytes;
 
-// Whether a quotient q computed as x * rcp(scale) (within 2 ulp of the
-// correctly rounded x / scale) could round to a different E4M3 code than the
-// exact quotient: only if it lies within a few ulp of a rounding boundary,
-// i.e. of a midpoint between neighbouring codes.  Below 2^-6 the codes are
-// the multiples of 2^-9 (midpoints at odd multiples of 2^-10); above, a
-// midpoint has exactly the top bit set in the 20 mantissa bits that rounding
-// to 3 bits drops (464, the saturation threshold, is one of them).
-__device__ __forceinline__ bool near_midpoint(float q) {
-    const float a = __builtin_fabsf(q);
-    if (a < 0.015625f) {
-        const float t = a * 512.0f;  // exact
-        return __builtin_fabsf(t - __builtin_floorf(t) - 0.5f) < 1e-5f;
-    }
-    return ((__builtin_bit_cast(uint32_t, a) & 0xFFFFFu) - 0x7FFF8u) <= 16u;  // within 8 of 0x80000
-}
-
 // Four floats -> four OCP E4M3FN codes (bytes 0..3 in order) with gfx950's
-// conversion instruction (round to nearest even), after clamping to +-448 so
-// that larger magnitudes saturate (clamping keeps the sign of zeros).
+// conversion instruction (round to nearest even).  kClamp: clamp to +-448
+// first, so that larger magnitudes saturate (clamping keeps the sign of
+// zeros); callers whose values cannot exceed 448 by more than a rounding
+// error skip it (such values still round to 448).
+template <bool kClamp>
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    auto clamp = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f); };
+    auto clamp = [](float x) { return kClamp ? __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f) : x; };
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(a), clamp(b), 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(c), clamp(d), w, true);
     return (uint32_t)w;
@@ -54,13 +41,18 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// This lane's share of a row's largest non-rotary magnitude (lane l holds
-// dims 8l .. 8l+7 in v: lanes 0..55 the non-rotary part, 56..63 the rotary).
-__device__ __forceinline__ float lane_amax(const pk_u32x4& v, int l) {
-    float amax = 0.f;
+// This lane's share of a row's largest non-rotary magnitude, as bf16 bits
+// (lane l holds dims 8l .. 8l+7 in v: lanes 0..55 the non-rotary part,
+// 56..63 the rotary).  Finite bf16 magnitudes order like their bit patterns
+// with the sign cleared, so the maximum is taken on those, two per packed
+// 16-bit integer max.
+typedef uint16_t pk_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t lane_amax_bits(const pk_u32x4& v, int l) {
+    pk_u16x2 m = __builtin_bit_cast(pk_u16x2, v[0] & 0x7FFF7FFFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(__builtin_fabsf(bf16_lo(v[j])), __builtin_fabsf(bf16_hi(v[j]))));
-    return l < 56 ? amax : 0.f;
+    for (int j = 1; j < 4; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(pk_u16x2, v[j] & 0x7FFF7FFFu));
+    const uint32_t r = max((uint32_t)m[0], (uint32_t)m[1]);
+    return l < 56 ? r : 0u;
 }
 
 // One row, given its largest non-rotary magnitude.
@@ -75,22 +67,31 @@ __device__ __forceinline__ void pack_row(const PackArgs& p, const pk_u32x4& v, i
     uint8_t* page = p.pool + (int64_t)(slot >> 8) * p.page_bytes;
     uint8_t* rec = page + (slot & 255) * kRecBytes;
     if (l < 56) {
-        // The quotients by a reciprocal multiply; where one of the wave's
-        // could round differently from the correctly rounded quotient (or the
-        // scale is subnormal, where the reciprocal overflows), by division.
+        // The codes of the correctly rounded quotients f / scale, without a
+        // division: q = f * rcp(scale) lies within 2 ulp of the correctly
+        // rounded quotient (rcp is within 1 ulp), so that quotient lies
+        // between q (1 - 2^-21) and q (1 + 2^-21), computed here as f * ra
+        // and f * rb (each within 1 more ulp).  Rounding to E4M3 is
+        // monotone, so where both bounds give the same code, so does the
+        // quotient.  Where one of the wave's pairs differs (the quotient is
+        // within a few ulp of a rounding midpoint), or the scale is
+        // subnormal (its reciprocal overflows), the quotients are divided.
+        // |f| <= amax = 448 scale, so no quotient exceeds 448 by more than a
+        // rounding error and none needs the saturating clamp.
         const float r = __builtin_amdgcn_rcpf(scale);
-        float q[8];
-        bool risky = false;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            q[j] = f[j] * r;
-            risky |= near_midpoint(q[j]);
-        }
-        if (__builtin_expect(__any(risky) || !(scale >= 1.17549435e-38f), 0)) {
+        const float ra = r * (1.0f - 0x1p-21f), rb = r * (1.0f + 0x1p-21f);
+        uint32_t c0 = e4m3x4<false>(f[0] * ra, f[1] * ra, f[2] * ra, f[3] * ra);
+        uint32_t c1 = e4m3x4<false>(f[4] * ra, f[5] * ra, f[6] * ra, f[7] * ra);
+        const uint32_t d0 = e4m3x4<false>(f[0] * rb, f[1] * rb, f[2] * rb, f[3] * rb);
+        const uint32_t d1 = e4m3x4<false>(f[4] * rb, f[5] * rb, f[6] * rb, f[7] * rb);
+        if (__builtin_expect(__any((c0 != d0) | (c1 != d1)) || !(scale >= 1.17549435e-38f), 0)) {
+            float q[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) q[j] = f[j] / scale;
+            c0 = e4m3x4<true>(q[0], q[1], q[2], q[3]);
+            c1 = e4m3x4<true>(q[4], q[5], q[6], q[7]);
         }
-        *(pk_u32x2*)(rec + 8 * l) = pk_u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
+        *(pk_u32x2*)(rec + 8 * l) = pk_u32x2{c0, c1};
     } else {
         *(pk_u32x4*)(rec + 448 + 16 * (l - 56)) = v;
     }
@@ -114,17 +115,17 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(PackArgs p) {
         v[r] = *(const pk_u32x4*)(p.k + row * p.k_s0 + 8 * l);
         slot[r] = row0 + r < p.n ? p.slots[row] : -1;
     }
-    // The rows' maxima over the wave, their shuffles interleaved.
-    float amax[kRowsPerWave];
+    // The rows' maxima over the wave (as bf16 bits), their shuffles interleaved.
+    uint32_t amax[kRowsPerWave];
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) amax[r] = lane_amax(v[r], l);
+    for (int r = 0; r < kRowsPerWave; ++r) amax[r] = lane_amax_bits(v[r], l);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
 #pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r) amax[r] = fmaxf(amax[r], __shfl_xor(amax[r], o));
+        for (int r = 0; r < kRowsPerWave; ++r) amax[r] = max(amax[r], (uint32_t)__shfl_xor((int)amax[r], o));
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
-        if (slot[r] >= 0) pack_row(p, v[r], slot[r], amax[r], l);
+        if (slot[r] >= 0) pack_row(p, v[r], slot[r], __builtin_bit_cast(float, amax[r] << 16), l);
 }
 
 }  // namespace
