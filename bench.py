@@ -14,9 +14,11 @@ Prints ONE JSON line: tokens (query rows) per second of the whole job over a
 timed HIP-graph replay of exactly --steps calls; a roofline object for the
 dominant kernel (the split kernel: the bytes it must read -- Q, C4 index
 lists and every unique KV row -- over its average duration from HIP events
-recorded on its stream inside the timed replay, every tenth call); the whole
-path's achieved GB/s per step; and the fp64 oracle timed on the host cores on
-a bounded sample of the same workload, with all threads and with one.
+recorded on its stream inside the timed replay, around every tenth call;
+each such interval also holds the event nodes' own cost, about a microsecond,
+so the fraction errs low); the whole path's achieved GB/s per step; and the
+fp64 oracle timed on the host cores on a bounded sample of the same
+workload, with all threads and with one.
 """
 from __future__ import annotations
 
@@ -45,8 +47,12 @@ KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_mqa_amd", "csrc", f)
 
 
 # Split-kernel variant (DSV4_KERNEL_* of dsv4_attn_plan) -> (name as rocprofv3 prints it, heads per workgroup).
-SPLIT_KERNELS = {1: ("attn_narrow_kernel", 16), 2: ("attn_wide_kernel<1>", 32), 3: ("attn_ws_kernel<1>", 32),
-                 4: ("attn_wide_kernel<2>", 64), 5: ("attn_fp8_kernel", 64)}
+# (name as rocprofv3 prints it, without the namespace: the second template
+# argument is the key-recording switch, off in every timed call; heads per
+# workgroup)
+SPLIT_KERNELS = {1: ("attn_narrow_kernel<false>", 16), 2: ("attn_wide_kernel<1, false>", 32),
+                 3: ("attn_ws_kernel<1, false>", 32), 4: ("attn_wide_kernel<2, false>", 64),
+                 5: ("attn_fp8_kernel<false>", 64)}
 
 
 def split_kernel_name(kernel: int) -> str:
@@ -629,19 +635,20 @@ def main() -> int:
     e_split, e_merge, e_calls = dsv4_attn_timing_read()
 
     # Timed region: one replay of a HIP graph holding exactly `steps` calls
-    # (rotating over the input sets).  Every `sample_every`-th call is captured
-    # with the library's timing on, which adds event-record nodes before its
-    # split kernel, between split and merge kernel and after the merge kernel,
-    # on the stream the kernels run on; the replay itself is bracketed by two
-    # more events.  (Instrumenting every call would add the event nodes' own
-    # cost to every step.)
+    # (rotating over the input sets), bracketed by two events.  Every N-th
+    # call (--sample-every) is captured with the library's timing on, which
+    # adds event-record nodes before its split kernel, between split and
+    # merge kernel and after the merge kernel, on the stream the kernels run
+    # on.  (Instrumenting every call would add the nodes' own cost to every
+    # step.)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
+    every = args.sample_every
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream):
             for i in range(args.steps):
-                sampled = i % args.sample_every == args.sample_every // 2
+                sampled = every > 0 and i % every == every // 2
                 if sampled:
                     dsv4_attn_timing_enable(True)
                 step(i)
@@ -659,19 +666,17 @@ def main() -> int:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     event_ms = ev0.elapsed_time(ev1)
-    split_ms, merge_ms, calls = dsv4_attn_timing_read()  # the timed replay's sampled calls
-    expected = sum(1 for i in range(args.steps) if i % args.sample_every == args.sample_every // 2)
-    if calls != expected or calls == 0:
-        print(f"[bench] expected {expected} sampled calls, the library recorded {calls}", file=sys.stderr)
+    g_split_ms, g_merge_ms, g_calls = dsv4_attn_timing_read()  # the timed replay's sampled calls
+    expected = sum(1 for i in range(args.steps) if every > 0 and i % every == every // 2)
+    if g_calls != expected or g_calls == 0 or e_calls != n_eager:
+        print(f"[bench] expected {n_eager} eager and {expected} sampled calls, the library recorded {e_calls} "
+              f"and {g_calls}", file=sys.stderr)
         return 1
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = case.T / (ms_per_step / 1e3)
-    # Each interval holds its kernel plus the event pair's own cost, so the
-    # split kernel's rate below is a lower bound (rocprofv3's kernel-trace
-    # average of the same command is a few percent shorter).
-    split_avg_ms = split_ms / calls
-    merge_avg_ms = merge_ms / calls
+    split_avg_ms = g_split_ms / g_calls
+    merge_avg_ms = g_merge_ms / g_calls
     kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
     achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
     tflops = ab["flops"] / (split_avg_ms * 1e-3) / 1e12
@@ -709,13 +714,15 @@ def main() -> int:
             "algorithmic_bytes_per_call": ab["total"],
             "achieved_gbs_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9,
             "frac_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "split_kernel_event_ms": split_avg_ms,
-            "merge_kernel_event_ms": merge_avg_ms,
+            "split_kernel_ms": split_avg_ms,
+            "merge_kernel_ms": merge_avg_ms,
+            "kernel_timing": f"event nodes around {g_calls} of the timed replay's calls (each interval "
+                             "also holds the nodes' own cost)",
+            "kernels_per_step_frac": (split_avg_ms + merge_avg_ms) / ms_per_step,
             "graph_event_ms_per_step": event_ms / args.steps,
-            "timed_calls_sampled": calls,
             "eager_ms_per_call": eager_ms,
-            "eager_split_kernel_event_ms": e_split / max(e_calls, 1),
-            "eager_merge_kernel_event_ms": e_merge / max(e_calls, 1),
+            "eager_split_kernel_ms": e_split / max(e_calls, 1),
+            "eager_merge_kernel_ms": e_merge / max(e_calls, 1),
         },
         "roofline": ({
             "bound": "mfma",
