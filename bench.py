@@ -14,11 +14,12 @@ Prints ONE JSON line: tokens (query rows) per second of the whole job over a
 timed HIP-graph replay of exactly --steps calls; a roofline object for the
 dominant kernel (the split kernel: the bytes it must read -- Q, C4 index
 lists and every unique KV row -- over its average duration from HIP events
-recorded on its stream inside the timed replay, around every tenth call;
-each such interval also holds the event nodes' own cost, about a microsecond,
-so the fraction errs low); the whole path's achieved GB/s per step; and the
-fp64 oracle timed on the host cores on a bounded sample of the same
-workload, with all threads and with one.
+recorded on its stream around each kernel of a timed run of eager calls on
+the same rotating inputs; these intervals agree with rocprofv3's kernel trace
+to about 1 %, where event nodes inside a graph replay add about a microsecond
+to each interval); the whole path's achieved GB/s per step; and the fp64
+oracle timed on the host cores on a bounded sample of the same workload, with
+all threads and with one.
 """
 from __future__ import annotations
 
@@ -621,7 +622,9 @@ def main() -> int:
           f"sets={n_sets} ({'cold' if cold else 'warm'}) algorithmic {ab['total'] / 1e6:.2f} MB/call",
           file=sys.stderr, flush=True)
 
-    # Eager calls, for context: host-driven loop time and per-call kernel time.
+    # Kernel durations: a timed run of eager calls on the same rotating inputs,
+    # each kernel bracketed by HIP events on the stream it runs on (the
+    # library's timing hook).  Also the host-driven loop time, for context.
     n_eager = min(args.steps, 100)
     dsv4_attn_timing_read()  # clear
     dsv4_attn_timing_enable(True)
@@ -638,9 +641,8 @@ def main() -> int:
     # (rotating over the input sets), bracketed by two events.  Every N-th
     # call (--sample-every) is captured with the library's timing on, which
     # adds event-record nodes before its split kernel, between split and
-    # merge kernel and after the merge kernel, on the stream the kernels run
-    # on.  (Instrumenting every call would add the nodes' own cost to every
-    # step.)
+    # merge kernel and after the merge kernel (for context: inside the graph
+    # each interval also holds the nodes' own cost).
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -668,15 +670,15 @@ def main() -> int:
     event_ms = ev0.elapsed_time(ev1)
     g_split_ms, g_merge_ms, g_calls = dsv4_attn_timing_read()  # the timed replay's sampled calls
     expected = sum(1 for i in range(args.steps) if every > 0 and i % every == every // 2)
-    if g_calls != expected or g_calls == 0 or e_calls != n_eager:
+    if g_calls != expected or e_calls != n_eager or n_eager == 0:
         print(f"[bench] expected {n_eager} eager and {expected} sampled calls, the library recorded {e_calls} "
               f"and {g_calls}", file=sys.stderr)
         return 1
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = case.T / (ms_per_step / 1e3)
-    split_avg_ms = g_split_ms / g_calls
-    merge_avg_ms = g_merge_ms / g_calls
+    split_avg_ms = e_split / n_eager
+    merge_avg_ms = e_merge / n_eager
     kernel_bytes = ab["q"] + ab["idx"] + ab["kv"] + (ab["out"] + ab["lse"] if splits == 1 else 0)
     achieved = kernel_bytes / (split_avg_ms * 1e-3) / 1e9
     tflops = ab["flops"] / (split_avg_ms * 1e-3) / 1e12
@@ -716,13 +718,13 @@ def main() -> int:
             "frac_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "split_kernel_ms": split_avg_ms,
             "merge_kernel_ms": merge_avg_ms,
-            "kernel_timing": f"event nodes around {g_calls} of the timed replay's calls (each interval "
-                             "also holds the nodes' own cost)",
+            "kernel_timing": f"HIP events around each kernel of {n_eager} timed eager calls",
             "kernels_per_step_frac": (split_avg_ms + merge_avg_ms) / ms_per_step,
             "graph_event_ms_per_step": event_ms / args.steps,
+            "graph_sampled_calls": g_calls,
+            "graph_sampled_split_interval_ms": g_split_ms / g_calls if g_calls else None,
+            "graph_sampled_merge_interval_ms": g_merge_ms / g_calls if g_calls else None,
             "eager_ms_per_call": eager_ms,
-            "eager_split_kernel_ms": e_split / max(e_calls, 1),
-            "eager_merge_kernel_ms": e_merge / max(e_calls, 1),
         },
         "roofline": ({
             "bound": "mfma",
