@@ -1893,20 +1893,35 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Packed FP8 KV.  The raw records stream into a 4-stage LDS ring with direct
-// global->LDS copies (three tiles in flight while one is computed); each wave
-// copies and decodes its own 8 keys of a tile (so the ring needs no barrier),
-// writing them as bf16 to LDS row-major and as 8-key columns.  E4M3 codes are
-// exact in bf16; the per-token scale multiplies the fp32 non-rotary score
-// partial and is folded into P for the non-rotary PV tiles.
+// Packed FP8 KV: 64-head workgroups, wave (hh, dh) owning heads 32hh .. +31
+// and dims 256dh .. +255 of both products.  The raw records stream into a
+// 4-stage LDS ring with direct global->LDS copies, three tiles ahead, and
+// both MFMA operands are decoded straight from the ring into registers:
+//  - S^T = K.Q^T: lane l reads 8 codes of key l & 31 (one 8-byte read per
+//    k-step) and converts them to bf16 with gfx950's conversion instruction
+//    (exact: every E4M3 value is a bf16 value); rotary k-steps read bf16;
+//  - O^T += K^T.P^T: the transposing 8-bit LDS read gives each lane one dim
+//    of 8 keys (16 lanes read 8 keys x 16 dims: source lane s of a 16-lane
+//    group addresses the key that P^T holds as element s / 2, at dims
+//    (first dim + 8 (s % 2)), and lane i receives dim (first dim + i) of the
+//    8 keys, in element order); rotary dims use the 16-bit transposing read
+//    (source lane s: element s / 4, dims (first dim + 4 (s % 4)); a second
+//    read 8 keys on gives elements 4..7).  P^T's element e of lane half h
+//    in k-step pp is tile key 16 pp + 4 h + (e % 4) + 8 (e / 4), the order
+//    of the score tile's MFMA output rows.
+// The per-token scale multiplies the fp32 non-rotary score partial and is
+// folded into P for the non-rotary PV product, so the decode adds no
+// rounding.  Two barriers per tile: one when the tile has landed, one in
+// the score exchange.
 //
-// Ring stage: wave w's 8 records of the tile (key group_key(w, e) at record
-// e) at byte w * 4608 + 576 * e, each record's 576 bytes as stored (448 codes,
-// 64 bf16 rotary dims); the 8 scales in a separate 32-byte slot per wave.
+// Ring stage: record of tile key k (its 576 bytes as stored: 448 codes, 64
+// bf16 rotary dims) at byte 592 k (a 16-byte pad after each record spreads
+// the keys of a read over the LDS banks); wave w copies keys 8w .. 8w+7 and
+// their scales (into a separate 128-byte slot per stage).
 // ---------------------------------------------------------------------------
 constexpr int kFp8Stages = 4;
-constexpr int kFp8RawWave = 8 * kFp8RecBytes;          // one wave's records of a tile
-constexpr int kFp8RawStage = 4 * kFp8RawWave;
+constexpr int kFp8RecSlot = 592;                       // LDS bytes per record (36 chunks + 1 pad chunk)
+constexpr int kFp8RawStage = kTileKeys * kFp8RecSlot;  // 18944
 constexpr int kFp8CopiesPerTile = 6;                   // per wave: 5 record copies + 1 scale copy
 
 // Direct global -> LDS copy of 4 bytes per lane: lane i's bytes land at LDS
@@ -1925,19 +1940,26 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
         : "memory");
 }
 
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// Eight E4M3 codes (two words) -> eight bf16, in order.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+    return __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                            e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
+}
+
 template <bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_krow[kTileKeys * 1024];
-    __shared__ __attribute__((aligned(16))) uint8_t s_kt[4 * 512 * 16];
-    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
-    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kFp8Stages][kFp8RawStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kFp8Stages][kFp8RawStage];
     __shared__ __attribute__((aligned(16))) float s_rsc[kFp8Stages][kTileKeys];
+    __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
     __shared__ int32_t s_slot[kMaxSplitKeys];
-    __shared__ __attribute__((aligned(16))) float s_scale[kTileKeys];
     // The page-table cache is needed only while the slot list is built, before
     // the exchange buffer's first use.
     int32_t* const s_table = (int32_t*)s_sx;
     static_assert(kTableCap * 4 <= sizeof(s_sx), "page-table cache fits the exchange buffer");
+    static_assert(2 * 32 * 1024 <= sizeof(s_raw), "the ring holds the epilogue's two 32-head staging blocks");
 
     fetch_args(a);
     Item it;
@@ -1946,6 +1968,18 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int hh = w >> 1, dh = w & 1;
 
+    // Q^T as the B operand of the scores, loaded first (lane: head 32hh +
+    // (l & 31), dims 256dh + 16j + 8(l >> 5) .. +8 of k-step j; heads past H
+    // read head H-1, whose results are never written).  The slot list's
+    // loads go out after it, and waiting for them waits for Q too.
+    bf16x8 qf[16];
+    {
+        const int head = min(it.hb * kWideHeadsPerBlock + 32 * hh + (l & 31), a.H - 1);
+        const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1 + 256 * dh + 8 * (l >> 5);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
+    }
+
     const RowKeys rk = row_keys(a.m, it.t, l);
     const int k0 = it.s * a.chunk;
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
@@ -1953,21 +1987,21 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
 
     // Copies of tile j into stage j % 4: five 16-byte copies per lane over
-    // the wave's 8 x 36 record chunks (chunk f = 64 i + l is chunk f % 36 of
-    // record f / 36; the last copy has 32 lanes), and one 4-byte copy of the
-    // scales (lanes 0..7).  Lane k < 32 resolves the record and scale
-    // addresses of tile key k; each copying lane fetches its key's addresses
-    // with a cross-lane permute.  Unused keys read the zero row (codes,
-    // rotary dims and scale all zero).
+    // the wave's 8 x 37 record slots (slot f = 64 i + l is chunk f % 37 of
+    // key 8w + f / 37, chunk 36 being the pad, filled from the zero row; the
+    // last copy has 40 lanes), and one 4-byte copy of the 8 scales (lanes
+    // 0..7).  Lane k < 32 resolves the record and scale addresses of tile key
+    // k; each copying lane fetches its key's addresses with a cross-lane
+    // permute.  Unused keys read the zero row (codes, rotary dims and scale
+    // all zero).
     int src_lane[5], chunk_off[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
         const int f = 64 * i + l;
-        const int e = min(f / 36, 7);
-        src_lane[i] = 4 * group_key(w, e);
-        chunk_off[i] = 16 * (f - 36 * (f / 36));
+        const int e = min(f / 37, 7);
+        src_lane[i] = 4 * (8 * w + e);
+        chunk_off[i] = f - 37 * (f / 37);  // 36: the pad
     }
-    const int sc_src = 4 * group_key(w, l & 7);
     auto bperm64 = [](int src4, uint64_t v) -> uint64_t {
         const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)(uint32_t)v);
         const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)(uint32_t)(v >> 32));
@@ -1986,42 +2020,15 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
         if constexpr (kDbg) {
             if (l < 32) a.dbg_keys[dbg_unit(a, it) * a.chunk + tb + l] = rec_ad;
         }
-        const uint32_t dst = lds_addr(&s_raw[j % kFp8Stages][w * kFp8RawWave]);
+        const uint32_t dst = lds_addr(&s_raw[j % kFp8Stages][8 * w * kFp8RecSlot]);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const uint8_t* row = (const uint8_t*)(uintptr_t)bperm64(src_lane[i], rec_ad);
-            if (i < 4 || l < 32) dma16_off<0>(row + chunk_off[i], dst + 1024 * i);
+            const uint8_t* src = chunk_off[i] < 36 ? row + 16 * chunk_off[i] : a.zero_row;
+            if (i < 4 || l < 8 * 37 - 256) dma16_off<0>(src, dst + 1024 * i);
         }
-        const void* scp = (const void*)(uintptr_t)bperm64(sc_src, sc_ad);
+        const void* scp = (const void*)(uintptr_t)bperm64(4 * (8 * w + (l & 7)), sc_ad);
         if (l < 8) dma4(scp, lds_addr(&s_rsc[j % kFp8Stages][8 * w]));
-    };
-    // Decode of the wave's 8 keys of tile j (its own copies, landed): lane
-    // l < 56 takes codes 8l .. 8l+7 of each record (the first 8 of the 16
-    // bytes it reads), lanes 56..63 the rotary dims 8(l-56) .. +8.  No branch:
-    // every lane reads and converts, and the result is selected.
-    const bool nope_lane = l < 56;
-    const int rd_off = nope_lane ? 8 * l : kNope + 16 * (l - 56);
-    auto commit_tile = [&](int j) {
-        const uint8_t* raw = &s_raw[j % kFp8Stages][w * kFp8RawWave] + rd_off;
-        u32x2 lo[8], hi[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lo[e] = *(const u32x2*)(raw + e * kFp8RecBytes);
-            hi[e] = *(const u32x2*)(raw + e * kFp8RecBytes + 8);
-        }
-        const float sc = s_rsc[j % kFp8Stages][8 * w + (l & 7)];
-        u32x4 rows[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t c0 = e4m3x2_to_bf16x2<false>(lo[e][0]), c1 = e4m3x2_to_bf16x2<true>(lo[e][0]);
-            const uint32_t c2 = e4m3x2_to_bf16x2<false>(lo[e][1]), c3 = e4m3x2_to_bf16x2<true>(lo[e][1]);
-            rows[e] = nope_lane ? u32x4{c0, c1, c2, c3} : u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x4*)(s_krow + krow_offset(group_key(w, e), l)) = rows[e];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(u32x4*)(s_kt + kt_offset(w, 8 * l + i)) = transpose_col(rows, i);
-        if (l < 8) s_scale[group_key(w, l)] = sc;
     };
 
     f32x16 oacc[8];
@@ -2029,113 +2036,128 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Q of the block's 64 heads, copied into LDS with whole-line copies (the
-    // score operand's register layout, one head per lane, would make every
-    // direct load touch 32 lines for 32 bytes each, and the splits of a row
-    // all load the same Q): wave w copies heads 16w .. 16w+15, one 1 KiB row
-    // per instruction, lane i the 16-byte chunk i ^ (h & 15) of head h, into
-    // s_krow (heads 0..31) and s_kt (heads 32..63), which the first tile
-    // overwrites only after Q has been read.  Chunk c of head h then sits at
-    // 16*(c ^ (h & 15)) in its 1 KiB slot.  The first three tiles' copies go
-    // out right after Q's.
-    auto q_slot = [&](int h) -> uint8_t* { return h < 32 ? s_krow + h * 1024 : s_kt + (h - 32) * 1024; };
-    {
-        const int head0 = it.hb * kWideHeadsPerBlock;
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const int h = 16 * w + n;
-            const uint16_t* src = a.q + (int64_t)it.t * a.q_s0 + (int64_t)min(head0 + h, a.H - 1) * a.q_s1 + 8 * (l ^ (h & 15));
-            dma16_off<0>(src, lds_addr(q_slot(h)));
-        }
-    }
+    // Q and the slot list have arrived (the compiler waited for the slot
+    // list, issued after Q); the explicit wait tells it so before any copy.
+    wait_vmcnt<0>();
     const int n_first = min(n_tiles, kFp8Stages - 1);
     for (int j = 0; j < n_first; ++j) issue_tile(j);
-    // Q and tile 0 landed (this wave's copies; the barrier makes them
-    // everyone's).
-    if (n_first == 3) wait_vmcnt<2 * kFp8CopiesPerTile>();
-    else if (n_first == 2) wait_vmcnt<kFp8CopiesPerTile>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // Q in LDS
-    bf16x8 qf[16];
-    {
-        const int hl = hh * 32 + (l & 31);
-        const uint8_t* qs = q_slot(hl);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int c = 32 * dh + 2 * j + (l >> 5);
-            qf[j] = *(const bf16x8*)(qs + 16 * (c ^ (l & 15)));
-        }
-    }
-    __syncthreads();  // every wave has read Q: the first tile may overwrite it
+
+    // Per-lane constants of the operand reads.
+    const int key_s = l & 31;                      // score operand: this lane's key
+    const int g = l >> 4, gi = l & 15;             // transposing reads: 16-lane group, lane in it
     for (int j = 0; j < n_tiles; ++j) {
         const int tb = j * kTileKeys;
-        if (j > 0) {
-            // This wave's copies of tile j (those of j+1 and j+2 may still be
-            // in flight).  The empty asm keeps the compiler from moving the
-            // ring reads above the wait.
-            if (j + 2 < n_tiles) wait_vmcnt<2 * kFp8CopiesPerTile>();
-            else if (j + 1 < n_tiles) wait_vmcnt<kFp8CopiesPerTile>();
-            else wait_vmcnt<0>();
-            asm volatile("" ::: "memory");
-        }
-        commit_tile(j);
-        // Stage (j+3) % 4 held tile j-1, which this wave decoded last iteration.
+        // This wave's copies of tile j (those of j+1 and j+2 may still be in
+        // flight); then every wave's.
+        if (j + 2 < n_tiles) wait_vmcnt<2 * kFp8CopiesPerTile>();
+        else if (j + 1 < n_tiles) wait_vmcnt<kFp8CopiesPerTile>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // tile j in LDS for every wave; every wave is done with tile j-1's stage
+        // Stage (j+3) % 4 held tile j-1.
         if (j + kFp8Stages - 1 < n_tiles) issue_tile(j + kFp8Stages - 1);
+        const uint8_t* stage = &s_raw[j % kFp8Stages][0];
         const int kv = tb + (l & 31);
         const bool valid = l < 32 && kv < n_here && s_slot[kv] >= 0;
         const uint64_t vmask = __ballot(valid);
-        __syncthreads();
 
-        // S^T partial over this wave's 256 dims; non-rotary k-steps (dims < 448)
-        // and the rotary k-steps of the dh = 1 wave (j >= 12) accumulate apart.
+        // S^T partial over this wave's 256 dims: the non-rotary k-steps
+        // (dims < 448) and the rotary ones (dh = 1, k-steps 12..15)
+        // accumulate apart; the non-rotary partial is scaled per key.  The
+        // two dim halves are separate instances (kD), so that every operand
+        // is a fixed register.
         f32x16 sacc = f32x16{};
         float sc_key[16];
-        {
-            const int k = l & 31;
-            f32x16 sacc_r = f32x16{};
-            bf16x8 av[16];
+        auto scores = [&](auto d_tag) __attribute__((always_inline)) {
+            constexpr int kD = decltype(d_tag)::value;
+            constexpr int kNopeSteps = kD == 0 ? 16 : 12;
+            const uint8_t* rec = stage + key_s * kFp8RecSlot + 256 * kD + 8 * (l >> 5);
+            u32x2 cn[kNopeSteps];
+            u32x4 cr[16 - kNopeSteps + 1];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) av[j] = *(const bf16x8*)(s_krow + krow_offset(k, dh * 32 + 2 * j + (l >> 5)));
+            for (int jj = 0; jj < kNopeSteps; ++jj) cn[jj] = *(const u32x2*)(rec + 16 * jj);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                if (dh == 1 && j >= 12)
-                    sacc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc_r, 0, 0, 0);
-                else
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], qf[j], sacc, 0, 0, 0);
+            for (int q = 0; q < 16 - kNopeSteps; ++q) {  // bf16 dims 448 + 16q + 8(l >> 5) .. +8
+                cr[q] = *(const u32x4*)(stage + key_s * kFp8RecSlot + kNope + 32 * q + 16 * (l >> 5));
             }
+            // Every read in flight before the first product (left alone, the
+            // scheduler issues one read ahead of its use, and with one wave
+            // per SIMD nothing hides the LDS latency of each).
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 sacc_r = f32x16{};
+#pragma unroll
+            for (int jj = 0; jj < kNopeSteps; ++jj)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16x8(cn[jj][0], cn[jj][1]), qf[jj], sacc, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 16 - kNopeSteps; ++q)
+                sacc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cr[q]), qf[kNopeSteps + q], sacc_r, 0, 0, 0);
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const f32x4 sc4 = *(const f32x4*)(s_scale + 8 * qd + 4 * (l >> 5));
+                const f32x4 sc4 = *(const f32x4*)(&s_rsc[j % kFp8Stages][8 * qd + 4 * (l >> 5)]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sc_key[4 * qd + j] = sc4[j];
-                    sacc[4 * qd + j] = sacc[4 * qd + j] * sc4[j] + sacc_r[4 * qd + j];
+                for (int jj = 0; jj < 4; ++jj) {
+                    sc_key[4 * qd + jj] = sc4[jj];
+                    sacc[4 * qd + jj] = sacc[4 * qd + jj] * sc4[jj] + sacc_r[4 * qd + jj];
                 }
             }
-        }
+        };
+        if (dh == 0) scores(std::integral_constant<int, 0>{});
+        else scores(std::integral_constant<int, 1>{});
         exchange_partial(s_sx, w, l, sacc);
 
         bf16x8 pb[2], pbs[2];
         softmax_tile<true>(sacc, vmask, a.scale_log2, l, sc_key, m_run, l_run, oacc, pb, pbs);
 
-        {
-            bf16x8 kt[16];
+        // O^T += K^T . P^T: lane l holds dim 256dh + 32mb + (l & 31) of the
+        // eight keys 16pp + 4h + {0..3, 8..11}, h = l >> 5, in the order in
+        // which P^T holds them (the score tile's MFMA output layout, see
+        // group_key); the transposing reads' source lanes address those keys.
+        // All operand reads go out before the products.
+        auto pv = [&](auto d_tag) __attribute__((always_inline)) {
+            constexpr int kD = decltype(d_tag)::value;
+            constexpr int kNopeMb = kD == 0 ? 8 : 6;  // dim blocks below 448
+            i32x2 c8[2 * kNopeMb];
+            bf16x4 c16[2 * (8 - kNopeMb) + 1][2];  // (+1: no zero-length array for kD = 0)
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
+            for (int mb = 0; mb < kNopeMb; ++mb)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
+                    const int js = gi >> 1;  // the key this source lane addresses: element js of the operand
+                    const int key = 16 * pp + 4 * (g >> 1) + (js & 3) + 8 * (js >> 2);
+                    const uint8_t* p0 = stage + key * kFp8RecSlot + dim_base + 8 * (gi & 1);
+                    c8[2 * mb + pp] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)lds_addr(p0));
+                }
+#pragma unroll
+            for (int mb = kNopeMb; mb < 8; ++mb)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
+                    const int key = 16 * pp + 4 * (g >> 1) + (gi >> 2);  // elements 0..3; 4..7 are 8 keys on
+                    const uint8_t* p0 = stage + key * kFp8RecSlot + kNope + 2 * (dim_base - kNope + 4 * (gi & 3));
+                    c16[2 * (mb - kNopeMb) + pp][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0));
+                    c16[2 * (mb - kNopeMb) + pp][1] =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0 + 8 * kFp8RecSlot));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < kNopeMb; ++mb)
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp)
-                    kt[2 * mb + pp] = *(const bf16x8*)(s_kt + kt_offset(2 * pp + (l >> 5), dh * 256 + 32 * mb + (l & 31)));
+                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        e4m3x8_to_bf16x8((uint32_t)c8[2 * mb + pp][0], (uint32_t)c8[2 * mb + pp][1]), pbs[pp], oacc[mb], 0, 0, 0);
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                const bool nope = dh == 0 || mb < 6;  // dims < 448
+            for (int mb = kNopeMb; mb < 8; ++mb)
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp)
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * mb + pp], nope ? pbs[pp] : pb[pp], oacc[mb], 0, 0, 0);
-            }
-        }
-        __syncthreads();
+                for (int pp = 0; pp < 2; ++pp) {
+                    const bf16x4 lo = c16[2 * (mb - kNopeMb) + pp][0], hi = c16[2 * (mb - kNopeMb) + pp][1];
+                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
+                                                                      pb[pp], oacc[mb], 0, 0, 0);
+                }
+        };
+        if (dh == 0) pv(std::integral_constant<int, 0>{});
+        else pv(std::integral_constant<int, 1>{});
     }
-    write_result<2>(a, it, hh, dh, l, oacc, m_run, l_run, s_krow, s_kt);
+    write_result<2>(a, it, hh, dh, l, oacc, m_run, l_run, &s_raw[0][0], &s_raw[0][0] + 32 * 1024);
 }
 
 // ---------------------------------------------------------------------------
