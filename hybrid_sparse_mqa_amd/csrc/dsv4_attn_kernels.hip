@@ -2007,12 +2007,15 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
         const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)(uint32_t)(v >> 32));
         return ((uint64_t)hi << 32) | lo;
     };
-    auto issue_tile = [&](int j) {
+    // Returns the tile's mask of used keys (bit k: tile key k).
+    auto issue_tile = [&](int j) -> uint64_t {
         const int tb = j * kTileKeys;
         uint64_t rec_ad, sc_ad;
+        bool used;
         {
             const int key = tb + (l & 31);
             const int32_t slot = key < n_here ? s_slot[key] : -1;
+            used = l < 32 && slot >= 0;
             const uint8_t* page = (k0 + key < rk.n_swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
             rec_ad = (uint64_t)(uintptr_t)(slot >= 0 ? page + (slot & 255) * kFp8RecBytes : a.zero_row);
             sc_ad = (uint64_t)(uintptr_t)(slot >= 0 ? page + kFp8ScaleOffset + 4 * (slot & 255) : a.zero_row);
@@ -2021,14 +2024,19 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             if (l < 32) a.dbg_keys[dbg_unit(a, it) * a.chunk + tb + l] = rec_ad;
         }
         const uint32_t dst = lds_addr(&s_raw[j % kFp8Stages][8 * w * kFp8RecSlot]);
+        // Every permute before the first copy (the copies are ordered asm, so
+        // alternating the two would wait out each permute on its own).
+        uint64_t row[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) row[i] = bperm64(src_lane[i], rec_ad);
+        const uint64_t scp = bperm64(4 * (8 * w + (l & 7)), sc_ad);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
-            const uint8_t* row = (const uint8_t*)(uintptr_t)bperm64(src_lane[i], rec_ad);
-            const uint8_t* src = chunk_off[i] < 36 ? row + 16 * chunk_off[i] : a.zero_row;
+            const uint8_t* src = chunk_off[i] < 36 ? (const uint8_t*)(uintptr_t)row[i] + 16 * chunk_off[i] : a.zero_row;
             if (i < 4 || l < 8 * 37 - 256) dma16_off<0>(src, dst + 1024 * i);
         }
-        const void* scp = (const void*)(uintptr_t)bperm64(4 * (8 * w + (l & 7)), sc_ad);
-        if (l < 8) dma4(scp, lds_addr(&s_rsc[j % kFp8Stages][8 * w]));
+        if (l < 8) dma4((const void*)(uintptr_t)scp, lds_addr(&s_rsc[j % kFp8Stages][8 * w]));
+        return __ballot(used);
     };
 
     f32x16 oacc[8];
@@ -2039,124 +2047,130 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     // Q and the slot list have arrived (the compiler waited for the slot
     // list, issued after Q); the explicit wait tells it so before any copy.
     wait_vmcnt<0>();
-    const int n_first = min(n_tiles, kFp8Stages - 1);
-    for (int j = 0; j < n_first; ++j) issue_tile(j);
+    // Used-key masks of the tiles in flight (tiles j, j+1, j+2).
+    uint64_t vm0 = n_tiles > 0 ? issue_tile(0) : 0;
+    uint64_t vm1 = n_tiles > 1 ? issue_tile(1) : 0;
+    uint64_t vm2 = n_tiles > 2 ? issue_tile(2) : 0;
+    static_assert(kFp8Stages == 4, "three tiles in flight");
 
     // Per-lane constants of the operand reads.
     const int key_s = l & 31;                      // score operand: this lane's key
     const int g = l >> 4, gi = l & 15;             // transposing reads: 16-lane group, lane in it
-    for (int j = 0; j < n_tiles; ++j) {
-        const int tb = j * kTileKeys;
-        // This wave's copies of tile j (those of j+1 and j+2 may still be in
-        // flight); then every wave's.
-        if (j + 2 < n_tiles) wait_vmcnt<2 * kFp8CopiesPerTile>();
-        else if (j + 1 < n_tiles) wait_vmcnt<kFp8CopiesPerTile>();
-        else wait_vmcnt<0>();
-        __syncthreads();  // tile j in LDS for every wave; every wave is done with tile j-1's stage
-        // Stage (j+3) % 4 held tile j-1.
-        if (j + kFp8Stages - 1 < n_tiles) issue_tile(j + kFp8Stages - 1);
-        const uint8_t* stage = &s_raw[j % kFp8Stages][0];
-        const int kv = tb + (l & 31);
-        const bool valid = l < 32 && kv < n_here && s_slot[kv] >= 0;
-        const uint64_t vmask = __ballot(valid);
+    // One instance of the loop per dim half (kD = dh): a branch on dh inside
+    // the loop made the compiler copy all 128 accumulators on every tile.
+    auto tile_loop = [&](auto d_tag) __attribute__((always_inline)) {
+        for (int j = 0; j < n_tiles; ++j) {
+            // This wave's copies of tile j (those of j+1 and j+2 may still be in
+            // flight); then every wave's.
+            if (j + 2 < n_tiles) wait_vmcnt<2 * kFp8CopiesPerTile>();
+            else if (j + 1 < n_tiles) wait_vmcnt<kFp8CopiesPerTile>();
+            else wait_vmcnt<0>();
+            __syncthreads();  // tile j in LDS for every wave; every wave is done with tile j-1's stage
+            // Stage (j+3) % 4 held tile j-1.
+            const uint64_t vmask = vm0;
+            vm0 = vm1;
+            vm1 = vm2;
+            vm2 = j + kFp8Stages - 1 < n_tiles ? issue_tile(j + kFp8Stages - 1) : 0;
+            const uint8_t* stage = &s_raw[j % kFp8Stages][0];
 
-        // S^T partial over this wave's 256 dims: the non-rotary k-steps
-        // (dims < 448) and the rotary ones (dh = 1, k-steps 12..15)
-        // accumulate apart; the non-rotary partial is scaled per key.  The
-        // two dim halves are separate instances (kD), so that every operand
-        // is a fixed register.
-        f32x16 sacc = f32x16{};
-        float sc_key[16];
-        auto scores = [&](auto d_tag) __attribute__((always_inline)) {
-            constexpr int kD = decltype(d_tag)::value;
-            constexpr int kNopeSteps = kD == 0 ? 16 : 12;
-            const uint8_t* rec = stage + key_s * kFp8RecSlot + 256 * kD + 8 * (l >> 5);
-            u32x2 cn[kNopeSteps];
-            u32x4 cr[16 - kNopeSteps + 1];
-#pragma unroll
-            for (int jj = 0; jj < kNopeSteps; ++jj) cn[jj] = *(const u32x2*)(rec + 16 * jj);
-#pragma unroll
-            for (int q = 0; q < 16 - kNopeSteps; ++q) {  // bf16 dims 448 + 16q + 8(l >> 5) .. +8
-                cr[q] = *(const u32x4*)(stage + key_s * kFp8RecSlot + kNope + 32 * q + 16 * (l >> 5));
-            }
-            // Every read in flight before the first product (left alone, the
-            // scheduler issues one read ahead of its use, and with one wave
-            // per SIMD nothing hides the LDS latency of each).
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 sacc_r = f32x16{};
-#pragma unroll
-            for (int jj = 0; jj < kNopeSteps; ++jj)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16x8(cn[jj][0], cn[jj][1]), qf[jj], sacc, 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 16 - kNopeSteps; ++q)
-                sacc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cr[q]), qf[kNopeSteps + q], sacc_r, 0, 0, 0);
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const f32x4 sc4 = *(const f32x4*)(&s_rsc[j % kFp8Stages][8 * qd + 4 * (l >> 5)]);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    sc_key[4 * qd + jj] = sc4[jj];
-                    sacc[4 * qd + jj] = sacc[4 * qd + jj] * sc4[jj] + sacc_r[4 * qd + jj];
+            // S^T partial over this wave's 256 dims: the non-rotary k-steps
+            // (dims < 448) and the rotary ones (dh = 1, k-steps 12..15)
+            // accumulate apart; the non-rotary partial is scaled per key.  The
+            // two dim halves are separate instances (kD), so that every operand
+            // is a fixed register.
+            f32x16 sacc = f32x16{};
+            float sc_key[16];
+            auto scores = [&](auto d_tag) __attribute__((always_inline)) {
+                constexpr int kD = decltype(d_tag)::value;
+                constexpr int kNopeSteps = kD == 0 ? 16 : 12;
+                const uint8_t* rec = stage + key_s * kFp8RecSlot + 256 * kD + 8 * (l >> 5);
+                u32x2 cn[kNopeSteps];
+                u32x4 cr[16 - kNopeSteps + 1];
+    #pragma unroll
+                for (int jj = 0; jj < kNopeSteps; ++jj) cn[jj] = *(const u32x2*)(rec + 16 * jj);
+    #pragma unroll
+                for (int q = 0; q < 16 - kNopeSteps; ++q) {  // bf16 dims 448 + 16q + 8(l >> 5) .. +8
+                    cr[q] = *(const u32x4*)(stage + key_s * kFp8RecSlot + kNope + 32 * q + 16 * (l >> 5));
                 }
-            }
-        };
-        if (dh == 0) scores(std::integral_constant<int, 0>{});
-        else scores(std::integral_constant<int, 1>{});
-        exchange_partial(s_sx, w, l, sacc);
+                // Every read in flight before the first product (left alone, the
+                // scheduler issues one read ahead of its use, and with one wave
+                // per SIMD nothing hides the LDS latency of each).
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 sacc_r = f32x16{};
+    #pragma unroll
+                for (int jj = 0; jj < kNopeSteps; ++jj)
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16x8(cn[jj][0], cn[jj][1]), qf[jj], sacc, 0, 0, 0);
+    #pragma unroll
+                for (int q = 0; q < 16 - kNopeSteps; ++q)
+                    sacc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cr[q]), qf[kNopeSteps + q], sacc_r, 0, 0, 0);
+    #pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const f32x4 sc4 = *(const f32x4*)(&s_rsc[j % kFp8Stages][8 * qd + 4 * (l >> 5)]);
+    #pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        sc_key[4 * qd + jj] = sc4[jj];
+                        sacc[4 * qd + jj] = sacc[4 * qd + jj] * sc4[jj] + sacc_r[4 * qd + jj];
+                    }
+                }
+            };
+            scores(d_tag);
+            exchange_partial(s_sx, w, l, sacc);
 
-        bf16x8 pb[2], pbs[2];
-        softmax_tile<true>(sacc, vmask, a.scale_log2, l, sc_key, m_run, l_run, oacc, pb, pbs);
+            bf16x8 pb[2], pbs[2];
+            softmax_tile<true>(sacc, vmask, a.scale_log2, l, sc_key, m_run, l_run, oacc, pb, pbs);
 
-        // O^T += K^T . P^T: lane l holds dim 256dh + 32mb + (l & 31) of the
-        // eight keys 16pp + 4h + {0..3, 8..11}, h = l >> 5, in the order in
-        // which P^T holds them (the score tile's MFMA output layout, see
-        // group_key); the transposing reads' source lanes address those keys.
-        // All operand reads go out before the products.
-        auto pv = [&](auto d_tag) __attribute__((always_inline)) {
-            constexpr int kD = decltype(d_tag)::value;
-            constexpr int kNopeMb = kD == 0 ? 8 : 6;  // dim blocks below 448
-            i32x2 c8[2 * kNopeMb];
-            bf16x4 c16[2 * (8 - kNopeMb) + 1][2];  // (+1: no zero-length array for kD = 0)
-#pragma unroll
-            for (int mb = 0; mb < kNopeMb; ++mb)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
-                    const int js = gi >> 1;  // the key this source lane addresses: element js of the operand
-                    const int key = 16 * pp + 4 * (g >> 1) + (js & 3) + 8 * (js >> 2);
-                    const uint8_t* p0 = stage + key * kFp8RecSlot + dim_base + 8 * (gi & 1);
-                    c8[2 * mb + pp] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)lds_addr(p0));
-                }
-#pragma unroll
-            for (int mb = kNopeMb; mb < 8; ++mb)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
-                    const int key = 16 * pp + 4 * (g >> 1) + (gi >> 2);  // elements 0..3; 4..7 are 8 keys on
-                    const uint8_t* p0 = stage + key * kFp8RecSlot + kNope + 2 * (dim_base - kNope + 4 * (gi & 3));
-                    c16[2 * (mb - kNopeMb) + pp][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0));
-                    c16[2 * (mb - kNopeMb) + pp][1] =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0 + 8 * kFp8RecSlot));
-                }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mb = 0; mb < kNopeMb; ++mb)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp)
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        e4m3x8_to_bf16x8((uint32_t)c8[2 * mb + pp][0], (uint32_t)c8[2 * mb + pp][1]), pbs[pp], oacc[mb], 0, 0, 0);
-#pragma unroll
-            for (int mb = kNopeMb; mb < 8; ++mb)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const bf16x4 lo = c16[2 * (mb - kNopeMb) + pp][0], hi = c16[2 * (mb - kNopeMb) + pp][1];
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
-                                                                      pb[pp], oacc[mb], 0, 0, 0);
-                }
-        };
-        if (dh == 0) pv(std::integral_constant<int, 0>{});
-        else pv(std::integral_constant<int, 1>{});
-    }
+            // O^T += K^T . P^T: lane l holds dim 256dh + 32mb + (l & 31) of the
+            // eight keys 16pp + 4h + {0..3, 8..11}, h = l >> 5, in the order in
+            // which P^T holds them (the score tile's MFMA output layout, see
+            // group_key); the transposing reads' source lanes address those keys.
+            // All operand reads go out before the products.
+            auto pv = [&](auto d_tag) __attribute__((always_inline)) {
+                constexpr int kD = decltype(d_tag)::value;
+                constexpr int kNopeMb = kD == 0 ? 8 : 6;  // dim blocks below 448
+                i32x2 c8[2 * kNopeMb];
+                bf16x4 c16[2 * (8 - kNopeMb) + 1][2];  // (+1: no zero-length array for kD = 0)
+    #pragma unroll
+                for (int mb = 0; mb < kNopeMb; ++mb)
+    #pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
+                        const int js = gi >> 1;  // the key this source lane addresses: element js of the operand
+                        const int key = 16 * pp + 4 * (g >> 1) + (js & 3) + 8 * (js >> 2);
+                        const uint8_t* p0 = stage + key * kFp8RecSlot + dim_base + 8 * (gi & 1);
+                        c8[2 * mb + pp] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)lds_addr(p0));
+                    }
+    #pragma unroll
+                for (int mb = kNopeMb; mb < 8; ++mb)
+    #pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
+                        const int key = 16 * pp + 4 * (g >> 1) + (gi >> 2);  // elements 0..3; 4..7 are 8 keys on
+                        const uint8_t* p0 = stage + key * kFp8RecSlot + kNope + 2 * (dim_base - kNope + 4 * (gi & 3));
+                        c16[2 * (mb - kNopeMb) + pp][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0));
+                        c16[2 * (mb - kNopeMb) + pp][1] =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0 + 8 * kFp8RecSlot));
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int mb = 0; mb < kNopeMb; ++mb)
+    #pragma unroll
+                    for (int pp = 0; pp < 2; ++pp)
+                        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            e4m3x8_to_bf16x8((uint32_t)c8[2 * mb + pp][0], (uint32_t)c8[2 * mb + pp][1]), pbs[pp], oacc[mb], 0, 0, 0);
+    #pragma unroll
+                for (int mb = kNopeMb; mb < 8; ++mb)
+    #pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const bf16x4 lo = c16[2 * (mb - kNopeMb) + pp][0], hi = c16[2 * (mb - kNopeMb) + pp][1];
+                        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
+                                                                          pb[pp], oacc[mb], 0, 0, 0);
+                    }
+            };
+            pv(d_tag);
+        }
+    };
+    if (dh == 0) tile_loop(std::integral_constant<int, 0>{});
+    else tile_loop(std::integral_constant<int, 1>{});
     write_result<2>(a, it, hh, dh, l, oacc, m_run, l_run, &s_raw[0][0], &s_raw[0][0] + 32 * 1024);
 }
 
