@@ -329,13 +329,12 @@ int32_t tile_keys(Layout layout) { return layout == Layout::kNarrow ? kNarrowTil
 int32_t max_split_keys(Layout layout) { return layout == Layout::kNarrow ? kNarrowMaxSplitKeys : kMaxSplitKeys; }
 
 // Keys per split: enough splits per row to fill the chip once, with at
-// least 64 keys per split for bf16 pools (32 for packed FP8, whose kernel
-// stages one tile through registers and is latency-bound on few rows); for
-// bf16 at least 128 keys (4 tiles) when that still occupies half the compute
-// units, which spreads the fixed per-workgroup cost (metadata, Q, partial
-// write) over more tiles.
-// (Measured on MI355X: FP8 C4 decode with 8 rows runs 28.0 us with 10
-// splits and 24.7 us with 20.)
+// least 64 keys (2 tiles) per split; for bf16 at least 128 keys (4 tiles)
+// when that still occupies half the compute units, which spreads the fixed
+// per-workgroup cost (metadata, Q, partial write) over more tiles.
+// (Measured on MI355X, FP8 C4 decode at 1M tokens, 8 rows, per step:
+// 20 splits of 32 keys 17.9 us, 10 of 64 17.0 us, 7 of 96 17.9 us; the
+// shorter splits' extra partials and merge outweigh their shorter loop.)
 void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int32_t* splits, int32_t* chunk) {
     const bool fp8 = layout == Layout::kFp8;
     const int64_t hpb = heads_per_block(layout);
@@ -346,7 +345,7 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
     } else {
         const int64_t rows = std::max<int64_t>(1, (int64_t)T * head_blocks);
         int64_t want = (cus + rows - 1) / rows;  // splits per row to fill the chip once
-        const int64_t min_keys = fp8 ? 32 : 64;
+        const int64_t min_keys = 64;
         const int64_t most = std::max<int64_t>(1, (nmax + min_keys - 1) / min_keys);
         want = std::min(std::max<int64_t>(want, 1), most);
         if (!fp8) {
