@@ -243,9 +243,9 @@ dsv4_status ensure_topk_count(DeviceState* d, hipStream_t st) {
         return fail(DSV4_ERR_WORKSPACE, "the top-k counters are not set up and the stream is being captured; call "
                                         "dsv4_attn_workspace_reserve before capturing");
     void* p = nullptr;
-    if (hipMalloc(&p, 2 * sizeof(uint32_t) * kTopkMaxRowsSplit) != hipSuccess)
+    if (hipMalloc(&p, 4 * sizeof(uint32_t) * kTopkMaxRowsSplit) != hipSuccess)
         return fail(DSV4_ERR_WORKSPACE, "hipMalloc of the top-k counters failed");
-    DSV4_HIP(hipMemset(p, 0, 2 * sizeof(uint32_t) * kTopkMaxRowsSplit));
+    DSV4_HIP(hipMemset(p, 0, 4 * sizeof(uint32_t) * kTopkMaxRowsSplit));
     DSV4_HIP(hipDeviceSynchronize());
     d->topk_count = (uint32_t*)p;  // kept for the life of the process
     return DSV4_OK;

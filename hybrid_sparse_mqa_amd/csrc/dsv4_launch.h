@@ -94,7 +94,7 @@ struct TopkArgs {
     // allocated, and by the finishing kernel after use).
     uint64_t* ws_list;   // [T, ws_cap] (key << 32) | index of each chunk's survivors
     int64_t ws_cap;
-    uint32_t* ws_count;  // [T, 2]: survivors appended so far, list-incomplete flag
+    uint32_t* ws_count;  // [T, 4]: survivors appended so far, list-incomplete flag, threshold bound (kBins - digit, 0: none), unused
 };
 // List workspace bytes of the multi-workgroup path for T rows (0 if ld is
 // short); binding takes the list workspace and the per-row counters.

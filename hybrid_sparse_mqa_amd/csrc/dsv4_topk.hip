@@ -25,15 +25,24 @@
 //                       (key, index) of every candidate at or above it
 //                       appended to the row's survivor list.  Every
 //                       candidate of the row's top K is in its chunk's top K,
-//                       so the list holds the whole answer;
-//   topk_finish_kernel  one workgroup per row: the first digit's histogram
-//                       over the survivor list, then a second pass over the
-//                       list moves the candidates above D0 to the kept list
-//                       and those at it to LDS, and the selection above; it
-//                       also clears the row's counter for the next call.  A
-//                       row whose list overflowed its capacity, or whose
-//                       threshold digit holds too many candidates for LDS
-//                       (heavy ties), runs the selection over the whole row.
+//                       so the list holds the whole answer.  Each full chunk
+//                       also offers a lower bound on the row's threshold
+//                       digit: with C full chunks and q = ceil(K / C), the
+//                       largest digit d_c with count(digit >= d_c) >= q in
+//                       chunk c; min_c d_c has at least C q >= K candidates
+//                       at or above it, so the row's K-th best lies there too;
+//   topk_finish_kernel  one workgroup per row: the list entries at or above
+//                       that bound (usually a tenth of the list) are
+//                       compacted into LDS and selected there (first-digit
+//                       histogram, split, selection at the threshold); a
+//                       list with too many of them takes the general route:
+//                       the fine first digit's histogram over the whole list,
+//                       then a second pass moves the candidates above D0 to
+//                       the kept list and those at it to LDS.  It also clears
+//                       the row's counters for the next call.  A row whose
+//                       list overflowed its capacity, or whose threshold
+//                       digit holds too many candidates for LDS (heavy ties),
+//                       runs the selection over the whole row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,17 +77,18 @@ struct Smem {
     uint32_t pick[2];
     uint32_t wsum[4];
     uint32_t count;
+    uint32_t kmax;
     uint32_t trash[3][kThreads];  // per-lane targets of the stores of elements not taken
     __attribute__((aligned(16))) int32_t sel[kTopkMaxK + 16];
-    union {  // the candidate list, then (once selected) the output bitmap
-        struct {
-            __attribute__((aligned(16))) uint32_t ckey[kCompCap + 16];
-            __attribute__((aligned(16))) int32_t cidx[kCompCap + 16];
-        };
-        uint32_t bitmap[kBitmapMax / 32];
-    };
+    __attribute__((aligned(16))) uint32_t ckey[kCompCap + 16];
+    __attribute__((aligned(16))) int32_t cidx[kCompCap + 16];
 };
-static_assert(2 * (kCompCap + 16) >= kBitmapMax / 32, "the bitmap fits the candidate list's place");
+// The output bitmap (once selected) lives in hist: word w of the bitmap at
+// word 36 (w / 32) + w % 32, so that the 32 words each thread scans start
+// 144 bytes apart and 16 lanes' 16-byte reads hit 16 different bank groups.
+__device__ __forceinline__ int bitmap_word(int w) { return 36 * (w >> 5) + (w & 31); }
+static_assert(36 * (kBitmapMax / 32 / 32) + 20 * 256 <= kFineBins, "the bitmap and its word places fit the histogram's place");
+static_assert(kBins + 2 * kCompCap <= kFineBins, "the bounded entries fit above the first digit's bins");
 
 // Adds one to hist[bin] for the active lanes; the lanes that share the first
 // active lane's bin add with one atomic.  For passes over whole rows, where
@@ -323,44 +333,62 @@ __device__ __forceinline__ void select_at_threshold(Smem& s, int m, uint32_t d0,
 
 // Writes the K kept indices s.sel[0 .. K) (distinct, all below n) to out in
 // ascending order.  For n <= kBitmapMax: a bitmap of the kept indices; each
-// thread counts the bits of its stretch of words, a workgroup scan gives its
-// first place, and it writes its indices in order.  Otherwise each index goes
+// thread counts the bits of its stretch of 32 words, a workgroup scan gives
+// its first place, and it records the place of each of its words' first bit
+// (the running count); then each kept index goes to the place of its word
+// plus the number of bits below it in that word.  Otherwise each index goes
 // to the place given by the number of kept indices below it.
 __device__ __forceinline__ void rank_sort_write(Smem& s, int K, int n, int32_t* out) {
     const int tid = threadIdx.x;
     if (n <= kBitmapMax) {
         const int words = (n + 31) >> 5;
         constexpr int kWpt = kBitmapMax / 32 / kThreads;  // words per thread (32)
-        for (int j = 4 * tid; j < words; j += 4 * kThreads) *(uint4*)&s.bitmap[j] = uint4{0u, 0u, 0u, 0u};
+        static_assert(kWpt == 32 && kTopkMaxK < 65536, "one bitmap stretch per thread; 16-bit places");
+        uint32_t* const bitmap = s.hist;                  // word w at bitmap_word(w)
+        uint32_t* const place = s.hist + 36 * kThreads;   // thread t's 32 word places, two 16-bit places per
+                                                          // word, at 20 t (16 lanes' 16-byte stores: 16 bank groups)
+        const int padded = 36 * ((words + 31) >> 5);
+        for (int j = 4 * tid; j < padded; j += 4 * kThreads) *(uint4*)&bitmap[j] = uint4{0u, 0u, 0u, 0u};
         __syncthreads();
         for (int i = tid; i < K; i += kThreads) {
             const int32_t v = s.sel[i];
-            atomicOr(&s.bitmap[v >> 5], 1u << (v & 31));
+            atomicOr(&bitmap[bitmap_word(v >> 5)], 1u << (v & 31));
         }
         __syncthreads();
         const int w0 = kWpt * tid;
-        uint32_t bits[kWpt];
-        uint32_t cnt = 0;
+        uint32_t cnt[kWpt];
+        uint32_t mine = 0;
 #pragma unroll
         for (int j = 0; j < kWpt; j += 4) {
-            const uint4 q = w0 + j < words ? *(const uint4*)&s.bitmap[w0 + j] : uint4{0u, 0u, 0u, 0u};
-            bits[j] = w0 + j < words ? q.x : 0u;
-            bits[j + 1] = w0 + j + 1 < words ? q.y : 0u;
-            bits[j + 2] = w0 + j + 2 < words ? q.z : 0u;
-            bits[j + 3] = w0 + j + 3 < words ? q.w : 0u;
+            const uint4 q = w0 + j < words ? *(const uint4*)&bitmap[36 * tid + j] : uint4{0u, 0u, 0u, 0u};
+            cnt[j] = w0 + j < words ? __popc(q.x) : 0u;
+            cnt[j + 1] = w0 + j + 1 < words ? __popc(q.y) : 0u;
+            cnt[j + 2] = w0 + j + 2 < words ? __popc(q.z) : 0u;
+            cnt[j + 3] = w0 + j + 3 < words ? __popc(q.w) : 0u;
         }
 #pragma unroll
-        for (int j = 0; j < kWpt; ++j) cnt += __popc(bits[j]);
+        for (int j = 0; j < kWpt; ++j) mine += cnt[j];
         uint32_t tot;
-        uint32_t pos = block_scan(cnt, tot, s.wsum);
+        uint32_t run = block_scan(mine, tot, s.wsum);
+        uint32_t pk[kWpt / 2];
 #pragma unroll
-        for (int j = 0; j < kWpt; ++j) {
-            uint32_t b = bits[j];
-            while (b != 0u) {
-                const int bit = __builtin_ctz(b);
-                out[pos++] = 32 * (w0 + j) + bit;
-                b &= b - 1u;
-            }
+        for (int j = 0; j < kWpt; j += 2) {
+            const uint32_t lo = run;
+            run += cnt[j];
+            pk[j / 2] = lo | (run << 16);
+            run += cnt[j + 1];
+        }
+#pragma unroll
+        for (int q = 0; q < kWpt / 8; ++q)
+            *(uint4*)&place[20 * tid + 4 * q] = uint4{pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]};
+        __syncthreads();
+        for (int i = tid; i < K; i += kThreads) {
+            const int32_t v = s.sel[i];
+            const int w = v >> 5;
+            const uint32_t word = bitmap[bitmap_word(w)];
+            const uint32_t pw = place[20 * (w >> 5) + ((w & 31) >> 1)];
+            const uint32_t first = (w & 1) ? pw >> 16 : pw & 0xFFFFu;
+            out[first + __popc(word & ((1u << (v & 31)) - 1u))] = v;
         }
         return;
     }
@@ -511,6 +539,7 @@ constexpr int kStage = kTopkMaxK + 1024;  // survivors a chunk stages in LDS (mo
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t pick[2];
+    __shared__ uint32_t pick_q[2];
     __shared__ uint32_t wsum[4];
     __shared__ uint32_t base;
     __shared__ uint64_t stage[kStage];
@@ -534,6 +563,10 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
         if (c_lo + tid + kThreads * j < c_hi) atomicAdd(&hist[k[j] >> kShift[0]], 1u);
     __syncthreads();
     pick_digit<true, kBins>(hist, (uint32_t)min(a.K, c_hi - c_lo), pick, wsum);
+    // A full chunk's share of the row's threshold bound: its q-th best digit.
+    const int full_chunks = n / kTopkChunk;
+    const bool full = c_hi - c_lo == kTopkChunk;
+    if (full) pick_digit<true, kBins>(hist, (uint32_t)((a.K + full_chunks - 1) / full_chunks), pick_q, wsum);
     __syncthreads();
     const uint32_t d0 = pick[0];
     uint32_t mine = 0;
@@ -542,8 +575,9 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     uint32_t tot;
     uint32_t pos = block_scan(mine, tot, wsum);
     if (tid == 0) {
-        base = atomicAdd(&a.ws_count[2 * t], tot);
-        if (tot > (uint32_t)kStage) atomicOr(&a.ws_count[2 * t + 1], 1u);  // the row's list is incomplete
+        base = atomicAdd(&a.ws_count[4 * t], tot);
+        if (tot > (uint32_t)kStage) atomicOr(&a.ws_count[4 * t + 1], 1u);  // the row's list is incomplete
+        if (full) atomicMax(&a.ws_count[4 * t + 2], (uint32_t)kBins - pick_q[0]);  // kBins - min_c d_c
     }
     // The survivors into LDS (branch-free: the others go to this lane's trash
     // word), then to the row's list with coalesced stores.
@@ -611,18 +645,107 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
     const uint64_t* list = a.ws_list + (int64_t)t * a.ws_cap;
     uint4 q0[kLB];
     load_list_pairs(list, (int)(a.ws_cap >> 1), 0, q0);
-    const uint32_t m = a.ws_count[2 * t];
-    const bool overflow = a.ws_count[2 * t + 1] != 0u;
+    const uint32_t m = a.ws_count[4 * t];
+    const bool overflow = a.ws_count[4 * t + 1] != 0u;
+    const uint32_t bound = a.ws_count[4 * t + 2];
     __syncthreads();  // every thread has read the counters
     if (tid == 0) {   // zero for the next call
-        a.ws_count[2 * t] = 0u;
-        a.ws_count[2 * t + 1] = 0u;
+        a.ws_count[4 * t] = 0u;
+        a.ws_count[4 * t + 1] = 0u;
+        a.ws_count[4 * t + 2] = 0u;
     }
     if (overflow || (int64_t)m > a.ws_cap) {  // the list is incomplete: the whole row
         select_row(s, a.scores + (int64_t)t * a.s_ld, n, K, out);
         return;
     }
     const int m2 = ((int)m + 1) >> 1;
+    if (bound != 0u && m2 <= kThreads * kLB) {
+        // The entries at or above the bound digit lb (kept in registers and
+        // then in LDS, in the fine histogram's upper bins) hold the row's top
+        // K.  Their keys span [lb << 20, kmax]; one histogram over that span
+        // cut into at most kBins bins (the key offset from lb << 20, shifted
+        // right by sh) usually leaves a handful of candidates in the
+        // threshold bin, which are then ranked directly.
+        const uint32_t lb = (uint32_t)kBins - bound;
+        uint32_t* ck = s.hist + kBins;
+        int32_t* ci = (int32_t*)(s.hist + 2 * kBins);
+        uint32_t k[2 * kLB];
+        int32_t c[2 * kLB];
+        unpack_list_pairs(q0, (int)m, 0, k, c);
+        uint32_t cnt = 0, kmax = 0;
+#pragma unroll
+        for (int j = 0; j < 2 * kLB; ++j) {
+            const bool in = k[j] != 0u && (k[j] >> kShift[0]) >= lb;  // key 0: no entry
+            cnt += in ? 1u : 0u;
+            kmax = in ? max(kmax, k[j]) : kmax;
+        }
+        if (tid == 0) s.kmax = 0u;
+        uint32_t tot;
+        uint32_t pos = block_scan(cnt, tot, s.wsum);  // (its barriers order the store above)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+        if ((tid & 63) == 0) atomicMax(&s.kmax, kmax);
+        if (tot <= (uint32_t)kCompCap) {
+#pragma unroll
+            for (int j = 0; j < 2 * kLB; ++j) {
+                if (k[j] != 0u && (k[j] >> kShift[0]) >= lb) {
+                    ck[pos] = k[j];
+                    ci[pos] = c[j];
+                    ++pos;
+                }
+            }
+        }
+        __syncthreads();
+        if (tot > (uint32_t)K && tot <= (uint32_t)kCompCap) {  // tot >= K always; tot == K: the general route
+            const uint32_t base = lb << kShift[0];
+            const uint32_t span = s.kmax - base;
+            const int sh = max(0, 20 - __clz((int)span));  // (span >> sh) < kBins
+            for (int j = tid; j < kBins; j += kThreads) s.hist[j] = 0u;
+            __syncthreads();
+            for (int e = tid; e < (int)tot; e += kThreads) atomicAdd(&s.hist[(ck[e] - base) >> sh], 1u);
+            __syncthreads();
+            pick_digit<true, kBins>(s.hist, (uint32_t)K, s.pick, s.wsum);
+            __syncthreads();
+            const uint32_t dt = s.pick[0];
+            const uint32_t need = (uint32_t)K - s.pick[1];
+            const uint32_t n_eq = s.hist[dt];
+            if (n_eq <= (uint32_t)kRankMax) {
+                // Above the threshold bin: kept; in it: ranked.
+                constexpr int kPerT = kCompCap / kThreads;
+                uint32_t bk[kPerT], bcnt = 0;
+                int32_t bc[kPerT];
+#pragma unroll
+                for (int j = 0; j < kPerT; ++j) {
+                    const int e = tid + kThreads * j;
+                    bk[j] = e < (int)tot ? ck[e] : base;  // no entry: bin 0 -> neither (dt > 0 or n_eq counts it)
+                    bc[j] = ci[min(e, (int)tot - 1)];
+                    const uint32_t d = (bk[j] - base) >> sh;
+                    bcnt += e < (int)tot ? (d > dt ? 1u : (d == dt ? 0x10000u : 0u)) : 0u;
+                }
+                uint32_t btot;
+                const uint32_t bpos = block_scan(bcnt, btot, s.wsum);
+                uint32_t pa = bpos & 0xFFFFu, pe = bpos >> 16;
+#pragma unroll
+                for (int j = 0; j < kPerT; ++j) {
+                    const int e = tid + kThreads * j;
+                    const uint32_t d = (bk[j] - base) >> sh;
+                    if (e < (int)tot && d > dt) s.sel[pa++] = bc[j];
+                    if (e < (int)tot && d == dt) {
+                        s.ckey[pe] = bk[j];
+                        s.cidx[pe] = bc[j];
+                        ++pe;
+                    }
+                }
+                __syncthreads();
+                if (tid == 0) s.count = btot & 0xFFFFu;
+                __syncthreads();
+                select_at_threshold(s, (int)n_eq, 0u, need);  // n_eq <= kRankMax: by rank
+                rank_sort_write(s, K, n, out);
+                return;
+            }
+            __syncthreads();  // hist is cleared below
+        }
+    }
     for (int j = 4 * tid; j < kFineBins; j += 4 * kThreads) *(uint4*)&s.hist[j] = uint4{0u, 0u, 0u, 0u};
     __syncthreads();
     uint32_t n_above = 0, n_at = 0, d0 = 0, need = 0, n_eq = 0;

@@ -161,3 +161,23 @@ def test_topk_one_chunk_overflows_its_stage():
     log("topk one chunk overflowing")
     for k in (512, 2048):
         _check(scores, n, k, f"stage overflow k={k}")
+
+
+@pytest.mark.parametrize("k", [512, 2048, 1])
+def test_topk_chunk_bound_layouts(k):
+    """Rows whose full chunks offer very different bounds on the threshold
+    digit: the best candidates all in one chunk, chunks offset from each
+    other, the best candidates in the partial last chunk (which offers no
+    bound), ties straddling the bound digit, and a plain row."""
+    rng = np.random.default_rng(300 + k)
+    T, ld = 6, (1 << 16) + 700
+    scores = rng.standard_normal((T, ld)).astype(np.float32)
+    scores[0] = np.linspace(-3.0, 3.0, ld, dtype=np.float32)          # increasing: the top K in the last chunk
+    for c in range(ld // 16384 + 1):                                    # chunk c shifted by 0.75 c
+        scores[1, 16384 * c:16384 * (c + 1)] += np.float32(0.75 * c)
+    scores[2, 1 << 16:] = rng.uniform(10.0, 11.0, 700).astype(np.float32)  # the partial chunk holds the best
+    scores[3] = np.round(scores[3] * 2) / 2                             # a few large tied digits
+    scores[4, ::5] = np.float32(2.5)                                     # a tie block across every chunk
+    n = np.array([ld, ld, ld, ld, ld, ld - 5000], np.int32)
+    log(f"topk chunk bounds: {T} x {ld}, k={k}")
+    _check(scores, n, k, f"chunk bounds k={k}")
