@@ -534,16 +534,31 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 // ---- multi-workgroup path -------------------------------------------------
 constexpr int kPer = kTopkChunk / kThreads;  // candidates per thread of a chunk (64)
 
-constexpr int kStage = kTopkMaxK + 1024;  // survivors a chunk stages in LDS (more: the row falls back)
+// Survivors a chunk stages in LDS (more: the row falls back): K + 1024, in
+// the dynamic LDS of the launch, so that small K leaves room for more
+// workgroups per compute unit.
+__host__ __device__ constexpr int chunk_stage(int K) { return K + 1024; }
 
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
+// Candidate of lane slot j (of kPer) of thread tid in its chunk: with
+// kVec = 4 each thread loads 16 scores at a time (candidates 1024 (j / 4) +
+// 4 tid + j % 4), else one (candidate 256 j + tid).
+template <int kVec>
+__device__ __forceinline__ int chunk_cand(int j, int tid) {
+    return kVec == 4 ? 1024 * (j >> 2) + 4 * tid + (j & 3) : kThreads * j + tid;
+}
+
+template <int kVec>
+__global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t pick[2];
     __shared__ uint32_t pick_q[2];
     __shared__ uint32_t wsum[4];
     __shared__ uint32_t base;
-    __shared__ uint64_t stage[kStage];
-    __shared__ uint64_t trash[kThreads];
+    __shared__ uint32_t trash[2][64];
+    extern __shared__ uint32_t stage[];  // chunk_stage(K) keys, then as many indices
+    const int kStage = chunk_stage(a.K);
+    uint32_t* const stage_k = stage;
+    uint32_t* const stage_c = stage + kStage;
     const int t = blockIdx.y;
     const int n = min(a.n_cand[t], a.ld);
     const int c_lo = blockIdx.x * kTopkChunk;
@@ -551,16 +566,42 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     const int c_hi = min(n, c_lo + kTopkChunk);
     const int tid = threadIdx.x;
     for (int j = tid; j < kBins; j += kThreads) hist[j] = 0;
-    const float* row = a.scores + (int64_t)t * a.s_ld;
-    uint32_t k[kPer];
+    // Offsets are taken from the chunk's start (a uniform base), 32-bit and
+    // unsigned, so that each load needs one offset register; which of the
+    // thread's candidates exist is one 64-bit mask (all of them in a full
+    // chunk), so that no per-candidate index stays live across the kernel.
+    const float* crow = a.scores + (int64_t)t * a.s_ld + c_lo;
+    const uint32_t span = (uint32_t)(c_hi - c_lo);
+    uint64_t exists = ~0ull;
+    if (span < (uint32_t)kTopkChunk) {
+        exists = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) k[j] = score_key(row[min(c_lo + tid + kThreads * j, c_hi - 1)]);
+        for (int j = 0; j < kPer; ++j) exists |= (uint64_t)((uint32_t)chunk_cand<kVec>(j, tid) < span) << j;
+    }
+    uint32_t k[kPer];
+    if constexpr (kVec == 4) {
+        // 16-byte loads (the launcher checked the alignment); a vector past
+        // the chunk's end is clamped to the chunk's last one (s_ld % 4 == 0,
+        // so it lies inside the row's storage).
+        const uint32_t last4 = (span - 1) & ~3u;
+#pragma unroll
+        for (int j = 0; j < kPer; j += 4) {
+            const float4 v = *(const float4*)(crow + min((uint32_t)chunk_cand<4>(j, tid), last4));
+            k[j] = score_key(v.x);
+            k[j + 1] = score_key(v.y);
+            k[j + 2] = score_key(v.z);
+            k[j + 3] = score_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) k[j] = score_key(crow[min((uint32_t)chunk_cand<1>(j, tid), span - 1)]);
+    }
     __syncthreads();
     // Plain atomics: at most 64 per lane, so even a chunk of equal keys
     // serialises for a bounded time.
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-        if (c_lo + tid + kThreads * j < c_hi) atomicAdd(&hist[k[j] >> kShift[0]], 1u);
+        if ((exists >> j) & 1u) atomicAdd(&hist[k[j] >> kShift[0]], 1u);
     __syncthreads();
     pick_digit<true, kBins>(hist, (uint32_t)min(a.K, c_hi - c_lo), pick, wsum);
     // A full chunk's share of the row's threshold bound: its q-th best digit.
@@ -571,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     const uint32_t d0 = pick[0];
     uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) mine += (c_lo + tid + kThreads * j < c_hi && (k[j] >> kShift[0]) >= d0) ? 1u : 0u;
+    for (int j = 0; j < kPer; ++j) mine += (((exists >> j) & 1u) && (k[j] >> kShift[0]) >= d0) ? 1u : 0u;
     uint32_t tot;
     uint32_t pos = block_scan(mine, tot, wsum);
     if (tid == 0) {
@@ -580,12 +621,18 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
         if (full) atomicMax(&a.ws_count[4 * t + 2], (uint32_t)kBins - pick_q[0]);  // kBins - min_c d_c
     }
     // The survivors into LDS (branch-free: the others go to this lane's trash
-    // word), then to the row's list with coalesced stores.
+    // word), then to the row's list with coalesced stores.  (The thread index
+    // is re-read, so that the candidate indices are recomputed here rather
+    // than kept from the loads.)
+    int tid_again = tid;
+    asm volatile("" : "+v"(tid_again));
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int c = c_lo + tid + kThreads * j;
-        const bool take = c < c_hi && (k[j] >> kShift[0]) >= d0;
-        *(take && pos < (uint32_t)kStage ? &stage[pos] : &trash[tid]) = ((uint64_t)k[j] << 32) | (uint32_t)c;
+        const int c = c_lo + chunk_cand<kVec>(j, tid_again);
+        const bool take = ((exists >> j) & 1u) && (k[j] >> kShift[0]) >= d0;
+        const bool keep = take && pos < (uint32_t)kStage;
+        *(keep ? &stage_k[pos] : &trash[0][tid & 63]) = k[j];
+        *(keep ? &stage_c[pos] : &trash[1][tid & 63]) = (uint32_t)c;
         pos += take ? 1u : 0u;
     }
     __syncthreads();
@@ -594,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     const int64_t b = base;
     const int n_st = (int)min(tot, (uint32_t)kStage);  // a larger total overflows the row's list anyway
     for (int i = tid; i < n_st; i += kThreads)
-        if (b + i < cap) list[b + i] = stage[i];
+        if (b + i < cap) list[b + i] = ((uint64_t)stage_k[i] << 32) | stage_c[i];
 }
 
 constexpr int kLB = 24;  // 16-byte list loads (two entries each) per thread per batch
@@ -805,7 +852,7 @@ __global__ __launch_bounds__(kThreads) void topk_finish_kernel(TopkArgs a) {
 
 int64_t topk_list_cap(int64_t ld, int64_t K) {
     const int64_t chunks = (ld + kTopkChunk - 1) / kTopkChunk;
-    const int64_t cap = chunks * std::min<int64_t>(kTopkChunk, K + 1024);
+    const int64_t cap = chunks * std::min<int64_t>(kTopkChunk, chunk_stage((int)K));
     return (cap + 1) & ~(int64_t)1;  // even: rows stay 16-byte aligned
 }
 
@@ -827,7 +874,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((a.ld + kTopkChunk - 1) / kTopkChunk), (unsigned)a.T);
-    hipLaunchKernelGGL(topk_chunk_kernel, grid, dim3(kThreads), 0, stream, a);
+    const size_t stage_bytes = 2 * sizeof(uint32_t) * (size_t)chunk_stage(a.K);
+    if (((uintptr_t)a.scores & 15) == 0 && (a.s_ld & 3) == 0)
+        hipLaunchKernelGGL(topk_chunk_kernel<4>, grid, dim3(kThreads), stage_bytes, stream, a);
+    else
+        hipLaunchKernelGGL(topk_chunk_kernel<1>, grid, dim3(kThreads), stage_bytes, stream, a);
     hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.T), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -181,3 +181,23 @@ def test_topk_chunk_bound_layouts(k):
     n = np.array([ld, ld, ld, ld, ld, ld - 5000], np.int32)
     log(f"topk chunk bounds: {T} x {ld}, k={k}")
     _check(scores, n, k, f"chunk bounds k={k}")
+
+
+def test_topk_unaligned_rows():
+    """Score rows that are not 16-byte aligned (a view one column into a
+    wider tensor, odd row stride): the long-row path loads one score at a
+    time there; the result must be the same."""
+    from hybrid_sparse_mqa_amd import dsv4_c4_topk
+
+    rng = np.random.default_rng(17)
+    T, ld = 4, (1 << 16) + 2
+    wide = rng.standard_normal((T, ld + 1)).astype(np.float32)  # row stride ld + 1, odd
+    wide[2] = np.round(wide[2] * 4) / 4  # ties
+    n = np.array([ld, ld - 1, ld - 2, 40000], np.int32)
+    view = torch.from_numpy(wide).cuda()[:, 1:]
+    assert view.data_ptr() % 16 != 0 and view.stride(0) % 4 != 0
+    for k in (512, 2048):
+        got = dsv4_c4_topk(view, torch.from_numpy(n).cuda(), k)
+        torch.cuda.synchronize()
+        want = topk_select(np.ascontiguousarray(wide[:, 1:]), n, k)
+        assert np.array_equal(got.cpu().numpy(), want), f"unaligned rows k={k}"
