@@ -243,6 +243,86 @@ __device__ __forceinline__ void build_slots(const AttnArgs& a, const RowKeys& rk
     __syncthreads();  // slot list ready
 }
 
+// Slot list of keys [k0, k0 + n_here) of row t in compressed-first order
+// (list index i < n_ext: compressed entry i, C4 entries as listed with -1
+// for unused ones; i >= n_ext: window position swa_lo + (i - n_ext)), in two
+// steps.  prefetch_slots issues the loads that need nothing from the row's
+// request bounds -- the C4 indices of the split's keys and the extra
+// page-table row of the request guessed from the row index (t B / T, exact
+// when every request has equally many query rows) -- so that they are in
+// flight with the bounds; finish_slots reloads the table row on a wrong
+// guess, fetches the window keys' page entries (which need the row's
+// position), and writes s_slot.  Every load is unconditional, from a
+// clamped index or from the zero row.
+struct SlotPrefetch {
+    int32_t raw[kMaxSplitKeys / 256];  // C4 index of key k0 + tid + 256 u
+    int32_t tab[kTableCap / 256];      // extra page-table entries tid + 256 j of the guessed request
+    int r_guess;
+};
+
+__device__ __forceinline__ void prefetch_slots(const AttnArgs& a, int t, int k0, int tid, SlotPrefetch& pf) {
+    constexpr int kU = kMaxSplitKeys / 256, kTU = kTableCap / 256;
+    pf.r_guess = min(a.m.B - 1, (int)((int64_t)t * a.m.B / max(a.T, 1)));
+    const int32_t* zero = (const int32_t*)a.zero_row;
+    const bool cached = a.m.R != 0 && a.ext_pages <= kTableCap;
+    const int32_t* ext_row = cached ? a.m.ext_table + (int64_t)pf.r_guess * a.m.ext_ld : zero;
+#pragma unroll
+    for (int j = 0; j < kTU; ++j) pf.tab[j] = ext_row[cached ? min(tid + 256 * j, a.ext_pages - 1) : 0];
+    const bool c4 = a.m.R == 4;
+    const int32_t* c4_row = c4 ? a.m.c4 + (int64_t)t * a.m.c4_ld : zero;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) pf.raw[u] = c4_row[c4 ? min(k0 + tid + 256 * u, max(a.m.K - 1, 0)) : 0];
+}
+
+__device__ __forceinline__ void finish_slots(const AttnArgs& a, const RowKeys& rk, int k0, int n_here,
+                                             SlotPrefetch& pf, int32_t* s_slot, int32_t* s_table, int tid) {
+    constexpr int kU = kMaxSplitKeys / 256, kTU = kTableCap / 256;
+    const bool cached = a.m.R != 0 && a.ext_pages <= kTableCap;
+    const int32_t* ext_row = a.m.ext_table + (int64_t)rk.r * a.m.ext_ld;
+    if (cached && rk.r != pf.r_guess) {  // a wrong guess: the row's own table
+#pragma unroll
+        for (int j = 0; j < kTU; ++j) pf.tab[j] = ext_row[min(tid + 256 * j, a.ext_pages - 1)];
+    }
+    // Page entries of this thread's window keys (clamped for the others).
+    const int32_t* swa_row = a.m.swa_table + (int64_t)rk.r * a.m.swa_ld;
+    int32_t wpg[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int w = min(max(k0 + tid + 256 * u - rk.n_ext, 0), rk.n_swa - 1);
+        wpg[u] = swa_row[(rk.swa_lo + w) >> 8];
+    }
+#pragma unroll
+    for (int j = 0; j < kTU; ++j)
+        if (cached && tid + 256 * j < a.ext_pages) s_table[tid + 256 * j] = pf.tab[j];
+    __syncthreads();  // s_table ready
+    // A table too long for LDS: one more round of (clamped) loads.
+    int32_t pg[kU] = {};
+    if (a.m.R != 0 && !cached) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int e = k0 + tid + 256 * u;
+            const int c = a.m.R == 4 ? pf.raw[u] : e;
+            pg[u] = ext_row[e < rk.n_ext && c >= 0 ? min(c >> 8, a.ext_pages - 1) : 0];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int i = tid + 256 * u;
+        if (i < n_here) {
+            const int e = k0 + i;
+            int32_t slot;
+            if (e < rk.n_ext) {
+                const int c = a.m.R == 4 ? pf.raw[u] : e;
+                slot = c < 0 ? -1 : (cached ? s_table[c >> 8] : pg[u]) * kPage + (c & (kPage - 1));
+            } else {
+                slot = wpg[u] * kPage + ((rk.swa_lo + e - rk.n_ext) & (kPage - 1));
+            }
+            s_slot[i] = slot;
+        }
+    }
+    __syncthreads();  // slot list ready
+}
+
 // ---- Compressed-first key lists (the wide kernels) -------------------------
 // The wide kernels walk a row's keys compressed entries first: list index
 // i < n_ext is compressed entry i (C4: c4_indices[t][i], negative = unused;
@@ -1914,6 +1994,10 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
 // rounding.  Two barriers per tile: one when the tile has landed, one in
 // the score exchange.
 //
+// A split walks its row's compressed entries first, then the window
+// (prefetch_slots / finish_slots), so that its first loads need nothing
+// from the row's request bounds.
+//
 // Ring stage: record of tile key k (its 576 bytes as stored: 448 codes, 64
 // bf16 rotary dims) at byte 592 k (a 16-byte pad after each record spreads
 // the keys of a read over the LDS banks); wave w copies keys 8w .. 8w+7 and
@@ -1968,10 +2052,15 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int hh = w >> 1, dh = w & 1;
 
-    // Q^T as the B operand of the scores, loaded first (lane: head 32hh +
-    // (l & 31), dims 256dh + 16j + 8(l >> 5) .. +8 of k-step j; heads past H
-    // read head H-1, whose results are never written).  The slot list's
-    // loads go out after it, and waiting for them waits for Q too.
+    // The request bounds first (the first wait, for them, leaves every later
+    // load in flight), then the slot list's loads that do not need them,
+    // then Q^T as the B operand of the scores (lane: head 32hh + (l & 31),
+    // dims 256dh + 16j + 8(l >> 5) .. +8 of k-step j; heads past H read head
+    // H-1, whose results are never written).
+    const RequestChunk rc = load_requests(a.m, 0, l);
+    const int k0 = it.s * a.chunk;
+    SlotPrefetch pf;
+    prefetch_slots(a, it.t, k0, tid, pf);
     bf16x8 qf[16];
     {
         const int head = min(it.hb * kWideHeadsPerBlock + 32 * hh + (l & 31), a.H - 1);
@@ -1980,11 +2069,10 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
         for (int j = 0; j < 16; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
     }
 
-    const RowKeys rk = row_keys(a.m, it.t, l);
-    const int k0 = it.s * a.chunk;
+    const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
     const int n_here = max(0, min(rk.n_swa + rk.n_ext, k0 + a.chunk) - k0);
     const int n_tiles = (n_here + kTileKeys - 1) / kTileKeys;
-    build_slots(a, rk, it.t, k0, n_here, s_slot, s_table, tid);
+    finish_slots(a, rk, k0, n_here, pf, s_slot, s_table, tid);
 
     // Copies of tile j into stage j % 4: five 16-byte copies per lane over
     // the wave's 8 x 37 record slots (slot f = 64 i + l is chunk f % 37 of
@@ -2016,7 +2104,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             const int key = tb + (l & 31);
             const int32_t slot = key < n_here ? s_slot[key] : -1;
             used = l < 32 && slot >= 0;
-            const uint8_t* page = (k0 + key < rk.n_swa ? a.swa_pool : a.ext_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
+            const uint8_t* page = (k0 + key < rk.n_ext ? a.ext_pool : a.swa_pool) + (int64_t)(slot >> 8) * kFp8PageBytes;
             rec_ad = (uint64_t)(uintptr_t)(slot >= 0 ? page + (slot & 255) * kFp8RecBytes : a.zero_row);
             sc_ad = (uint64_t)(uintptr_t)(slot >= 0 ? page + kFp8ScaleOffset + 4 * (slot & 255) : a.zero_row);
         }
@@ -2044,8 +2132,9 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Q and the slot list have arrived (the compiler waited for the slot
-    // list, issued after Q); the explicit wait tells it so before any copy.
+    // Q and the slot list have arrived (the compiler waited for the window
+    // page entries, issued after Q); the explicit wait tells it so before
+    // any copy.
     wait_vmcnt<0>();
     // Used-key masks of the tiles in flight (tiles j, j+1, j+2).
     uint64_t vm0 = n_tiles > 0 ? issue_tile(0) : 0;

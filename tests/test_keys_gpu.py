@@ -9,11 +9,11 @@ back to (pool, physical slot) and compare them, in the kernel's own key order,
 with the oracle's gather (canonical slot lists) plus the row's C4 index list
 (for the position of unused entries):
 
-* the 32- and 64-head kernels walk the compressed entries first (C4: the
-  whole index list, -1 entries reading the zero row and masked out; C128:
-  entries 0 .. visible-1), then the window ascending;
-* the 16-head and FP8 kernels walk the window first, then the compressed
-  entries in the same way.
+* the 32- and 64-head and FP8 kernels walk the compressed entries first
+  (C4: the whole index list, -1 entries reading the zero row and masked
+  out; C128: entries 0 .. visible-1), then the window ascending;
+* the 16-head kernel walks the window first, then the compressed entries in
+  the same way.
 
 Keys past a split's end up to its last tile must read the zero row; the
 valid-key masks must mark exactly the used keys.  The recording build must
@@ -36,7 +36,7 @@ MASK_SENTINEL = 0xA5A5A5A5
 H16, H32, ROLES, H64, FP8 = 1, 2, 3, 4, 5
 TILE = {H16: 16, H32: 32, ROLES: 32, H64: 32, FP8: 32}
 HEADS = {H16: 16, H32: 32, ROLES: 32, H64: 64, FP8: 64}
-COMPRESSED_FIRST = {H16: False, H32: True, ROLES: True, H64: True, FP8: False}
+COMPRESSED_FIRST = {H16: False, H32: True, ROLES: True, H64: True, FP8: True}
 MASKED = {H32, ROLES, H64}
 
 
