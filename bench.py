@@ -15,9 +15,10 @@ timed HIP-graph replay of exactly --steps calls; a roofline object for the
 dominant kernel (the split kernel: the bytes it must read -- Q, C4 index
 lists and every unique KV row -- over its average duration from HIP events
 recorded on its stream around each kernel of a timed run of eager calls on
-the same rotating inputs; these intervals agree with rocprofv3's kernel trace
-to about 1 %, where event nodes inside a graph replay add about a microsecond
-to each interval); the whole path's achieved GB/s per step; and the fp64
+the same rotating inputs, queued behind a spin kernel so that they run back
+to back; inside a graph replay event nodes add about a microsecond to each
+interval, and host-paced eager calls add the launch gaps); the whole path's
+achieved GB/s per step; and the fp64
 oracle timed on the host cores on a bounded sample of the same workload, with
 all threads and with one.
 """
@@ -624,18 +625,35 @@ def main() -> int:
 
     # Kernel durations: a timed run of eager calls on the same rotating inputs,
     # each kernel bracketed by HIP events on the stream it runs on (the
-    # library's timing hook).  Also the host-driven loop time, for context.
+    # library's timing hook).  The calls are queued behind a spin kernel that
+    # outlasts the host's queueing, so that they run back to back and each
+    # interval holds its kernel, not the host's launch gaps.
     n_eager = min(args.steps, 100)
-    dsv4_attn_timing_read()  # clear
-    dsv4_attn_timing_enable(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(n_eager):  # the host's queueing time (the GPU work is warm-up)
+        step(i)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    sl0, sl1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sl0.record()
+    torch.cuda._sleep(1 << 22)
+    sl1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 22) / max(sl0.elapsed_time(sl1), 1e-3)
+    dsv4_attn_timing_read()  # clear
+    torch.cuda._sleep(int(cycles_per_ms * (2.0 * host_ms + 2.0)))
+    spin_end = torch.cuda.Event()
+    spin_end.record()
+    dsv4_attn_timing_enable(True)
     for i in range(n_eager):
         step(i)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / n_eager
     dsv4_attn_timing_enable(False)
+    queued_ahead = not spin_end.query()  # the spin still ran when the last call was queued
+    torch.cuda.synchronize()
     e_split, e_merge, e_calls = dsv4_attn_timing_read()
+    if not queued_ahead:
+        print("[bench] the host queued the timed eager calls slower than the spin kernel ran; "
+              "their event intervals may hold launch gaps", file=sys.stderr)
 
     # Timed region: one replay of a HIP graph holding exactly `steps` calls
     # (rotating over the input sets), bracketed by two events.  Every N-th
@@ -718,13 +736,14 @@ def main() -> int:
             "frac_per_step": ab["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "split_kernel_ms": split_avg_ms,
             "merge_kernel_ms": merge_avg_ms,
-            "kernel_timing": f"HIP events around each kernel of {n_eager} timed eager calls",
+            "kernel_timing": f"HIP events around each kernel of {n_eager} eager calls queued back to back "
+                             f"behind a spin kernel ({'queued ahead' if queued_ahead else 'NOT queued ahead'})",
             "kernels_per_step_frac": (split_avg_ms + merge_avg_ms) / ms_per_step,
             "graph_event_ms_per_step": event_ms / args.steps,
             "graph_sampled_calls": g_calls,
             "graph_sampled_split_interval_ms": g_split_ms / g_calls if g_calls else None,
             "graph_sampled_merge_interval_ms": g_merge_ms / g_calls if g_calls else None,
-            "eager_ms_per_call": eager_ms,
+            "host_queue_ms_per_call": host_ms / n_eager,
         },
         "roofline": ({
             "bound": "mfma",
