@@ -581,8 +581,8 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
     uint32_t k[kPer];
     if constexpr (kVec == 4) {
         // 16-byte loads (the launcher checked the alignment); a vector past
-        // the chunk's end is clamped to the chunk's last one (s_ld % 4 == 0,
-        // so it lies inside the row's storage).
+        // the chunk's end is clamped to the chunk's last one, which lies
+        // within the row's ld scores (ld % 4 == 0).
         const uint32_t last4 = (span - 1) & ~3u;
 #pragma unroll
         for (int j = 0; j < kPer; j += 4) {
@@ -875,7 +875,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     }
     const dim3 grid((unsigned)((a.ld + kTopkChunk - 1) / kTopkChunk), (unsigned)a.T);
     const size_t stage_bytes = 2 * sizeof(uint32_t) * (size_t)chunk_stage(a.K);
-    if (((uintptr_t)a.scores & 15) == 0 && (a.s_ld & 3) == 0)
+    // 16-byte loads need aligned rows, and a row width that is a multiple of
+    // 4 (a vector never reaches past a row's last score).
+    if (((uintptr_t)a.scores & 15) == 0 && (a.s_ld & 3) == 0 && (a.ld & 3) == 0)
         hipLaunchKernelGGL(topk_chunk_kernel<4>, grid, dim3(kThreads), stage_bytes, stream, a);
     else
         hipLaunchKernelGGL(topk_chunk_kernel<1>, grid, dim3(kThreads), stage_bytes, stream, a);

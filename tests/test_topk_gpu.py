@@ -183,21 +183,32 @@ def test_topk_chunk_bound_layouts(k):
     _check(scores, n, k, f"chunk bounds k={k}")
 
 
-def test_topk_unaligned_rows():
-    """Score rows that are not 16-byte aligned (a view one column into a
-    wider tensor, odd row stride): the long-row path loads one score at a
-    time there; the result must be the same."""
+@pytest.mark.parametrize("layout", ["offset-odd-stride", "aligned-ragged-width"])
+def test_topk_unaligned_rows(layout):
+    """Score rows the long-row path cannot read 16 bytes at a time: a view
+    one column into a wider tensor (odd row stride, unaligned rows), and
+    aligned rows whose width is not a multiple of 4 (the last vector would
+    reach past the row's last score).  One score at a time there; the result
+    must be the same."""
     from hybrid_sparse_mqa_amd import dsv4_c4_topk
 
     rng = np.random.default_rng(17)
     T, ld = 4, (1 << 16) + 2
-    wide = rng.standard_normal((T, ld + 1)).astype(np.float32)  # row stride ld + 1, odd
+    wide = rng.standard_normal((T, ld + 2)).astype(np.float32)
     wide[2] = np.round(wide[2] * 4) / 4  # ties
     n = np.array([ld, ld - 1, ld - 2, 40000], np.int32)
-    view = torch.from_numpy(wide).cuda()[:, 1:]
-    assert view.data_ptr() % 16 != 0 and view.stride(0) % 4 != 0
+    full = torch.from_numpy(wide).cuda()
+    if layout == "offset-odd-stride":
+        full = full[:, : ld + 1]
+        full = torch.as_strided(full.contiguous(), (T, ld), (ld + 1, 1), 1)
+        host = full.cpu().numpy()
+        assert full.data_ptr() % 16 != 0 and full.stride(0) % 4 != 0
+    else:
+        full = full[:, :ld]
+        host = wide[:, :ld]
+        assert full.data_ptr() % 16 == 0 and full.stride(0) % 4 == 0 and ld % 4 != 0
     for k in (512, 2048):
-        got = dsv4_c4_topk(view, torch.from_numpy(n).cuda(), k)
+        got = dsv4_c4_topk(full, torch.from_numpy(n).cuda(), k)
         torch.cuda.synchronize()
-        want = topk_select(np.ascontiguousarray(wide[:, 1:]), n, k)
-        assert np.array_equal(got.cpu().numpy(), want), f"unaligned rows k={k}"
+        want = topk_select(np.ascontiguousarray(host), n, k)
+        assert np.array_equal(got.cpu().numpy(), want), f"{layout} k={k}"
