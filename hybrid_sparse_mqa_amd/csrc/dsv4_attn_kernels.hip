@@ -5,6 +5,8 @@
 //  * split kernels -- gather + KV tile load (+ FP8 decode) + scores + online
 //    softmax + PV for one (query row, head block, key split); with a single
 //    split they also apply the sink and write out / lse:
+//      attn_ws_kernel<1>    bf16 KV, 32-head blocks with wave roles (two
+//                           score waves, two PV waves one tile behind);
 //      attn_wide_kernel<2>  bf16 KV, 64-head blocks (two head groups x two
 //                           dim halves), one 32-key tile per step;
 //      attn_wide_kernel<1>  bf16 KV, 32-head blocks (four dim quarters),
@@ -21,9 +23,9 @@
 //    The second product reduces over keys.  The bf16 kernels stream key rows
 //    straight from HBM into LDS (global_load_lds) and read PV operands with
 //    the gfx950 transposing LDS read (ds_read_b64_tr_b16).  The FP8 kernel
-//    stages rows through registers, decodes them, and writes the tile twice
-//    (row-major for S, 8-key columns for PV, via an in-register 8x8
-//    transpose).
+//    streams the raw records into LDS the same way and converts the codes
+//    into bf16 operands in registers: row-wise reads for S, the 8-bit
+//    transposing read (ds_read_b64_tr_b8) for PV.
 //
 // Work items (row, head block, split) are laid out so that consecutive
 // items -- the head blocks and splits of one row -- go to the same XCD
@@ -48,39 +50,6 @@ constexpr float kRescaleLog2 = 8.0f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Tile-relative index of the e-th key (e = 0..7) loaded by wave w.  Wave w
-// owns the 8-key group G(w) = {16p + 4h + j, 16p + 8 + 4h + j : j < 4} with
-// p = w >> 1, h = w & 1: exactly the keys that lane half h of the score tile
-// holds for PV k-step p (see the MFMA output layout below), so the transposed
-// group feeds PV with no further shuffling.
-__device__ __forceinline__ int group_key(int w, int e) {
-    return 16 * (w >> 1) + 4 * (w & 1) + (e & 3) + 8 * (e >> 2);
-}
-
-// Row-major tile: 32 rows of 1 KiB; 16-byte chunk c of row k is stored at
-// chunk c ^ row_swz(k).  row_swz is a permutation of 0..15 over any 16
-// consecutive rows, so 16 lanes reading one column of 16 rows hit 16
-// distinct 16-byte bank groups; and the 4 rows k = 4q .. 4q+3 are spread
-// by 4 chunks each, so the 4 rows x 4 chunks that 32 lanes of a
-// transposing read touch (rows 4q + j, chunks 4m .. 4m+3) land in 16
-// distinct bank groups.
-__device__ __forceinline__ int row_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
-__device__ __forceinline__ int krow_offset(int k, int chunk) { return k * 1024 + 16 * (chunk ^ row_swz(k)); }
-
-// Column tile: group g (8 keys) x 512 dims x 16 bytes; dim d is stored at
-// d ^ ((d >> 3) & 15), conflict-free for the transposing writes (lanes step
-// 8 dims) and for the PV reads (lanes step 1 dim).
-__device__ __forceinline__ int kt_offset(int g, int d) { return (g * 512 + (d ^ ((d >> 3) & 15))) * 16; }
-
-// Column i (dim 8l+i) of an 8x8 block of bf16: element j = row j's element i.
-__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&rows)[8], int i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 c;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) c[k] = __builtin_amdgcn_perm(rows[2 * k + 1][i >> 1], rows[2 * k][i >> 1], sel);
-    return c;
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     __bf16 x = (__bf16)a, y = (__bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -94,11 +63,6 @@ template <bool kHi>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
 }
-
-struct TileRegs {
-    u32x4 v[8];   // bf16: 8 dims of 8 keys; fp8 lanes < 56: 8 codes in v[e].xy
-    float sc[8];  // fp8 per-token scale of each key
-};
 
 
 // vmcnt-only wait (expcnt / lgkmcnt left at their maxima), gfx9 encoding.
@@ -2210,8 +2174,9 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
 
             // O^T += K^T . P^T: lane l holds dim 256dh + 32mb + (l & 31) of the
             // eight keys 16pp + 4h + {0..3, 8..11}, h = l >> 5, in the order in
-            // which P^T holds them (the score tile's MFMA output layout, see
-            // group_key); the transposing reads' source lanes address those keys.
+            // which P^T holds them (the score tile's MFMA output layout: lane
+            // half h holds keys 8q + 4h + {0..3} in registers 4q .. 4q+3); the
+            // transposing reads' source lanes address those keys.
             // All operand reads go out before the products.
             auto pv = [&](auto d_tag) __attribute__((always_inline)) {
                 constexpr int kD = decltype(d_tag)::value;
