@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdsv4_attn.so")
 SOURCES = ["dsv4_attn_kernels.hip", "dsv4_pack.hip", "dsv4_topk.hip", "dsv4_api.cpp"]
 ARCH = os.environ.get("DSV4_OFFLOAD_ARCH", "gfx950")
+# Per-source flags.  The top-k kernels issue their list-offset atomic from one
+# thread and use its result later; the compiler's atomic combining (a wave
+# reduction around a uniform-address atomic) would wait for the result at once.
+EXTRA_FLAGS = {"dsv4_topk.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
@@ -37,7 +41,7 @@ def compile_flags():
 def _compile(src: str, verbose: bool) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(CSRC, src + ".o")
-    cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", path, "-o", obj]
+    cmd = [hipcc(), *compile_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

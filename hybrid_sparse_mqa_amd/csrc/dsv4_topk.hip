@@ -615,13 +615,16 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
     for (int j = 0; j < kPer; ++j) mine += (((exists >> j) & 1u) && (k[j] >> kShift[0]) >= d0) ? 1u : 0u;
     uint32_t tot;
     uint32_t pos = block_scan(mine, tot, wsum);
+    uint32_t base0 = 0;
     if (tid == 0) {
-        base = atomicAdd(&a.ws_count[4 * t], tot);
+        base0 = atomicAdd(&a.ws_count[4 * t], tot);
         if (tot > (uint32_t)kStage) atomicOr(&a.ws_count[4 * t + 1], 1u);  // the row's list is incomplete
         if (full) atomicMax(&a.ws_count[4 * t + 2], (uint32_t)kBins - pick_q[0]);  // kBins - min_c d_c
     }
     // The survivors into LDS (branch-free: the others go to this lane's trash
-    // word), then to the row's list with coalesced stores.  (The thread index
+    // word), then to the row's list with coalesced stores.  The list offset
+    // is waited for only after the LDS stores (this file is built without the
+    // compiler's atomic combining, which would wait for it right away).  (The thread index
     // is re-read, so that the candidate indices are recomputed here rather
     // than kept from the loads.)
     int tid_again = tid;
@@ -635,6 +638,7 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
         *(keep ? &stage_c[pos] : &trash[1][tid & 63]) = (uint32_t)c;
         pos += take ? 1u : 0u;
     }
+    if (tid == 0) base = base0;
     __syncthreads();
     const int64_t cap = a.ws_cap;
     uint64_t* list = a.ws_list + (int64_t)t * cap;
