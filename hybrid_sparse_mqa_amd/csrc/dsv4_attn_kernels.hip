@@ -1012,9 +1012,12 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(AttnArgs a) {
             }
         }
         {
-            const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i) >> key_shift;
+            const uint32_t tm = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i);
+            if (tm != 0xFFFFFFFFu) {  // a tile with unused keys (uniform)
+                const uint32_t mine = tm >> key_shift;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r] = ((mine >> (8 * (r >> 2) + (r & 3))) & 1u) ? sv[r] : -INFINITY;
+                for (int r = 0; r < 16; ++r) sv[r] = ((mine >> (8 * (r >> 2) + (r & 3))) & 1u) ? sv[r] : -INFINITY;
+            }
         }
         float smax = sv[0];
 #pragma unroll
@@ -1431,9 +1434,12 @@ __global__ __launch_bounds__(256, 1) void attn_ws_kernel(AttnArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) sv[k] = pa[k >> 2][k & 3] + pb2[k >> 2][k & 3];
             {
-                const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i) >> (8 * g);
+                const uint32_t tm = (uint32_t)__builtin_amdgcn_readlane((int)tile_mask, i);
+                if (tm != 0xFFFFFFFFu) {  // a tile with unused keys (uniform)
+                    const uint32_t mine = tm >> (8 * g);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) sv[k] = ((mine >> k) & 1u) ? sv[k] : -INFINITY;
+                    for (int k = 0; k < 8; ++k) sv[k] = ((mine >> k) & 1u) ? sv[k] : -INFINITY;
+                }
             }
             float smax = sv[0];
 #pragma unroll
