@@ -183,7 +183,8 @@ dsv4_status dsv4_kv_pack_fp8(const dsv4_tensor* k, const dsv4_tensor* slots, con
  * compressed entries per query; its kernel section names a TopK kernel).
  *
  *  scores          f32 [T, ld]: scores[t][c] of candidate c (finite); only
- *                  c < num_candidates[t] is read
+ *                  c < num_candidates[t] is used (scores up to ld may be
+ *                  read, never used)
  *  num_candidates  i32 [T]: candidates of row t, 0 <= n <= ld (for C4 at
  *                  position p, floor((p+1)/4)); a caller contract, checked
  *                  with DSV4_VALIDATE=1
