@@ -117,8 +117,9 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t& total) {
     return incl - v;
 }
 
-// Exclusive prefix of `v` over the workgroup, and its total (every thread
-// must call it; `wsum` is 4 words of LDS).
+// Exclusive prefix of `v` over the workgroup of kT threads, and its total
+// (every thread must call it; `wsum` is kT / 64 words of LDS).
+template <int kT = kThreads>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, uint32_t* wsum) {
     const int w = threadIdx.x >> 6;
     uint32_t wt;
@@ -129,7 +130,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, uint
     uint32_t before = 0;
     total = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kT / 64; ++u) {
         const uint32_t x = wsum[u];
         before += u < w ? x : 0u;
         total += x;
@@ -138,16 +139,16 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t& total, uint
 }
 
 // The digit of one radix pass from the LDS histogram hist[0 .. kNbT), by all
-// threads of the workgroup (each holds kNbT/256 consecutive bins).
+// kT threads of the workgroup (each holds kNbT/kT consecutive bins).
 // Descending (top keys): the largest d with count(digit >= d) >= need;
 // out[1] = count(digit > d).  Ascending (low indices): the smallest d with
 // count(digit <= d) >= need; out[1] = count(digit < d).  out[0] = d.
 // need >= 1 and the histogram total >= need; exactly one thread writes out.
 // The caller synchronises before reading out.
-template <bool kDescending, int kNbT>
+template <bool kDescending, int kNbT, int kT = kThreads>
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t need, uint32_t* out, uint32_t* wsum) {
-    constexpr int kPerT = kNbT / kThreads;
-    static_assert(kPerT * kThreads == kNbT && kPerT % 4 == 0, "whole 16-byte groups of bins per thread");
+    constexpr int kPerT = kNbT / kT;
+    static_assert(kPerT * kT == kNbT && kPerT % 4 == 0, "whole 16-byte groups of bins per thread");
     const int tid = threadIdx.x;
     uint32_t v[kPerT];
 #pragma unroll
@@ -162,7 +163,7 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t need, 
 #pragma unroll
     for (int j = 0; j < kPerT; ++j) mine += v[j];
     uint32_t total;
-    uint32_t le = block_scan(mine, total, wsum);  // count(digit < kPerT*tid)
+    uint32_t le = block_scan<kT>(mine, total, wsum);  // count(digit < kPerT*tid)
     // Branch-free search of this thread's bins; one store by the one thread
     // whose bins hold the digit.
     int found = -1;
@@ -532,7 +533,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 }
 
 // ---- multi-workgroup path -------------------------------------------------
-constexpr int kPer = kTopkChunk / kThreads;  // candidates per thread of a chunk (64)
+constexpr int kChunkThreads = 512;               // threads of a chunk workgroup (8 waves)
+constexpr int kPer = kTopkChunk / kChunkThreads;  // candidates per thread of a chunk (32)
 
 // Survivors a chunk stages in LDS (more: the row falls back): K + 1024, in
 // the dynamic LDS of the launch, so that small K leaves room for more
@@ -540,19 +542,21 @@ constexpr int kPer = kTopkChunk / kThreads;  // candidates per thread of a chunk
 __host__ __device__ constexpr int chunk_stage(int K) { return K + 1024; }
 
 // Candidate of lane slot j (of kPer) of thread tid in its chunk: with
-// kVec = 4 each thread loads 16 scores at a time (candidates 1024 (j / 4) +
-// 4 tid + j % 4), else one (candidate 256 j + tid).
+// kVec = 4 each thread loads 4 scores at a time (candidates 2048 (j / 4) +
+// 4 tid + j % 4), else one (candidate 512 j + tid).
 template <int kVec>
 __device__ __forceinline__ int chunk_cand(int j, int tid) {
-    return kVec == 4 ? 1024 * (j >> 2) + 4 * tid + (j & 3) : kThreads * j + tid;
+    return kVec == 4 ? 4 * kChunkThreads * (j >> 2) + 4 * tid + (j & 3) : kChunkThreads * j + tid;
 }
 
 template <int kVec>
-__global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
+// Four waves per SIMD (at most 128 registers; it takes 99): asking for more
+// makes the compiler spill, which measured slower.
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_chunk_kernel(TopkArgs a) {
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t pick[2];
     __shared__ uint32_t pick_q[2];
-    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t wsum[kChunkThreads / 64];
     __shared__ uint32_t base;
     __shared__ uint32_t trash[2][64];
     extern __shared__ uint32_t stage[];  // chunk_stage(K) keys, then as many indices
@@ -565,19 +569,24 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
     if (n <= a.K || c_lo >= n) return;  // the row keeps everything, or the chunk lies past its end
     const int c_hi = min(n, c_lo + kTopkChunk);
     const int tid = threadIdx.x;
-    for (int j = tid; j < kBins; j += kThreads) hist[j] = 0;
+    for (int j = tid; j < kBins; j += kChunkThreads) hist[j] = 0;
     // Offsets are taken from the chunk's start (a uniform base), 32-bit and
     // unsigned, so that each load needs one offset register; which of the
-    // thread's candidates exist is one 64-bit mask (all of them in a full
+    // thread's candidates exist is one 32-bit mask (all of them in a full
     // chunk), so that no per-candidate index stays live across the kernel.
     const float* crow = a.scores + (int64_t)t * a.s_ld + c_lo;
     const uint32_t span = (uint32_t)(c_hi - c_lo);
-    uint64_t exists = ~0ull;
-    if (span < (uint32_t)kTopkChunk) {
-        exists = 0;
+    constexpr int kMaskWords = (kPer + 31) / 32;
+    uint32_t exists[kMaskWords];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) exists |= (uint64_t)((uint32_t)chunk_cand<kVec>(j, tid) < span) << j;
+    for (int q = 0; q < kMaskWords; ++q) exists[q] = ~0u;
+    if (span < (uint32_t)kTopkChunk) {
+#pragma unroll
+        for (int q = 0; q < kMaskWords; ++q) exists[q] = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) exists[j >> 5] |= (uint32_t)((uint32_t)chunk_cand<kVec>(j, tid) < span) << (j & 31);
     }
+    auto has = [&](int j) { return (exists[j >> 5] >> (j & 31)) & 1u; };
     uint32_t k[kPer];
     if constexpr (kVec == 4) {
         // 16-byte loads (the launcher checked the alignment); a vector past
@@ -601,20 +610,20 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
     // serialises for a bounded time.
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-        if ((exists >> j) & 1u) atomicAdd(&hist[k[j] >> kShift[0]], 1u);
+        if (has(j)) atomicAdd(&hist[k[j] >> kShift[0]], 1u);
     __syncthreads();
-    pick_digit<true, kBins>(hist, (uint32_t)min(a.K, c_hi - c_lo), pick, wsum);
+    pick_digit<true, kBins, kChunkThreads>(hist, (uint32_t)min(a.K, c_hi - c_lo), pick, wsum);
     // A full chunk's share of the row's threshold bound: its q-th best digit.
     const int full_chunks = n / kTopkChunk;
     const bool full = c_hi - c_lo == kTopkChunk;
-    if (full) pick_digit<true, kBins>(hist, (uint32_t)((a.K + full_chunks - 1) / full_chunks), pick_q, wsum);
+    if (full) pick_digit<true, kBins, kChunkThreads>(hist, (uint32_t)((a.K + full_chunks - 1) / full_chunks), pick_q, wsum);
     __syncthreads();
     const uint32_t d0 = pick[0];
     uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) mine += (((exists >> j) & 1u) && (k[j] >> kShift[0]) >= d0) ? 1u : 0u;
+    for (int j = 0; j < kPer; ++j) mine += (has(j) && (k[j] >> kShift[0]) >= d0) ? 1u : 0u;
     uint32_t tot;
-    uint32_t pos = block_scan(mine, tot, wsum);
+    uint32_t pos = block_scan<kChunkThreads>(mine, tot, wsum);
     uint32_t base0 = 0;
     if (tid == 0) {
         base0 = atomicAdd(&a.ws_count[4 * t], tot);
@@ -632,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int c = c_lo + chunk_cand<kVec>(j, tid_again);
-        const bool take = ((exists >> j) & 1u) && (k[j] >> kShift[0]) >= d0;
+        const bool take = has(j) && (k[j] >> kShift[0]) >= d0;
         const bool keep = take && pos < (uint32_t)kStage;
         *(keep ? &stage_k[pos] : &trash[0][tid & 63]) = k[j];
         *(keep ? &stage_c[pos] : &trash[1][tid & 63]) = (uint32_t)c;
@@ -644,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 3) void topk_chunk_kernel(TopkArgs a) {
     uint64_t* list = a.ws_list + (int64_t)t * cap;
     const int64_t b = base;
     const int n_st = (int)min(tot, (uint32_t)kStage);  // a larger total overflows the row's list anyway
-    for (int i = tid; i < n_st; i += kThreads)
+    for (int i = tid; i < n_st; i += kChunkThreads)
         if (b + i < cap) list[b + i] = ((uint64_t)stage_k[i] << 32) | stage_c[i];
 }
 
@@ -882,9 +891,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     // 16-byte loads need aligned rows, and a row width that is a multiple of
     // 4 (a vector never reaches past a row's last score).
     if (((uintptr_t)a.scores & 15) == 0 && (a.s_ld & 3) == 0 && (a.ld & 3) == 0)
-        hipLaunchKernelGGL(topk_chunk_kernel<4>, grid, dim3(kThreads), stage_bytes, stream, a);
+        hipLaunchKernelGGL(topk_chunk_kernel<4>, grid, dim3(kChunkThreads), stage_bytes, stream, a);
     else
-        hipLaunchKernelGGL(topk_chunk_kernel<1>, grid, dim3(kThreads), stage_bytes, stream, a);
+        hipLaunchKernelGGL(topk_chunk_kernel<1>, grid, dim3(kChunkThreads), stage_bytes, stream, a);
     hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.T), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
