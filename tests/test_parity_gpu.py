@@ -318,6 +318,28 @@ def _slot(table, r, x):
     return int(table[r, x // 256]) * 256 + x % 256
 
 
+_BEYOND_CACHE = {}
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS, indirect=True)
+def test_page_table_beyond_lds_cache(orc, variant):
+    """C4 rows of requests whose extra page table has more entries than a
+    workgroup caches in LDS (1024 pages, i.e. contexts past 1M tokens): the
+    split kernels resolve compressed slots through one more round of
+    page-table loads.  A decode row and three verify rows; every row
+    checked, on every kernel variant."""
+    _, kv = variant
+    if kv not in _BEYOND_CACHE:
+        _BEYOND_CACHE.clear()  # one case on the device at a time
+        case = make_case(seq_lens=[1_200_000, 1_060_000], n_q=[1, 3], H=64, R=4, seed=91, kv=kv)
+        _BEYOND_CACHE[kv] = (case, G.to_gpu(case), orc.attention(case))
+    case, g, (ro, rl, _) = _BEYOND_CACHE[kv]
+    assert case.extra_page_table.shape[1] > 1024
+    log(f"page table beyond the LDS cache: {case.extra_page_table.shape[1]} pages, kv={kv}")
+    out, lse = G.run_forward(case, g)
+    G.compare(out, lse, ro, rl, what=f"table beyond cache {kv}")
+
+
 @pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS, indirect=True)
 @pytest.mark.parametrize("name,R,sl,nq,where,visible", SPIKES, ids=[s[0] for s in SPIKES])
 def test_spikes(orc, name, R, sl, nq, where, visible, variant):
