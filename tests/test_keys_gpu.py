@@ -204,3 +204,15 @@ def test_keys_prefill_reduced(orc, n, kernel):
     """Prefill rows (2 requests x 96 rows): every row's keys, bit-exact."""
     case = make_config(n, batch=2, rows=96)
     check_keys(orc, case, kernel, what=f"{case.name}-reduced-k{kernel}")
+
+
+@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64, FP8])
+def test_keys_page_table_beyond_lds_cache(orc, kernel):
+    """Requests whose extra page table is longer than a workgroup's LDS cache
+    of it (contexts past 1M tokens): compressed slots resolved through one
+    more round of page-table loads, bit-exact on every variant."""
+    kv = "fp8" if kernel == FP8 else "bf16"
+    case = make_case(seq_lens=[1_200_000, 1_060_000], n_q=[1, 3], H=64, R=4, seed=91, kv=kv)
+    assert case.extra_page_table.shape[1] > 1024
+    log(f"keys beyond the page-table cache kernel={kernel}")
+    check_keys(orc, case, 0 if kernel == FP8 else kernel, what=f"beyond-cache-k{kernel}")
