@@ -216,3 +216,18 @@ def test_keys_page_table_beyond_lds_cache(orc, kernel):
     assert case.extra_page_table.shape[1] > 1024
     log(f"keys beyond the page-table cache kernel={kernel}")
     check_keys(orc, case, 0 if kernel == FP8 else kernel, what=f"beyond-cache-k{kernel}")
+
+
+@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64, FP8])
+@pytest.mark.parametrize("R", [4, 128])
+def test_keys_many_requests(orc, R, kernel):
+    """150 requests: rows past the first 64-request chunk of the
+    row-to-request search, bit-exact key sets on every variant."""
+    kv = "fp8" if kernel == FP8 else "bf16"
+    rng = np.random.default_rng(500 + R)
+    B = 150
+    nq = rng.integers(0, 4, size=B)
+    sl = np.maximum(rng.integers(1, 700, size=B), nq) + (128 if R == 128 else 0)
+    case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=501 + R, kv=kv, n_sel=40)
+    log(f"keys many requests R={R} kernel={kernel}")
+    check_keys(orc, case, 0 if kernel == FP8 else kernel, what=f"many-requests-R{R}-k{kernel}")

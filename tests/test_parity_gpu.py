@@ -318,6 +318,24 @@ def _slot(table, r, x):
     return int(table[r, x // 256]) * 256 + x % 256
 
 
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS, indirect=True)
+@pytest.mark.parametrize("R", [0, 4, 128])
+def test_many_requests(orc, R, variant):
+    """150 requests (more than one 64-request chunk of the row-to-request
+    search), decode and verify rows of ragged lengths, some requests without
+    rows; every row checked on every kernel variant."""
+    _, kv = variant
+    rng = np.random.default_rng(500 + R)
+    B = 150
+    nq = rng.integers(0, 4, size=B)
+    sl = np.maximum(rng.integers(1, 700, size=B), nq) + (128 if R == 128 else 0)
+    case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=501 + R, kv=kv, n_sel=40)
+    log(f"many requests B={B} T={case.T} R={R} kv={kv}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"many requests R{R} {kv}")
+
+
 _BEYOND_CACHE = {}
 
 
