@@ -444,6 +444,37 @@ def bench_topk(args) -> int:
     return 0
 
 
+def plain_read_ms(nbytes: int, reps: int = 50, workgroups: int = 1024) -> float:
+    """Average duration of the library's plain streaming read of `nbytes`
+    bytes (dsv4_read_probe), each call bracketed by its own event pair and all
+    of them queued behind a spin kernel, as the split kernel's durations are;
+    successive calls read disjoint windows of a buffer four times larger than
+    the 256 MB MALL, so that every call reads from HBM."""
+    import torch
+
+    from hybrid_sparse_mqa_amd import dsv4_read_probe
+
+    nbytes = (nbytes + 255) // 256 * 256
+    span = max(4 * nbytes, 1 << 30)
+    buf = torch.ones(span + nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    stride = nbytes + 4096  # no two consecutive windows share a line
+    offsets = [(i * stride) % span // 256 * 256 for i in range(reps)]
+    for o in offsets[:3]:
+        dsv4_read_probe(buf[o:], nbytes, workgroups, sink)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in offsets]
+    torch.cuda._sleep(1 << 24)
+    for (e0, e1), o in zip(evs, offsets):
+        e0.record()
+        dsv4_read_probe(buf[o:], nbytes, workgroups, sink)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+    del buf
+    return ms
+
+
 def bench_stream(args) -> int:
     """Achievable HBM bandwidth on this device, for context beside the 8 TB/s
     peak the roofline fractions use: torch's own kernels reading (a sum over
@@ -475,11 +506,19 @@ def bench_stream(args) -> int:
     read = timed(lambda: torch.sum(x, dim=0, dtype=torch.float32, out=acc), 2 * n)
     write = timed(lambda: y.fill_(1.0), 2 * n)
     copy = timed(lambda: y.copy_(x), 4 * n)
+    del x, y
+    # The library's plain streaming read at a range of sizes: small reads
+    # cannot reach the large-read rate (launch, ramp-up and drain are fixed).
+    probe = {}
+    for nbytes in (1 << 30, 256 << 20, 80 << 20, 24 << 20, 4 << 20):
+        ms = plain_read_ms(nbytes, reps=20 if nbytes >= (256 << 20) else 50)
+        probe[str(nbytes)] = {"us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                              "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     print(json.dumps({
-        "metric": "achievable HBM bandwidth (torch kernels, 1 GiB operands)",
+        "metric": "achievable HBM bandwidth (torch kernels, 1 GiB operands; plain read probe by size)",
         "unit": "GB/s", "read_gbs": read, "write_gbs": write, "copy_gbs": copy,
         "read_frac": read / HBM_PEAK_GBS, "write_frac": write / HBM_PEAK_GBS, "copy_frac": copy / HBM_PEAK_GBS,
-        "peak": HBM_PEAK_GBS, "reps": args.steps,
+        "plain_read_probe": probe, "peak": HBM_PEAK_GBS, "reps": args.steps,
     }), flush=True)
     return 0
 
@@ -772,6 +811,15 @@ def main() -> int:
         }),
         "cpu_baseline": None,
     }
+    if not mfma_bound:
+        # Context, not the roofline: the same bytes read by a plain streaming
+        # kernel (no metadata, no arithmetic, no stores), timed the same way.
+        pr_ms = plain_read_ms(kernel_bytes)
+        result["roofline"]["plain_read_same_bytes"] = {
+            "us": pr_ms * 1e3, "gbs": kernel_bytes / (pr_ms * 1e-3) / 1e9,
+            "frac": kernel_bytes / (pr_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "split_kernel_vs_plain_read": pr_ms / split_avg_ms,
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)

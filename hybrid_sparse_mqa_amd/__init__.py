@@ -22,5 +22,6 @@ from .api import (  # noqa: F401
     dsv4_attn_workspace_release,
     dsv4_attn_workspace_reserve,
     dsv4_last_error,
+    dsv4_read_probe,
 )
 from ._native import Dsv4Error, LIB_PATH  # noqa: F401

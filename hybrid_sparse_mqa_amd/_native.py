@@ -85,6 +85,8 @@ def load() -> ctypes.CDLL:
         L.dsv4_attn_timing_read.restype = ctypes.c_int
         L.dsv4_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_int64)]
+        L.dsv4_read_probe.restype = ctypes.c_int
+        L.dsv4_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.dsv4_attn_debug_keys.restype = ctypes.c_int
         L.dsv4_attn_debug_keys.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64]
         _lib = L

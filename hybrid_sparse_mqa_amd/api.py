@@ -178,3 +178,16 @@ def dsv4_attn_timing_read() -> Tuple[float, float, int]:
     n = ctypes.c_int64()
     N.check(N.load().dsv4_attn_timing_read(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)))
     return a.value, b.value, n.value
+
+
+def dsv4_read_probe(buf: torch.Tensor, nbytes: int, workgroups: int, sink: torch.Tensor,
+                    stream: Optional[int] = None) -> None:
+    """Plain streaming read of the first ``nbytes`` bytes of ``buf`` (timing helper)."""
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if sink.numel() * sink.element_size() < 16:
+        raise ValueError("sink must hold 16 bytes")
+    N.check(N.load().dsv4_read_probe(ctypes.c_void_p(buf.data_ptr()), int(nbytes), int(workgroups),
+                                     ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(N.stream_handle(buf.device) if stream is None else stream)))
+

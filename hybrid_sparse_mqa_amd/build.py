@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdsv4_attn.so")
-SOURCES = ["dsv4_attn_kernels.hip", "dsv4_pack.hip", "dsv4_topk.hip", "dsv4_api.cpp"]
+SOURCES = ["dsv4_attn_kernels.hip", "dsv4_pack.hip", "dsv4_topk.hip", "dsv4_probe.hip", "dsv4_api.cpp"]
 ARCH = os.environ.get("DSV4_OFFLOAD_ARCH", "gfx950")
 # Per-source flags.  The top-k kernels issue their list-offset atomic from one
 # thread and use its result later; the compiler's atomic combining (a wave

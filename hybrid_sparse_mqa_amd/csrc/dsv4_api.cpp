@@ -16,6 +16,7 @@
 
 #include "../../include/dsv4_attn.h"
 #include "dsv4_launch.h"
+#include "dsv4_probe.h"
 
 using namespace dsv4;
 
@@ -587,6 +588,17 @@ dsv4_status dsv4_attn_timing_read(double* split_ms, double* merge_ms, int64_t* c
     g_timing_recs.clear();
     if (split_ms) *split_ms = a;
     if (merge_ms) *merge_ms = b;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_read_probe(const void* buf, int64_t bytes, int32_t workgroups, void* sink, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return fail(DSV4_ERR_INVALID, "bytes must be a nonnegative multiple of 16, got %lld", (long long)bytes);
+    if (workgroups < 1 || workgroups > (1 << 20))
+        return fail(DSV4_ERR_INVALID, "workgroups must be 1 .. 2^20, got %d", workgroups);
+    if (bytes == 0) return DSV4_OK;
+    if (buf == nullptr || !aligned16(buf)) return fail(DSV4_ERR_INVALID, "buf must be a 16-byte aligned device pointer");
+    if (sink == nullptr || !aligned16(sink)) return fail(DSV4_ERR_INVALID, "sink must be a 16-byte aligned device pointer");
+    DSV4_HIP(launch_read_probe(buf, bytes, workgroups, sink, (hipStream_t)stream));
     return DSV4_OK;
 }
 

@@ -322,6 +322,22 @@ dsv4_status dsv4_attn_timing_enable(int32_t enable);
 dsv4_status dsv4_attn_timing_read(double* split_ms, double* merge_ms, int64_t* calls);
 
 /*
+ * Timing helper, not part of the attention: a plain streaming read of
+ * `bytes` bytes of device memory at `buf`, launched on `stream`, for
+ * measuring how fast this device reads a given number of bytes with nothing
+ * else to do (no metadata to resolve, no arithmetic, no stores) -- the
+ * yardstick beside the attention kernels' own rates.  `workgroups`
+ * workgroups of 256 threads each read one contiguous share with 16-byte
+ * non-temporal loads.  `sink` (device memory, 16 bytes) receives a store
+ * only if the folded bytes equal one fixed 128-bit constant (it exists so
+ * that the loads are kept); the caller owns both buffers.  Errors:
+ * DSV4_ERR_INVALID for bytes negative or not a multiple of 16, workgroups
+ * outside 1 .. 2^20, or a null or unaligned buf / sink (bytes = 0 launches
+ * nothing); DSV4_ERR_HIP if the launch fails.
+ */
+dsv4_status dsv4_read_probe(const void* buf, int64_t bytes, int32_t workgroups, void* sink, void* stream);
+
+/*
  * Test hook, not for production calls: record the KV rows the split kernels
  * read.  While `keys` is non-NULL, dsv4_attn_forward launches the recording
  * build of its split kernel (the same source, plus stores of what it

@@ -184,6 +184,23 @@ def test_c4_topk_argument_errors():
     assert call(desc(N.DSV4_F32, [0, 1000]), desc(N.DSV4_I32, [0]), desc(N.DSV4_I32, [0, 512])) == 0
 
 
+def test_read_probe_argument_errors():
+    L = N.load()
+
+    def call(buf, nbytes, wgs, sink):
+        return L.dsv4_read_probe(ctypes.c_void_p(buf), nbytes, wgs, ctypes.c_void_p(sink), None)
+
+    assert call(FAKE, 1000, 256, FAKE) == INVALID  # not a multiple of 16
+    assert call(FAKE, -16, 256, FAKE) == INVALID
+    assert call(FAKE, 1 << 20, 0, FAKE) == INVALID
+    assert call(FAKE, 1 << 20, (1 << 20) + 1, FAKE) == INVALID
+    assert call(None, 1 << 20, 256, FAKE) == INVALID
+    assert call(FAKE + 8, 1 << 20, 256, FAKE) == INVALID
+    assert call(FAKE, 1 << 20, 256, None) == INVALID
+    assert call(FAKE, 1 << 20, 256, FAKE + 4) == INVALID
+    assert call(None, 0, 256, None) == OK  # nothing to read: nothing launched
+
+
 def test_plan_is_host_only_and_sane():
     L = N.load()
     s = ctypes.c_int32()

@@ -24,7 +24,7 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(ROOT, "hybrid_sparse_mqa_amd", "csrc")
-KERNEL_OBJS = [os.path.join(CSRC, f + ".o") for f in ("dsv4_attn_kernels.hip", "dsv4_pack.hip", "dsv4_topk.hip")]
+KERNEL_OBJS = [os.path.join(CSRC, f + ".o") for f in ("dsv4_attn_kernels.hip", "dsv4_pack.hip", "dsv4_topk.hip", "dsv4_probe.hip")]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
