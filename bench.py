@@ -54,7 +54,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_mqa_amd", "csrc", f)
 # workgroup)
 SPLIT_KERNELS = {1: ("attn_narrow_kernel<false>", 16), 2: ("attn_wide_kernel<1, false>", 32),
                  3: ("attn_ws_kernel<1, false>", 32), 4: ("attn_wide_kernel<2, false>", 64),
-                 5: ("attn_fp8_kernel<false>", 64)}
+                 5: ("attn_fp8_kernel<2, false>", 64), 6: ("attn_fp8_kernel<1, false>", 32)}
 
 
 def split_kernel_name(kernel: int) -> str:

@@ -203,7 +203,7 @@ constexpr int kTopkMaxRowsSplit = 65535;  // rows of a long-row top-k call (grid
 std::mutex g_mu;
 std::vector<DeviceState> g_dev;
 int32_t g_force_split_keys = 0;
-int32_t g_force_kernel = DSV4_KERNEL_AUTO;  // bf16 pools only
+int32_t g_force_kernel = DSV4_KERNEL_AUTO;  // 1..4 apply to bf16 pools, 5..6 to FP8 pools
 // Test hook: key recording (dsv4_attn_debug_keys).
 uint64_t* g_dbg_keys = nullptr;
 int64_t g_dbg_keys_cap = 0;
@@ -280,8 +280,20 @@ dsv4_status ensure_workspace(DeviceState* d, size_t bytes, hipStream_t st) {
     return DSV4_OK;
 }
 
-// Kernel layout: FP8 pools -> the FP8 kernel; otherwise the variant forced
-// by dsv4_attn_set_kernel, else the 16-head kernel for at most 16 heads (no
+void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int32_t* splits, int32_t* chunk);
+
+// Kernel layout.  FP8 pools: the FP8 variant forced by dsv4_attn_set_kernel,
+// else the 32-head one when there are at most 32 heads, or when its whole
+// grid (rows x head blocks x its splits) fits the compute units once with at
+// most kFp8H32MaxTiles tiles per split: with few rows the 64-head grid leaves
+// compute units idle, and halving each workgroup's heads halves its products
+// and operand decodes per tile, which is most of its loop; else the 64-head
+// one, which loads each tile once for all 64 heads.  Measured on MI355X (C4
+// decode at 1M tokens, 640 keys per row, per step, 64-head vs 32-head):
+// 8 rows 16.8 vs 14.5 us (10 splits each), 16 rows 18.3 vs 16.4 (10 / 7
+// splits), 24 rows 20.7 vs 19.1 (10 / 5), 32 rows 21.3 vs 20.5 (7 / 4),
+// 64 rows 27.3 vs 29.3 (4 / 2 splits: the 32-head splits hold 10 tiles).
+// bf16 pools: the variant forced by dsv4_attn_set_kernel, else the 16-head kernel for at most 16 heads (no
 // padding of heads); above that the 64-head kernel when the rows alone give
 // every compute unit at least two 64-head workgroups (prefill / extend:
 // compute-bound, and a 64-head tile does twice the MFMA work per LDS tile
@@ -291,8 +303,16 @@ dsv4_status ensure_workspace(DeviceState* d, size_t bytes, hipStream_t st) {
 // roles fastest -- C4 decode 32 rows 16.8 vs 17.1 us (32-head dim split),
 // C128 decode 64 rows 30.9 vs 33.2 us (64-head), C4 verify 128 rows 28.6 vs
 // 31.0 us.
-Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8) {
-    if (fp8) return Layout::kFp8;
+Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8, int64_t nmax) {
+    if (fp8) {
+        if (g_force_kernel == DSV4_KERNEL_FP8) return Layout::kFp8;
+        if (g_force_kernel == DSV4_KERNEL_FP8_H32 || H <= kWide32HeadsPerBlock) return Layout::kFp8H32;
+        constexpr int kFp8H32MaxTiles = 6;
+        int32_t s = 1, c = 0;
+        plan_splits(cus, T, H, nmax, Layout::kFp8H32, &s, &c);
+        const int64_t items = (int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) * s;
+        return items <= cus && c <= kFp8H32MaxTiles * kTileKeys ? Layout::kFp8H32 : Layout::kFp8;
+    }
     switch (g_force_kernel) {
         case DSV4_KERNEL_H16: return Layout::kNarrow;
         case DSV4_KERNEL_H32: return Layout::kWide32;
@@ -309,7 +329,8 @@ Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8) {
 int32_t heads_per_block(Layout layout) {
     switch (layout) {
         case Layout::kWide32:
-        case Layout::kRoles32: return kWide32HeadsPerBlock;
+        case Layout::kRoles32:
+        case Layout::kFp8H32: return kWide32HeadsPerBlock;
         case Layout::kNarrow: return kNarrowHeadsPerBlock;
         default: return kWideHeadsPerBlock;
     }
@@ -321,6 +342,7 @@ int32_t kernel_id(Layout layout) {
         case Layout::kWide32: return DSV4_KERNEL_H32;
         case Layout::kRoles32: return DSV4_KERNEL_H32_ROLES;
         case Layout::kWide: return DSV4_KERNEL_H64;
+        case Layout::kFp8H32: return DSV4_KERNEL_FP8_H32;
         default: return DSV4_KERNEL_FP8;
     }
 }
@@ -337,7 +359,7 @@ int32_t max_split_keys(Layout layout) { return layout == Layout::kNarrow ? kNarr
 // 20 splits of 32 keys 17.9 us, 10 of 64 17.0 us, 7 of 96 17.9 us; the
 // shorter splits' extra partials and merge outweigh their shorter loop.)
 void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int32_t* splits, int32_t* chunk) {
-    const bool fp8 = layout == Layout::kFp8;
+    const bool fp8 = layout == Layout::kFp8 || layout == Layout::kFp8H32;
     const int64_t hpb = heads_per_block(layout);
     const int64_t head_blocks = (H + hpb - 1) / hpb;
     int64_t c;
@@ -494,9 +516,8 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split) {
 }
 
 dsv4_status dsv4_attn_set_kernel(int32_t kernel) {
-    if (kernel != DSV4_KERNEL_AUTO && kernel != DSV4_KERNEL_H16 && kernel != DSV4_KERNEL_H32 &&
-        kernel != DSV4_KERNEL_H32_ROLES && kernel != DSV4_KERNEL_H64)
-        return fail(DSV4_ERR_INVALID, "kernel must be DSV4_KERNEL_AUTO or one of the bf16 kernels (1..4), got %d",
+    if (kernel < DSV4_KERNEL_AUTO || kernel > DSV4_KERNEL_FP8_H32)
+        return fail(DSV4_ERR_INVALID, "kernel must be DSV4_KERNEL_AUTO (0) or a split-kernel variant (1..6), got %d",
                     kernel);
     std::lock_guard<std::mutex> lk(g_mu);
     g_force_kernel = kernel;
@@ -518,9 +539,9 @@ dsv4_status dsv4_attn_plan(int32_t num_rows, int32_t num_heads, int32_t compress
         DeviceState* d = device_state(dev);
         if (d) cus = d->cus;
     }
-    const Layout layout = choose_layout(num_rows, num_heads, cus, kv_fp8 != 0);
-    plan_splits(cus, num_rows, num_heads, (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages),
-                layout, splits, keys_per_split);
+    const int64_t nmax = (int64_t)window + extra_bound(compress_ratio, c4_width, extra_pages);
+    const Layout layout = choose_layout(num_rows, num_heads, cus, kv_fp8 != 0, nmax);
+    plan_splits(cus, num_rows, num_heads, nmax, layout, splits, keys_per_split);
     if (kernel != nullptr) *kernel = kernel_id(layout);
     return DSV4_OK;
 }
@@ -782,9 +803,9 @@ dsv4_status forward_impl(const dsv4_tensor* q, const dsv4_tensor* swa_pool, cons
     a.T = (int32_t)T;
     a.H = (int32_t)H;
     a.scale_log2 = scale * 1.4426950408889634f;
-    const Layout layout = choose_layout(a.T, a.H, d->cus, swa.fp8);
-    plan_splits(d->cus, a.T, a.H, (int64_t)window + extra_bound(md.R, md.K, md.P_extra), layout, &a.splits,
-                &a.chunk);
+    const int64_t nmax = (int64_t)window + extra_bound(md.R, md.K, md.P_extra);
+    const Layout layout = choose_layout(a.T, a.H, d->cus, swa.fp8, nmax);
+    plan_splits(d->cus, a.T, a.H, nmax, layout, &a.splits, &a.chunk);
     a.head_blocks = (int32_t)((H + heads_per_block(layout) - 1) / heads_per_block(layout));
     a.ext_pages = md.P_extra;
     const int64_t n_items = (int64_t)a.T * a.head_blocks * a.splits;

@@ -458,6 +458,27 @@ __device__ __forceinline__ void exchange_partial(float* s_sx, int w, int l, f32x
     }
 }
 
+// The same over the four waves that share all 32 heads (each holding one
+// dim quarter), added pairwise -- (own + w^1) + (w^2 + w^3) -- so that every
+// wave gets the same sums (each addition is commutative).
+__device__ __forceinline__ void exchange_partial4(float* s_sx, int w, int l, f32x16& sacc) {
+    f32x4* mine = (f32x4*)s_sx + w * 256 + l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+    __syncthreads();
+    f32x4 o[3][4];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) {
+        const f32x4* other = (const f32x4*)s_sx + (w ^ v) * 256 + l;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[v - 1][q] = other[64 * q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[4 * q + j] = (sacc[4 * q + j] + o[0][q][j]) + (o[1][q][j] + o[2][q][j]);
+}
+
 // Multiply every output accumulator by alpha in place.  Each register is
 // read out of the accumulation file, scaled and written back by one short
 // asm sequence, so the accumulators never have to live in VGPRs (letting the
@@ -520,10 +541,10 @@ __device__ __forceinline__ void scale_accumulators(f32x4 (&oacc)[NB], float alph
 // exchange).  l_run is this lane's share of the denominator (its 16 keys per
 // tile); the two shares are added once, in write_result.  A tile whose 32
 // keys are all valid skips the masking.
-template <bool kFp8>
+template <bool kFp8, int NB>
 __device__ __forceinline__ void softmax_tile(const f32x16& s_all, uint64_t vmask, float scale_log2, int l,
                                              const float (&sc_key)[16], float& m_run, float& l_run,
-                                             f32x16 (&oacc)[8], bf16x8 (&pb)[2], bf16x8 (&pbs)[2]) {
+                                             f32x16 (&oacc)[NB], bf16x8 (&pb)[2], bf16x8 (&pbs)[2]) {
     float sv[16];
     float tmax = -INFINITY;
     if ((uint32_t)vmask == 0xFFFFFFFFu) {
@@ -1943,8 +1964,14 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Packed FP8 KV: 64-head workgroups, wave (hh, dh) owning heads 32hh .. +31
-// and dims 256dh .. +255 of both products.  The raw records stream into a
+// Packed FP8 KV, two layouts (kHH = head groups of 32 per workgroup):
+//  - kHH = 2: 64-head workgroups, wave (hh, dq) owning heads 32hh .. +31 and
+//    dims 256dq .. +255 of both products; the two dim halves of a head group
+//    add their score partials;
+//  - kHH = 1: 32-head workgroups, wave dq owning all 32 heads and dims
+//    128dq .. +127; the four dim quarters add their score partials.  Half the
+//    products and operand decodes per wave and tile, for batches whose
+//    64-head grid leaves compute units idle.  The raw records stream into a
 // 4-stage LDS ring with direct global->LDS copies, three tiles ahead, and
 // both MFMA operands are decoded straight from the ring into registers:
 //  - S^T = K.Q^T: lane l reads 8 codes of key l & 31 (one 8-byte read per
@@ -1959,6 +1986,8 @@ __global__ __launch_bounds__(256, 1) void attn_narrow_kernel(AttnArgs a) {
 //    read 8 keys on gives elements 4..7).  P^T's element e of lane half h
 //    in k-step pp is tile key 16 pp + 4 h + (e % 4) + 8 (e / 4), the order
 //    of the score tile's MFMA output rows.
+// (The descriptions below use the 64-head layout's 256-dim slices; the
+// 32-head layout's 128-dim slices are the same with 128 in place of 256.)
 // The per-token scale multiplies the fp32 non-rotary score partial and is
 // folded into P for the non-rotary PV product, so the decode adds no
 // rounding.  Two barriers per tile: one when the tile has landed, one in
@@ -2003,8 +2032,13 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                                             e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
 }
 
-template <bool kDbg>
+template <int kHH, bool kDbg>
 __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
+    constexpr int kDims = 128 * kHH;   // head dims per wave (a dim slice)
+    constexpr int kSteps = kDims / 16;  // score k-steps per wave and tile
+    constexpr int kMb = kDims / 32;     // PV dim blocks per wave
+    constexpr int kHeads = 32 * kHH;    // heads per workgroup
+    static_assert(kHH == 1 || kHH == 2, "one or two 32-head groups");
     __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kFp8Stages][kFp8RawStage];
     __shared__ __attribute__((aligned(16))) float s_rsc[kFp8Stages][kTileKeys];
     __shared__ __attribute__((aligned(16))) float s_sx[4 * 64 * 16];
@@ -2020,23 +2054,24 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     if (!decode_item(a, it)) return;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int hh = w >> 1, dh = w & 1;
+    const int hh = kHH == 2 ? w >> 1 : 0;  // head group
+    const int dq = kHH == 2 ? w & 1 : w;   // dim slice
 
     // The request bounds first (the first wait, for them, leaves every later
     // load in flight), then the slot list's loads that do not need them,
     // then Q^T as the B operand of the scores (lane: head 32hh + (l & 31),
-    // dims 256dh + 16j + 8(l >> 5) .. +8 of k-step j; heads past H read head
-    // H-1, whose results are never written).
+    // dims kDims*dq + 16j + 8(l >> 5) .. +8 of k-step j; heads past H read
+    // head H-1, whose results are never written).
     const RequestChunk rc = load_requests(a.m, 0, l);
     const int k0 = it.s * a.chunk;
     SlotPrefetch pf;
     prefetch_slots(a, it.t, k0, tid, pf);
-    bf16x8 qf[16];
+    bf16x8 qf[kSteps];
     {
-        const int head = min(it.hb * kWideHeadsPerBlock + 32 * hh + (l & 31), a.H - 1);
-        const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1 + 256 * dh + 8 * (l >> 5);
+        const int head = min(it.hb * kHeads + 32 * hh + (l & 31), a.H - 1);
+        const uint16_t* qrow = a.q + (int64_t)it.t * a.q_s0 + (int64_t)head * a.q_s1 + kDims * dq + 8 * (l >> 5);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
+        for (int j = 0; j < kSteps; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j));
     }
 
     const RowKeys rk = row_keys_from(a.m, it.t, l, rc);
@@ -2097,9 +2132,9 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
         return __ballot(used);
     };
 
-    f32x16 oacc[8];
+    f32x16 oacc[kMb];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x16{};
+    for (int mb = 0; mb < kMb; ++mb) oacc[mb] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
     // Q and the slot list have arrived (the compiler waited for the window
@@ -2115,8 +2150,8 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
     // Per-lane constants of the operand reads.
     const int key_s = l & 31;                      // score operand: this lane's key
     const int g = l >> 4, gi = l & 15;             // transposing reads: 16-lane group, lane in it
-    // One instance of the loop per dim half (kD = dh): a branch on dh inside
-    // the loop made the compiler copy all 128 accumulators on every tile.
+    // One instance of the loop per dim slice (kD = dq): a branch on dq inside
+    // the loop made the compiler copy all the accumulators on every tile.
     auto tile_loop = [&](auto d_tag) __attribute__((always_inline)) {
         for (int j = 0; j < n_tiles; ++j) {
             // This wave's copies of tile j (those of j+1 and j+2 may still be in
@@ -2132,23 +2167,25 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             vm2 = j + kFp8Stages - 1 < n_tiles ? issue_tile(j + kFp8Stages - 1) : 0;
             const uint8_t* stage = &s_raw[j % kFp8Stages][0];
 
-            // S^T partial over this wave's 256 dims: the non-rotary k-steps
-            // (dims < 448) and the rotary ones (dh = 1, k-steps 12..15)
-            // accumulate apart; the non-rotary partial is scaled per key.  The
-            // two dim halves are separate instances (kD), so that every operand
-            // is a fixed register.
+            // S^T partial over this wave's kDims dims: the non-rotary k-steps
+            // (dims < 448) and the rotary ones (the last slice's last four
+            // k-steps) accumulate apart; the non-rotary partial is scaled per
+            // key.  The dim slices are separate instances (kD), so that every
+            // operand is a fixed register.
             f32x16 sacc = f32x16{};
             float sc_key[16];
             auto scores = [&](auto d_tag) __attribute__((always_inline)) {
                 constexpr int kD = decltype(d_tag)::value;
-                constexpr int kNopeSteps = kD == 0 ? 16 : 12;
-                const uint8_t* rec = stage + key_s * kFp8RecSlot + 256 * kD + 8 * (l >> 5);
+                constexpr int kLo = kDims * kD;  // the slice's first dim (every slice starts below 448)
+                constexpr int kNopeSteps = (kNope - kLo) / 16 < kSteps ? (kNope - kLo) / 16 : kSteps;
+                static_assert(kLo < kNope && (kNope - kLo) % 16 == 0, "slices start at non-rotary dims");
+                const uint8_t* rec = stage + key_s * kFp8RecSlot + kLo + 8 * (l >> 5);
                 u32x2 cn[kNopeSteps];
-                u32x4 cr[16 - kNopeSteps + 1];
+                u32x4 cr[kSteps - kNopeSteps + 1];
     #pragma unroll
                 for (int jj = 0; jj < kNopeSteps; ++jj) cn[jj] = *(const u32x2*)(rec + 16 * jj);
     #pragma unroll
-                for (int q = 0; q < 16 - kNopeSteps; ++q) {  // bf16 dims 448 + 16q + 8(l >> 5) .. +8
+                for (int q = 0; q < kSteps - kNopeSteps; ++q) {  // bf16 dims 448 + 16q + 8(l >> 5) .. +8
                     cr[q] = *(const u32x4*)(stage + key_s * kFp8RecSlot + kNope + 32 * q + 16 * (l >> 5));
                 }
                 // Every read in flight before the first product (left alone, the
@@ -2160,7 +2197,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
                 for (int jj = 0; jj < kNopeSteps; ++jj)
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_to_bf16x8(cn[jj][0], cn[jj][1]), qf[jj], sacc, 0, 0, 0);
     #pragma unroll
-                for (int q = 0; q < 16 - kNopeSteps; ++q)
+                for (int q = 0; q < kSteps - kNopeSteps; ++q)
                     sacc_r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cr[q]), qf[kNopeSteps + q], sacc_r, 0, 0, 0);
     #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
@@ -2173,12 +2210,13 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
                 }
             };
             scores(d_tag);
-            exchange_partial(s_sx, w, l, sacc);
+            if constexpr (kHH == 2) exchange_partial(s_sx, w, l, sacc);
+            else exchange_partial4(s_sx, w, l, sacc);
 
             bf16x8 pb[2], pbs[2];
             softmax_tile<true>(sacc, vmask, a.scale_log2, l, sc_key, m_run, l_run, oacc, pb, pbs);
 
-            // O^T += K^T . P^T: lane l holds dim 256dh + 32mb + (l & 31) of the
+            // O^T += K^T . P^T: lane l holds dim kDims*dq + 32mb + (l & 31) of the
             // eight keys 16pp + 4h + {0..3, 8..11}, h = l >> 5, in the order in
             // which P^T holds them (the score tile's MFMA output layout: lane
             // half h holds keys 8q + 4h + {0..3} in registers 4q .. 4q+3); the
@@ -2186,24 +2224,26 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             // All operand reads go out before the products.
             auto pv = [&](auto d_tag) __attribute__((always_inline)) {
                 constexpr int kD = decltype(d_tag)::value;
-                constexpr int kNopeMb = kD == 0 ? 8 : 6;  // dim blocks below 448
+                constexpr int kLo = kDims * kD;
+                constexpr int kNopeMb = (kNope - kLo) / 32 < kMb ? (kNope - kLo) / 32 : kMb;  // dim blocks below 448
+                static_assert((kNope - kLo) % 32 == 0, "dim blocks do not straddle the rotary boundary");
                 i32x2 c8[2 * kNopeMb];
-                bf16x4 c16[2 * (8 - kNopeMb) + 1][2];  // (+1: no zero-length array for kD = 0)
+                bf16x4 c16[2 * (kMb - kNopeMb) + 1][2];  // (+1: no zero-length array for an all-FP8 slice)
     #pragma unroll
                 for (int mb = 0; mb < kNopeMb; ++mb)
     #pragma unroll
                     for (int pp = 0; pp < 2; ++pp) {
-                        const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
+                        const int dim_base = kLo + 32 * mb + 16 * (g & 1);
                         const int js = gi >> 1;  // the key this source lane addresses: element js of the operand
                         const int key = 16 * pp + 4 * (g >> 1) + (js & 3) + 8 * (js >> 2);
                         const uint8_t* p0 = stage + key * kFp8RecSlot + dim_base + 8 * (gi & 1);
                         c8[2 * mb + pp] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)lds_addr(p0));
                     }
     #pragma unroll
-                for (int mb = kNopeMb; mb < 8; ++mb)
+                for (int mb = kNopeMb; mb < kMb; ++mb)
     #pragma unroll
                     for (int pp = 0; pp < 2; ++pp) {
-                        const int dim_base = 256 * kD + 32 * mb + 16 * (g & 1);
+                        const int dim_base = kLo + 32 * mb + 16 * (g & 1);
                         const int key = 16 * pp + 4 * (g >> 1) + (gi >> 2);  // elements 0..3; 4..7 are 8 keys on
                         const uint8_t* p0 = stage + key * kFp8RecSlot + kNope + 2 * (dim_base - kNope + 4 * (gi & 3));
                         c16[2 * (mb - kNopeMb) + pp][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)lds_addr(p0));
@@ -2218,7 +2258,7 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
                         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             e4m3x8_to_bf16x8((uint32_t)c8[2 * mb + pp][0], (uint32_t)c8[2 * mb + pp][1]), pbs[pp], oacc[mb], 0, 0, 0);
     #pragma unroll
-                for (int mb = kNopeMb; mb < 8; ++mb)
+                for (int mb = kNopeMb; mb < kMb; ++mb)
     #pragma unroll
                     for (int pp = 0; pp < 2; ++pp) {
                         const bf16x4 lo = c16[2 * (mb - kNopeMb) + pp][0], hi = c16[2 * (mb - kNopeMb) + pp][1];
@@ -2229,9 +2269,13 @@ __global__ __launch_bounds__(256, 1) void attn_fp8_kernel(AttnArgs a) {
             pv(d_tag);
         }
     };
-    if (dh == 0) tile_loop(std::integral_constant<int, 0>{});
-    else tile_loop(std::integral_constant<int, 1>{});
-    write_result<2>(a, it, hh, dh, l, oacc, m_run, l_run, &s_raw[0][0], &s_raw[0][0] + 32 * 1024);
+    if (dq == 0) tile_loop(std::integral_constant<int, 0>{});
+    else if (dq == 1) tile_loop(std::integral_constant<int, 1>{});
+    else if constexpr (kHH == 1) {
+        if (dq == 2) tile_loop(std::integral_constant<int, 2>{});
+        else tile_loop(std::integral_constant<int, 3>{});
+    }
+    write_result<kHH>(a, it, hh, dq, l, oacc, m_run, l_run, &s_raw[0][0], &s_raw[0][0] + 32 * 1024);
 }
 
 // ---------------------------------------------------------------------------
@@ -2338,7 +2382,10 @@ template <bool kDbg>
 void launch_split(const AttnArgs& a, Layout layout, dim3 grid, hipStream_t stream) {
     switch (layout) {
         case Layout::kFp8:
-            hipLaunchKernelGGL(attn_fp8_kernel<kDbg>, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fp8_kernel<2, kDbg>), grid, dim3(256), 0, stream, a);
+            break;
+        case Layout::kFp8H32:
+            hipLaunchKernelGGL(HIP_KERNEL_NAME(attn_fp8_kernel<1, kDbg>), grid, dim3(256), 0, stream, a);
             break;
         case Layout::kWide:
             hipLaunchKernelGGL((attn_wide_kernel<2, kDbg>), grid, dim3(256), 0, stream, a);

@@ -21,7 +21,7 @@ constexpr int kNarrowMaxSplitKeys = 2048; // keys one narrow workgroup may own
 // into two head groups x two dim halves), bf16 with 32 heads per workgroup
 // (four dim quarters), bf16 with 16 heads per workgroup (four independent
 // waves), or packed FP8 (64 heads per workgroup).
-enum class Layout { kWide, kWide32, kRoles32, kNarrow, kFp8 };
+enum class Layout { kWide, kWide32, kRoles32, kNarrow, kFp8, kFp8H32 };
 constexpr int kTableCap = 1024;      // extra page-table entries a workgroup caches in LDS
 constexpr int kStages = 4;           // bf16 key tiles resident in LDS
 

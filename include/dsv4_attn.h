@@ -271,8 +271,11 @@ dsv4_status dsv4_attn_set_split_keys(int32_t keys_per_split);
  *                          softmax (one dim half each), two accumulate P.V
  *                          (one dim half each);
  *   DSV4_KERNEL_H64        64 heads, two head groups x two dim halves;
- *   DSV4_KERNEL_FP8        64 heads on packed FP8 pools (the only variant for
- *                          that format).
+ *   DSV4_KERNEL_FP8        packed FP8 pools: 64 heads, two head groups x two
+ *                          dim halves;
+ *   DSV4_KERNEL_FP8_H32    packed FP8 pools: 32 heads, each wave one quarter
+ *                          of the head dims.
+ * bf16 pools run one of the first four, packed FP8 pools one of the last two.
  */
 enum {
     DSV4_KERNEL_AUTO = 0,
@@ -280,21 +283,24 @@ enum {
     DSV4_KERNEL_H32 = 2,
     DSV4_KERNEL_H32_ROLES = 3,
     DSV4_KERNEL_H64 = 4,
-    DSV4_KERNEL_FP8 = 5
+    DSV4_KERNEL_FP8 = 5,
+    DSV4_KERNEL_FP8_H32 = 6
 };
 
 /*
- * Tuning / test hook: force the bf16 split-kernel variant (DSV4_KERNEL_H16 ..
- * DSV4_KERNEL_H64), or DSV4_KERNEL_AUTO for the automatic choice.  Packed FP8
- * pools always use DSV4_KERNEL_FP8.  Any other value returns
- * DSV4_ERR_INVALID.  Process-wide.
+ * Tuning / test hook: force a split-kernel variant, or DSV4_KERNEL_AUTO for
+ * the automatic choice.  A forced bf16 variant (DSV4_KERNEL_H16 ..
+ * DSV4_KERNEL_H64) applies to calls on bf16 pools only, a forced FP8 variant
+ * (DSV4_KERNEL_FP8, DSV4_KERNEL_FP8_H32) to calls on packed FP8 pools only;
+ * calls on the other format keep their automatic choice.  Any other value
+ * returns DSV4_ERR_INVALID.  Process-wide.
  */
 dsv4_status dsv4_attn_set_kernel(int32_t kernel);
 
 /*
  * Plan that dsv4_attn_forward would use for these sizes: number of key
  * splits per (row, head block), keys per split, and the split-kernel variant
- * (DSV4_KERNEL_*; its heads per workgroup are 16, 32, 32, 64 or 64).  kv_fp8
+ * (DSV4_KERNEL_*; its heads per workgroup are 16, 32, 32, 64, 64 or 32).  kv_fp8
  * is nonzero for packed FP8 pools (the two formats run different kernels and
  * are planned differently).  kernel may be NULL.  Host-only, no device
  * access.

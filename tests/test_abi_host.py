@@ -231,14 +231,32 @@ def test_plan_is_host_only_and_sane():
     # 64 rows x two 32-head blocks fill the chip with two splits: the role kernel
     assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 3 and s.value == 2
+    # packed FP8, 8 rows: the 32-head grid (8 x 2 x 10 splits) fits 256 compute units once
     assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
-    assert k.value == 5  # packed FP8 always runs the FP8 kernel
+    assert k.value == 6 and 8 * 2 * s.value <= 256
+    # packed FP8, 256 rows: the 64-head kernel
+    assert L.dsv4_attn_plan(256, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 5
+    # packed FP8, 32 rows: the 32-head grid fits once with 5 tiles per split; 64 rows: 10 tiles, the 64-head kernel
+    assert L.dsv4_attn_plan(32, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 6 and c.value <= 192
+    assert L.dsv4_attn_plan(64, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 5
+    # packed FP8 with at most 32 heads: always the 32-head kernel
+    assert L.dsv4_attn_plan(256, 32, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 6
     for forced in (1, 2, 3, 4):
         assert L.dsv4_attn_set_kernel(forced) == 0
         assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
         assert k.value == forced
+        assert L.dsv4_attn_plan(256, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+        assert k.value == 5  # FP8 pools ignore a forced bf16 variant
+    for forced in (5, 6):
+        assert L.dsv4_attn_set_kernel(forced) == 0
         assert L.dsv4_attn_plan(8, 64, 4, 128, 512, 1024, 1, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
-        assert k.value == 5  # FP8 pools ignore the forced bf16 variant
-    for bad in (5, 6, -1, 32):
+        assert k.value == forced
+        assert L.dsv4_attn_plan(64, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+        assert k.value == 3  # bf16 pools ignore a forced FP8 variant
+    for bad in (7, -1, 32):
         assert L.dsv4_attn_set_kernel(bad) == INVALID
     assert L.dsv4_attn_set_kernel(0) == 0

@@ -33,10 +33,11 @@ pytestmark = [pytest.mark.gpu,
 
 SENTINEL = 0x5A5A5A5A5A5A5A5A
 MASK_SENTINEL = 0xA5A5A5A5
-H16, H32, ROLES, H64, FP8 = 1, 2, 3, 4, 5
-TILE = {H16: 16, H32: 32, ROLES: 32, H64: 32, FP8: 32}
-HEADS = {H16: 16, H32: 32, ROLES: 32, H64: 64, FP8: 64}
-COMPRESSED_FIRST = {H16: False, H32: True, ROLES: True, H64: True, FP8: True}
+H16, H32, ROLES, H64, FP8, FP8_H32 = 1, 2, 3, 4, 5, 6
+FP8_KERNELS = (FP8, FP8_H32)
+TILE = {H16: 16, H32: 32, ROLES: 32, H64: 32, FP8: 32, FP8_H32: 32}
+HEADS = {H16: 16, H32: 32, ROLES: 32, H64: 64, FP8: 64, FP8_H32: 32}
+COMPRESSED_FIRST = {H16: False, H32: True, ROLES: True, H64: True, FP8: True, FP8_H32: True}
 MASKED = {H32, ROLES, H64}
 
 
@@ -57,7 +58,8 @@ def record(case, kernel=0, split_keys=0, g=None):
                                        dsv4_attn_set_split_keys)
 
     g = G.to_gpu(case) if g is None else g
-    dsv4_attn_set_kernel(kernel if case.kv == "bf16" else 0)
+    assert kernel == 0 or (kernel in FP8_KERNELS) == (case.kv == "fp8"), "a forced variant of the other format"
+    dsv4_attn_set_kernel(kernel)
     dsv4_attn_set_split_keys(split_keys)
     try:
         p_extra = 0 if case.extra_page_table is None else case.extra_page_table.shape[1]
@@ -119,7 +121,7 @@ class Decoder:
 def check_keys(orc, case, kernel=0, split_keys=0, what=""):
     keys, masks, (splits, chunk, kern), g, _, _ = record(case, kernel, split_keys)
     if kernel:
-        assert kern == (kernel if case.kv == "bf16" else FP8)
+        assert kern == kernel
     dec = Decoder(case, g)
     tile = TILE[kern]
     hb_n = keys.shape[1]
@@ -162,25 +164,26 @@ def test_keys_small_bf16(orc, i, kernel):
     check_keys(orc, small_case(i), kernel, what=SMALL_IDS[i])
 
 
+@pytest.mark.parametrize("kernel", [0, FP8, FP8_H32])
 @pytest.mark.parametrize("i", FP8_CASES, ids=[SMALL_IDS[i] for i in FP8_CASES])
-def test_keys_small_fp8(orc, i):
-    log(f"keys {SMALL_IDS[i]} fp8")
-    check_keys(orc, small_case(i), what=SMALL_IDS[i])
+def test_keys_small_fp8(orc, i, kernel):
+    log(f"keys {SMALL_IDS[i]} fp8 kernel={kernel}")
+    check_keys(orc, small_case(i), kernel, what=SMALL_IDS[i])
 
 
-@pytest.mark.parametrize("kernel", [H16, H32, ROLES, H64, FP8])
+@pytest.mark.parametrize("kernel", [H16, H32, ROLES, H64, FP8, FP8_H32])
 @pytest.mark.parametrize("keys", [16, 32, 48, 96, 160, 1024])
 def test_keys_forced_splits(orc, keys, kernel):
     """Split boundaries at every forced size, on a C4 case with scattered
     unused entries (some splits hold only unused entries or only window keys)
     and a C128 case."""
-    kv = "fp8" if kernel == FP8 else "bf16"
+    kv = "fp8" if kernel in FP8_KERNELS else "bf16"
     cases = [make_case(seq_lens=[3000, 700, 5], n_q=[2, 3, 1], H=100, R=4, seed=31, pad_mode="scatter", kv=kv,
                        n_sel=200),
              make_case(seq_lens=[9000, 130], n_q=[3, 1], H=64, R=128, seed=32, kv=kv)]
     for c in cases:
         log(f"keys forced split {keys} kernel={kernel} R={c.R}")
-        check_keys(orc, c, 0 if kernel == FP8 else kernel, split_keys=keys, what=f"R{c.R}-split{keys}-k{kernel}")
+        check_keys(orc, c, kernel, split_keys=keys, what=f"R{c.R}-split{keys}-k{kernel}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
@@ -198,6 +201,12 @@ def test_keys_workloads_other_kernels(orc, n, kernel):
     check_keys(orc, case, kernel, what=f"{case.name}-k{kernel}")
 
 
+@pytest.mark.parametrize("kernel", [FP8, FP8_H32])
+def test_keys_fp8_workload_both_kernels(orc, kernel):
+    case = make_config(5)
+    check_keys(orc, case, kernel, what=f"{case.name}-k{kernel}")
+
+
 @pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64])
 @pytest.mark.parametrize("n", [6, 7])
 def test_keys_prefill_reduced(orc, n, kernel):
@@ -206,28 +215,28 @@ def test_keys_prefill_reduced(orc, n, kernel):
     check_keys(orc, case, kernel, what=f"{case.name}-reduced-k{kernel}")
 
 
-@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64, FP8])
+@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64, FP8, FP8_H32])
 def test_keys_page_table_beyond_lds_cache(orc, kernel):
     """Requests whose extra page table is longer than a workgroup's LDS cache
     of it (contexts past 1M tokens): compressed slots resolved through one
     more round of page-table loads, bit-exact on every variant."""
-    kv = "fp8" if kernel == FP8 else "bf16"
+    kv = "fp8" if kernel in FP8_KERNELS else "bf16"
     case = make_case(seq_lens=[1_200_000, 1_060_000], n_q=[1, 3], H=64, R=4, seed=91, kv=kv)
     assert case.extra_page_table.shape[1] > 1024
     log(f"keys beyond the page-table cache kernel={kernel}")
-    check_keys(orc, case, 0 if kernel == FP8 else kernel, what=f"beyond-cache-k{kernel}")
+    check_keys(orc, case, kernel, what=f"beyond-cache-k{kernel}")
 
 
-@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64, FP8])
+@pytest.mark.parametrize("kernel", [0, H16, H32, ROLES, H64, FP8, FP8_H32])
 @pytest.mark.parametrize("R", [4, 128])
 def test_keys_many_requests(orc, R, kernel):
     """150 requests: rows past the first 64-request chunk of the
     row-to-request search, bit-exact key sets on every variant."""
-    kv = "fp8" if kernel == FP8 else "bf16"
+    kv = "fp8" if kernel in FP8_KERNELS else "bf16"
     rng = np.random.default_rng(500 + R)
     B = 150
     nq = rng.integers(0, 4, size=B)
     sl = np.maximum(rng.integers(1, 700, size=B), nq) + (128 if R == 128 else 0)
     case = make_case(seq_lens=sl, n_q=nq, H=64, R=R, seed=501 + R, kv=kv, n_sel=40)
     log(f"keys many requests R={R} kernel={kernel}")
-    check_keys(orc, case, 0 if kernel == FP8 else kernel, what=f"many-requests-R{R}-k{kernel}")
+    check_keys(orc, case, kernel, what=f"many-requests-R{R}-k{kernel}")

@@ -96,11 +96,14 @@ def test_gather_workloads_bit_exact(orc, n):
 # bf16 split-kernel variants (DSV4_KERNEL_*): 0 automatic, 1 16 heads, 2 32 heads
 # (dim quarters), 3 32 heads (score / PV roles), 4 64 heads.
 BF16_KERNELS = [1, 2, 3, 4]
+# FP8 split-kernel variants: 5 64 heads (dim halves), 6 32 heads (dim quarters).
+FP8_KERNELS = [5, 6]
 
 
 @pytest.fixture
 def kernel(request):
-    """Force one bf16 kernel variant for the test, then restore the automatic choice."""
+    """Force one kernel variant for the test (it applies to pools of its own
+    format), then restore the automatic choice."""
     from hybrid_sparse_mqa_amd import dsv4_attn_set_kernel
 
     dsv4_attn_set_kernel(request.param)
@@ -144,6 +147,19 @@ def test_forward_small(orc, i):
 @pytest.mark.parametrize("kernel", BF16_KERNELS, indirect=True)
 @pytest.mark.parametrize("i", [0, 3, 5, 8, 11, 12, 14, 15, 16], ids=[SMALL_IDS[i] for i in [0, 3, 5, 8, 11, 12, 14, 15, 16]])
 def test_forward_small_each_bf16_kernel(orc, i, kernel):
+    case = small_case(i)
+    log(f"forward small {SMALL_IDS[i]} kernel={kernel}")
+    out, lse = G.run_forward(case)
+    ro, rl, _ = orc.attention(case)
+    G.compare(out, lse, ro, rl, what=f"{SMALL_IDS[i]}-k{kernel}")
+
+
+FP8_SMALL = [i for i, c in enumerate(SMALL) if c[5] == "fp8"]
+
+
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
+@pytest.mark.parametrize("i", FP8_SMALL, ids=[SMALL_IDS[i] for i in FP8_SMALL])
+def test_forward_small_each_fp8_kernel(orc, i, kernel):
     case = small_case(i)
     log(f"forward small {SMALL_IDS[i]} kernel={kernel}")
     out, lse = G.run_forward(case)
@@ -200,7 +216,8 @@ def test_forward_workloads_all_rows(orc, n):
     log(f"  max abs err {e[0]:.3g}  lse err {e[1]:.3g}  rel L2 {e[2]:.3g}")
 
 
-def test_forward_fp8_1m_tiled_batch_all_rows(orc):
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
+def test_forward_fp8_1m_tiled_batch_all_rows(orc, kernel):
     """The FP8 1M-token decode at a larger batch, built as the benchmark's
     batch sweep builds it (copies of two requests, each copy through its own
     C4 lists): 32 rows, every row against the oracle."""
@@ -299,9 +316,9 @@ SPIKES = [
     ("c4 last used entry", 4, [3000], 2, "c4:last", True),
     ("c4 unlisted", 4, [3000], 2, "c4:unlisted", False),
 ]
-# (kernel forced, kv): every bf16 variant, the automatic choice, and FP8.
-VARIANTS = [(0, "bf16"), (1, "bf16"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (0, "fp8")]
-VARIANT_IDS = ["auto", "h16", "h32", "roles", "h64", "fp8"]
+# (kernel forced, kv): every bf16 variant, the automatic choice, and both FP8 variants.
+VARIANTS = [(0, "bf16"), (1, "bf16"), (2, "bf16"), (3, "bf16"), (4, "bf16"), (5, "fp8"), (6, "fp8")]
+VARIANT_IDS = ["auto", "h16", "h32", "roles", "h64", "fp8", "fp8-h32"]
 
 
 @pytest.fixture
@@ -426,8 +443,9 @@ def test_spikes_at_split_boundaries(orc, keys, R, variant):
         dsv4_attn_set_split_keys(0)
 
 
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
 @pytest.mark.parametrize("R", [0, 128])
-def test_growing_scores_fp8(orc, R):
+def test_growing_scores_fp8(orc, R, kernel):
     """The growing-score test on packed FP8 pools: every key row of row 0 is
     re-stored (quantised) as the blend towards 2 * q[0, head 0]."""
     from synth import store_float_rows
@@ -443,11 +461,12 @@ def test_growing_scores_fp8(orc, R):
         store_float_rows(getattr(case, pool_name), "fp8", slots, rows.astype(np.float32))
     out, lse = G.run_forward(case)
     ro, rl, _ = orc.attention(case)
-    G.compare(out, lse, ro, rl, what=f"growing-fp8-R{R}")
+    G.compare(out, lse, ro, rl, what=f"growing-fp8-R{R}-k{kernel}")
 
 
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
 @pytest.mark.parametrize("keys", [32, 64, 160, 1024])
-def test_forced_split_sizes_fp8(orc, keys):
+def test_forced_split_sizes_fp8(orc, keys, kernel):
     from hybrid_sparse_mqa_amd import dsv4_attn_set_split_keys
 
     case = make_case(seq_lens=[3000, 700, 5], n_q=[2, 3, 1], H=100, R=4, seed=31, pad_mode="scatter", kv="fp8")
@@ -457,7 +476,7 @@ def test_forced_split_sizes_fp8(orc, keys):
         out, lse = G.run_forward(case)
     finally:
         dsv4_attn_set_split_keys(0)
-    G.compare(out, lse, ro, rl, what=f"fp8 split{keys}")
+    G.compare(out, lse, ro, rl, what=f"fp8 split{keys} k{kernel}")
 
 
 @pytest.mark.parametrize("kernel", BF16_KERNELS, indirect=True)
@@ -487,7 +506,8 @@ def test_growing_scores(orc, R, kernel):
 # --------------------------------------------------------------------------
 # FP8: every finite E4M3 code through the dequant path
 # --------------------------------------------------------------------------
-def test_fp8_all_codes(orc):
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
+def test_fp8_all_codes(orc, kernel):
     from synth.workloads import FP8_SCALE_OFFSET
 
     case = make_case(seq_lens=[2000], n_q=2, H=64, R=128, kv="fp8", seed=3)
@@ -522,8 +542,9 @@ def _fp8_pool_from_bf16(pool):
     return out
 
 
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
 @pytest.mark.parametrize("R", [4, 128])
-def test_fp8_against_unquantised_bf16(orc, R):
+def test_fp8_against_unquantised_bf16(orc, R, kernel):
     """How far FP8 storage moves the result (informational, bounded at the
     5e-2 with which the test-matrix page's reference notes absorb FP8 noise
     against the saved bf16 keys): the FP8 path over pools packed from a bf16
@@ -541,7 +562,8 @@ def test_fp8_against_unquantised_bf16(orc, R):
     assert np.allclose(o, ro, atol=5e-2, rtol=5e-2) and np.allclose(l, rl, atol=5e-2)
 
 
-def test_fp8_decode_bit_exact(orc):
+@pytest.mark.parametrize("kernel", FP8_KERNELS, indirect=True)
+def test_fp8_decode_bit_exact(orc, kernel):
     """One visible key (position 0, window only), no sink, per-token scale 1:
     every head's softmax weight is exactly 1, so every output row is the key's
     dequantised row.  Its 448 codes cycle through all 254 finite E4M3 codes
