@@ -11,16 +11,17 @@ namespace dsv4 {
 
 constexpr int kTileKeys = 32;        // keys per LDS tile
 constexpr int kMaxSplitKeys = 1024;  // keys one workgroup may own (LDS slot list)
-constexpr int kWideHeadsPerBlock = 64;  // query heads per workgroup, wide bf16 and FP8 kernels
-constexpr int kWide32HeadsPerBlock = 32;  // query heads per workgroup, 32-head wide bf16 kernel
+constexpr int kWideHeadsPerBlock = 64;  // query heads per workgroup, 64-head bf16 and FP8 layouts
+constexpr int kWide32HeadsPerBlock = 32;  // query heads per workgroup, 32-head bf16 (both) and FP8 layouts
 constexpr int kNarrowHeadsPerBlock = 16;  // query heads per workgroup, narrow bf16 kernel
 constexpr int kNarrowTileKeys = 16;       // keys per LDS tile of the narrow kernel
 constexpr int kNarrowMaxSplitKeys = 2048; // keys one narrow workgroup may own
 
 // Which split kernel runs: bf16 with 64 heads per workgroup (waves split
 // into two head groups x two dim halves), bf16 with 32 heads per workgroup
-// (four dim quarters), bf16 with 16 heads per workgroup (four independent
-// waves), or packed FP8 (64 heads per workgroup).
+// (four dim quarters, or score and PV roles), bf16 with 16 heads per
+// workgroup (four independent waves), or packed FP8 with 64 heads (two head
+// groups x two dim halves) or 32 heads (four dim quarters) per workgroup.
 enum class Layout { kWide, kWide32, kRoles32, kNarrow, kFp8, kFp8H32 };
 constexpr int kTableCap = 1024;      // extra page-table entries a workgroup caches in LDS
 constexpr int kStages = 4;           // bf16 key tiles resident in LDS
