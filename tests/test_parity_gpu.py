@@ -70,6 +70,8 @@ SMALL = [  # (seq_lens, n_q, R, W, H, kv, extra kwargs)
     ([5000, 12], [4, 0], 4, 128, 64, "fp8", {}),
     ([600, 90], [1, 3], 128, 128, 8, "fp8", {}),
     ([200], 1, 0, 128, 64, "fp8", {}),
+    ([3000, 700, 5], [2, 3, 1], 4, 3, 128, "fp8", dict(pad_mode="scatter", n_sel=300)),
+    ([131, 2000], [3, 1], 128, 128, 33, "fp8", {}),
 ]
 SMALL_IDS = [f"{i}-R{c[2]}-W{c[3]}-H{c[4]}-{c[5]}" for i, c in enumerate(SMALL)]
 
