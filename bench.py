@@ -179,14 +179,16 @@ def cpu_baseline(case, target_s: float):
         affinity = len(os.sched_getaffinity(0))
     except AttributeError:
         affinity = os.cpu_count()
+    per_row = algorithmic_bytes(case)["total"] / case.T  # the call's algorithmic bytes per query row
     return {
         "value": v_all,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
+        "effective_gbs": v_all * per_row / 1e9,  # the same algorithmic bytes per row, at the oracle's rate
         "sample": f"{n} of {case.T} query rows of the same workload x {reps} repetitions "
                   f"(fp64 C, OpenMP over rows, {threads} threads), {dt:.1f} s",
-        "one_thread": {"value": v_one, "unit": "tokens/s", "cores": 1,
+        "one_thread": {"value": v_one, "unit": "tokens/s", "cores": 1, "effective_gbs": v_one * per_row / 1e9,
                        "sample": f"{n1} rows x {reps1} repetitions, {dt1:.1f} s"},
         "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity": affinity,
                  "omp_threads": omp_threads},
