@@ -535,8 +535,8 @@ def main() -> int:
                          "6 and 7 are the C4 and C128 sparse-prefill workloads)")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--batch", type=int, default=0,
-                    help="workload 5 only: requests per call, a multiple of 8 (copies of the 8 requests, each "
-                         "copy reading through its own C4 index lists)")
+                    help="requests per call: workloads 2-4, B requests of the workload's shape; workload 5, a "
+                         "multiple of 8 (copies of the 8 requests, each copy reading through its own C4 index lists)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample size target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-keys", type=int, default=0, help="force keys per split (0 = library plan)")
@@ -592,18 +592,24 @@ def main() -> int:
     # from the same pools.  --batch B runs B/8 copies of the 8 requests, copy
     # k reading through its own index set (synth.tile_requests), so that the
     # batch sweep at 1M tokens needs no per-request pools.
+    # For workloads 2-4, --batch B draws B requests of the same shape (a
+    # batch sweep of the bf16 decode and verify kernels).
     copies = 1
+    batch = None
     if args.batch:
-        if args.config != 5 or args.batch % 8:
-            print("--batch applies to workload 5 and takes a multiple of 8", file=sys.stderr)
+        if args.config == 5 and args.batch % 8 == 0:
+            copies = args.batch // 8
+        elif args.config in (2, 3, 4) and args.batch > 0:
+            batch = args.batch
+        else:
+            print("--batch applies to workloads 2-4 (any B > 0) and 5 (a multiple of 8)", file=sys.stderr)
             return 2
-        copies = args.batch // 8
     idx_sets = 0
     if args.config == 5:
         # distinct bytes per rotation step: C4 rows (8 x 512 x 584 B) and Q per copy
         steps_needed = int(-(-3 * MALL_BYTES // (copies * (8 * 512 * 584 + 8 * 64 * 1024))))
         idx_sets = (args.sets or max(2, steps_needed)) * copies
-    case = make_config(args.config, index_sets=max(1, idx_sets))
+    case = make_config(args.config, index_sets=max(1, idx_sets), batch=batch)
     if copies > 1:
         case = tile_requests(case, copies)
     ab = algorithmic_bytes(case)

@@ -293,16 +293,19 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
 // 8 rows 16.8 vs 14.5 us (10 splits each), 16 rows 18.3 vs 16.4 (10 / 7
 // splits), 24 rows 20.7 vs 19.1 (10 / 5), 32 rows 21.3 vs 20.5 (7 / 4),
 // 64 rows 27.3 vs 29.3 (4 / 2 splits: the 32-head splits hold 10 tiles).
-// bf16 pools: the variant forced by dsv4_attn_set_kernel, else the 16-head kernel for at most 16 heads (no
-// padding of heads); above that the 64-head kernel when the rows alone give
-// every compute unit at least two 64-head workgroups (prefill / extend:
-// compute-bound, and a 64-head tile does twice the MFMA work per LDS tile
-// copy), else the 32-head score/PV role kernel.  Measured on MI355X (graph
-// replay per call): C4 prefill 4 x 2048 rows 1.02 ms (64-head) vs 1.28 ms
-// (roles); C128 prefill 0.74 vs 0.94 ms; decode and verify (32-128 rows):
-// roles fastest -- C4 decode 32 rows 16.8 vs 17.1 us (32-head dim split),
-// C128 decode 64 rows 30.9 vs 33.2 us (64-head), C4 verify 128 rows 28.6 vs
-// 31.0 us.
+// bf16 pools: the variant forced by dsv4_attn_set_kernel, else the 16-head
+// kernel for at most 16 heads (no padding of heads); above that the 32-head
+// score/PV role kernel while its whole grid (rows x 32-head blocks x its
+// splits) fits the compute units once, and the 64-head kernel, which loads
+// each tile once for all 64 heads, when it does not (more than 32 heads; for
+// 17-32 heads, only when the rows alone give every compute unit two 64-head
+// workgroups, since a 64-head workgroup then multiplies padded heads).
+// Measured on MI355X (graph replay per call, roles vs 64-head): C4 decode
+// 32 rows 16.8 vs 17.1 us (32-head dim split), 128 rows 29.1 vs 39.0, 256
+// rows 62.7 vs 57.2; C128 decode at 128K, 64 rows 30.9 vs 33.2 us, 128 rows
+// 63.7 vs 55.4, 512 rows 215 vs 188; C4 verify 128 rows 28.6 vs 31.0 us, 512
+// rows 108 vs 97; C4 prefill 4 x 2048 rows 1.28 vs 1.02 ms; C128 prefill
+// 0.94 vs 0.74 ms.
 Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8, int64_t nmax) {
     if (fp8) {
         if (g_force_kernel == DSV4_KERNEL_FP8) return Layout::kFp8;
@@ -321,9 +324,11 @@ Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8, int64_t nmax) {
         default: break;
     }
     if (H <= kNarrowHeadsPerBlock) return Layout::kNarrow;
-    const int64_t blocks64 = (int64_t)T * ((H + kWideHeadsPerBlock - 1) / kWideHeadsPerBlock);
-    if (blocks64 >= 2 * (int64_t)cus) return Layout::kWide;
-    return Layout::kRoles32;
+    if (H <= kWide32HeadsPerBlock) return (int64_t)T >= 2 * (int64_t)cus ? Layout::kWide : Layout::kRoles32;
+    int32_t s = 1, c = 0;
+    plan_splits(cus, T, H, nmax, Layout::kRoles32, &s, &c);
+    const int64_t items = (int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) * s;
+    return items <= cus ? Layout::kRoles32 : Layout::kWide;
 }
 
 int32_t heads_per_block(Layout layout) {
@@ -378,6 +383,15 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
         c = (nmax + want - 1) / want;
         const int64_t unit = tile_keys(layout);
         c = (c + unit - 1) / unit * unit;
+        // When a workgroup's key limit forces more splits than wanted, make
+        // them equal rather than leaving a short last one: the workgroups of
+        // a call end together only if their splits are alike (measured:
+        // C128 decode at 1152 keys per row, 128 requests, roles kernel:
+        // 1024 + 128 keys 64.3 us against 53.2 us for 2 x 576 keys).
+        if (c > max_split_keys(layout)) {
+            const int64_t n = (nmax + max_split_keys(layout) - 1) / max_split_keys(layout);
+            c = ((nmax + n - 1) / n + unit - 1) / unit * unit;
+        }
     }
     c = (c + tile_keys(layout) - 1) / tile_keys(layout) * tile_keys(layout);
     c = std::min<int64_t>(std::max<int64_t>(c, tile_keys(layout)), max_split_keys(layout));
