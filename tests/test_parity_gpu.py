@@ -184,6 +184,55 @@ def test_forced_split_sizes_each_bf16_kernel(orc, keys, kernel):
     G.compare(out, lse, ro, rl, what=f"split{keys}-k{kernel}")
 
 
+def _random_wide_case(seed):
+    """Random shapes that reach the planner's other branches: many requests
+    (grids past one round of workgroups, where the 64-head kernels take
+    over), long C128 rows (more keys than one workgroup's limit: equal
+    splits), and small mixed cases."""
+    rng = np.random.default_rng(seed)
+    R = int(rng.choice([0, 4, 128]))
+    mode = rng.random()
+    if mode < 0.3:
+        B = int(rng.integers(64, 300))
+        nq = rng.integers(1, 3, size=B)
+        sl = np.maximum(rng.integers(1, 3000, size=B), nq)
+    elif mode < 0.7 and R == 128:
+        B = int(rng.integers(1, 4))
+        nq = rng.integers(1, 4, size=B)
+        sl = rng.integers(100_000, 200_000, size=B)
+    else:
+        B = int(rng.integers(1, 9))
+        nq = rng.integers(0, 6, size=B)
+        sl = np.maximum(rng.integers(1, 6000, size=B), nq) + (int(rng.integers(0, 300)) if R == 128 else 0)
+    heads = [16, 33, 64] if mode < 0.3 else [1, 5, 16, 17, 32, 33, 64, 65, 100, 128]
+    case = make_case(seq_lens=sl, n_q=nq, H=int(rng.choice(heads)), R=R, W=int(rng.choice([1, 2, 3, 64, 128, 200])),
+                     kv=str(rng.choice(["bf16", "fp8"])), sink=bool(rng.random() < 0.8), seed=9000 + seed,
+                     K=int(rng.choice([32, 64, 512, 600])), pad_mode=str(rng.choice(["tail", "scatter"])))
+    return case, int(rng.choice([0, 0, 32, 64, 96, 160]))
+
+
+@pytest.mark.parametrize("seed", range(2000, 2040))
+def test_forward_random_every_variant(orc, seed):
+    """Random cases (see _random_wide_case) on the automatic plan and every
+    variant of the pool's format, under a random forced split size."""
+    from hybrid_sparse_mqa_amd import dsv4_attn_set_kernel, dsv4_attn_set_split_keys
+
+    case, split = _random_wide_case(seed)
+    if case.T == 0:
+        pytest.skip("no query rows drawn")
+    log(f"random every variant seed={seed} R={case.R} T={case.T} H={case.H} W={case.W} kv={case.kv} split={split}")
+    ro, rl, _ = orc.attention(case)
+    for k in ([0] + FP8_KERNELS if case.kv == "fp8" else [0] + BF16_KERNELS):
+        dsv4_attn_set_kernel(k)
+        dsv4_attn_set_split_keys(split)
+        try:
+            out, lse = G.run_forward(case)
+        finally:
+            dsv4_attn_set_kernel(0)
+            dsv4_attn_set_split_keys(0)
+        G.compare(out, lse, ro, rl, what=f"random seed {seed} k{k} split{split}")
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_forward_random(orc, seed):
     rng = np.random.default_rng(seed)
