@@ -296,16 +296,19 @@ void plan_splits(int cus, int32_t T, int32_t H, int64_t nmax, Layout layout, int
 // bf16 pools: the variant forced by dsv4_attn_set_kernel, else the 16-head
 // kernel for at most 16 heads (no padding of heads); above that the 32-head
 // score/PV role kernel while its whole grid (rows x 32-head blocks x its
-// splits) fits the compute units once, and the 64-head kernel, which loads
-// each tile once for all 64 heads, when it does not (more than 32 heads; for
+// splits) needs less than two rounds of workgroups on the compute units,
+// and the 64-head kernel, which loads each tile once for all 64 heads, from
+// two rounds on (more than 32 heads; for
 // 17-32 heads, only when the rows alone give every compute unit two 64-head
 // workgroups, since a 64-head workgroup then multiplies padded heads).
-// Measured on MI355X (graph replay per call, roles vs 64-head): C4 decode
-// 32 rows 16.8 vs 17.1 us (32-head dim split), 128 rows 29.1 vs 39.0, 256
-// rows 62.7 vs 57.2; C128 decode at 128K, 64 rows 30.9 vs 33.2 us, 128 rows
-// 63.7 vs 55.4, 512 rows 215 vs 188; C4 verify 128 rows 28.6 vs 31.0 us, 512
-// rows 108 vs 97; C4 prefill 4 x 2048 rows 1.28 vs 1.02 ms; C128 prefill
-// 0.94 vs 0.74 ms.
+// Measured on MI355X (graph replay per call, roles vs 64-head; the roles
+// grid in rounds of 256 workgroups): C4 decode 32 rows 16.8 vs 17.1 us
+// (32-head dim split), 128 rows (1 round) 29.1 vs 39.0, 160 rows (1.25)
+// 48.7 vs 55.3, 192 rows (1.5) 53.9 vs 62.0, 256 rows (2) 62.7 vs 57.2; C128
+// decode at 128K, 64 rows (1) 30.9 vs 33.2 us, 96 rows (1.5) 55.0 vs 56.6,
+// 128 rows (2) 63.7 vs 55.4, 512 rows (8) 215 vs 188; C4 verify 128 rows
+// (1) 28.6 vs 31.0 us, 192 rows (1.5) 50.4 vs 57.6, 512 rows (4) 108 vs 97;
+// C4 prefill 4 x 2048 rows 1.28 vs 1.02 ms; C128 prefill 0.94 vs 0.74 ms.
 Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8, int64_t nmax) {
     if (fp8) {
         if (g_force_kernel == DSV4_KERNEL_FP8) return Layout::kFp8;
@@ -328,7 +331,7 @@ Layout choose_layout(int32_t T, int32_t H, int cus, bool fp8, int64_t nmax) {
     int32_t s = 1, c = 0;
     plan_splits(cus, T, H, nmax, Layout::kRoles32, &s, &c);
     const int64_t items = (int64_t)T * ((H + kWide32HeadsPerBlock - 1) / kWide32HeadsPerBlock) * s;
-    return items <= cus ? Layout::kRoles32 : Layout::kWide;
+    return items < 2 * (int64_t)cus ? Layout::kRoles32 : Layout::kWide;
 }
 
 int32_t heads_per_block(Layout layout) {

@@ -235,9 +235,12 @@ def test_plan_is_host_only_and_sane():
     # kernel, in two equal splits (not 1024 + 128)
     assert L.dsv4_attn_plan(128, 64, 128, 128, 0, 4, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 4 and s.value == 2 and c.value == 576
-    # 256 rows of C4 decode: 512 role workgroups, the 64-head kernel; 128 rows fit once: the role kernel
+    # C4 decode: 256 rows (512 role workgroups, two rounds) the 64-head kernel; 192 rows (1.5 rounds)
+    # and 128 rows (one) the role kernel
     assert L.dsv4_attn_plan(256, 64, 4, 128, 512, 32, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 4 and s.value == 1
+    assert L.dsv4_attn_plan(192, 64, 4, 128, 512, 32, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert k.value == 3 and s.value == 1
     assert L.dsv4_attn_plan(128, 64, 4, 128, 512, 32, 0, ctypes.byref(s), ctypes.byref(c), ctypes.byref(k)) == 0
     assert k.value == 3 and s.value == 1
     # packed FP8, 8 rows: the 32-head grid (8 x 2 x 10 splits) fits 256 compute units once
